@@ -1,0 +1,237 @@
+/*
+ * oracle.c -- plain, slow fp64 CPU oracle for masked softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the GPU library, and it never calls it.
+ *
+ * What it computes is the plain definition of attention, with no tiling,
+ * blocking, online softmax or reordering:
+ *
+ *     s_j = scale * sum_d Q[i,d] K[j,d]          (fp64, d ascending)
+ *     m   = max_j s_j,  w_j = exp(s_j - m),  Z = sum_j w_j   (j ascending)
+ *     O[i,:] = sum_j (w_j / Z) V[j,:]                        (j ascending)
+ *     lse = m + log(Z)
+ *
+ * over the allowed key set of each query row.  Sources:
+ *  - "RFC: Gemma-4-31B-it train/rollout consistency" (RL-Kernel issue 415),
+ *    section 3 "Architecture map": sliding and global layers are distinct
+ *    attention cores with different head geometry and mask semantics;
+ *    section 1 "Motivation", Phase B: vision tokens carry a bidirectional
+ *    mask.
+ *  - "Gemma-4-E4B-it multimodal baseline" (vllm.cpp PR 3476), commit log:
+ *    an image expands into one contiguous run of soft tokens, which is the
+ *    span that is bidirectional.
+ *  - "Vime ROCm Attention operator ablation", section "Prerequisites": strict
+ *    decode reads the paged KV cache directly through the block table.
+ *
+ * Readings taken where the pages are silent (every one is a reading, not a
+ * page fact): the window W admits key j for query i when 0 <= i - j < W
+ * (W keys including the query itself), W < 0 means no window (global
+ * causal); a key j is also admitted, whatever the window, when i and j lie
+ * in the same bidirectional span [s, e); GQA groups are contiguous, so query
+ * head h reads KV head h / (Hq / Hkv); decode's query is the last token of
+ * its sequence and its own key is already in the cache.
+ *
+ * Inputs may be bf16 bit patterns (converted exactly), fp32 or fp64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2 };
+
+/* Exact widening of one stored element to fp64. */
+static double load_elem(const void* base, int dtype, int64_t idx) {
+    if (dtype == ORACLE_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    return ((const double*)base)[idx];
+}
+
+/* Is key j admitted for query i of a sequence?  i, j are positions within
+ * the sequence; span_lo/span_hi are the sequence-relative bounds of the
+ * span holding i, or -1 when i is in no span. */
+static int allowed(int64_t i, int64_t j, int32_t window,
+                   int64_t span_lo, int64_t span_hi) {
+    int causal_ok = (j <= i) && (window < 0 || i - j < (int64_t)window);
+    int span_ok = span_lo >= 0 && j >= span_lo && j < span_hi;
+    return causal_ok || span_ok;
+}
+
+/* One query row against an explicit list of key rows.
+ * q: pointer/offset of the query vector; key_off[n]: element offsets of the
+ * key rows (same offsets serve V).  out: D doubles.  s: scratch, n doubles. */
+static void attend_row(const void* q, int qt, int64_t q_off,
+                       const void* k, const void* v, int kvt,
+                       const int64_t* key_off, int64_t n, int32_t d,
+                       double scale, double* s, double* out, double* lse) {
+    double m = -INFINITY;
+    for (int64_t a = 0; a < n; ++a) {
+        double dot = 0.0;
+        for (int32_t c = 0; c < d; ++c)
+            dot += load_elem(q, qt, q_off + c) * load_elem(k, kvt, key_off[a] + c);
+        s[a] = scale * dot;
+        if (s[a] > m) m = s[a];
+    }
+    double z = 0.0;
+    for (int64_t a = 0; a < n; ++a) {
+        s[a] = exp(s[a] - m);
+        z += s[a];
+    }
+    for (int32_t c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t a = 0; a < n; ++a) {
+        double p = s[a] / z;
+        for (int32_t c = 0; c < d; ++c) out[c] += p * load_elem(v, kvt, key_off[a] + c);
+    }
+    if (lse) *lse = m + log(z);
+}
+
+/*
+ * Prefill over packed variable-length sequences.
+ *   q   [T, hq, d], k/v [T, hkv, d]  (dtype codes above)
+ *   o   [T, hq, d] fp64 out; lse [T, hq] fp64 out or NULL
+ *   cu_seqlens[batch+1]: sequence b holds packed tokens [cu[b], cu[b+1])
+ *   spans[num_spans][2]: packed [start, end) ranges, each inside one sequence
+ *   rows: optional list of n_rows (token, head) pairs to compute; NULL = all.
+ *     With a row list, o and lse are indexed by list position: o[n_rows, d],
+ *     lse[n_rows].
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_prefill(const void* q, int qdtype, const void* k, const void* v,
+                   int kvdtype, double* o, double* lse,
+                   const int32_t* cu_seqlens, int32_t batch, int32_t hq,
+                   int32_t hkv, int32_t d, int32_t window, double scale,
+                   const int32_t* spans, int32_t num_spans,
+                   const int64_t* rows, int64_t n_rows, int32_t threads) {
+    if (batch < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
+    const int64_t total = cu_seqlens[batch];
+    const int32_t group = hq / hkv;
+    int64_t max_len = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t len = cu_seqlens[b + 1] - cu_seqlens[b];
+        if (len < 0) return -1;
+        if (len > max_len) max_len = len;
+    }
+    /* Sequence id of every packed token. */
+    int32_t* seq_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total > 0 ? total : 1));
+    for (int32_t b = 0; b < batch; ++b)
+        for (int64_t t = cu_seqlens[b]; t < cu_seqlens[b + 1]; ++t) seq_of[t] = b;
+    const int64_t n_work = rows ? n_rows : total * hq;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#endif
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+        int64_t* key_off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(max_len > 0 ? max_len : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t w = 0; w < n_work; ++w) {
+            int64_t t = rows ? rows[2 * w] : w / hq;
+            int32_t h = (int32_t)(rows ? rows[2 * w + 1] : w % hq);
+            if (t < 0 || t >= total || h < 0 || h >= hq) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int32_t b = seq_of[t];
+            int64_t start = cu_seqlens[b], len = cu_seqlens[b + 1] - start;
+            int64_t i = t - start;
+            int64_t span_lo = -1, span_hi = -1;
+            for (int32_t sp = 0; sp < num_spans; ++sp) {
+                if (t >= spans[2 * sp] && t < spans[2 * sp + 1]) {
+                    span_lo = spans[2 * sp] - start;
+                    span_hi = spans[2 * sp + 1] - start;
+                }
+            }
+            int32_t g = h / group;
+            int64_t n = 0;
+            for (int64_t j = 0; j < len; ++j)
+                if (allowed(i, j, window, span_lo, span_hi))
+                    key_off[n++] = ((start + j) * hkv + g) * (int64_t)d;
+            double* out = o + (rows ? w : t * hq + h) * (int64_t)d;
+            double* l = lse ? lse + (rows ? w : t * hq + h) : NULL;
+            attend_row(q, qdtype, (t * hq + h) * (int64_t)d, k, v, kvdtype,
+                       key_off, n, d, scale, s, out, l);
+        }
+        free(s);
+        free(key_off);
+    }
+    free(seq_of);
+    return bad ? -1 : 0;
+}
+
+/*
+ * Single-token decode against a paged KV cache.
+ *   q [batch, hq, d]; k_cache/v_cache [num_blocks, block_size, hkv, d]
+ *   block_table [batch, max_blocks]; seq_lens[batch] counts the current token
+ *   o [batch, hq, d] fp64 out; lse [batch, hq] fp64 out or NULL.
+ * Key j of sequence b sits in physical block block_table[b][j / block_size],
+ * slot j % block_size.  The query is position seq_lens[b] - 1.
+ */
+int oracle_decode(const void* q, int qdtype, const void* k_cache,
+                  const void* v_cache, int kvdtype,
+                  const int32_t* block_table, int32_t max_blocks,
+                  const int32_t* seq_lens, int32_t batch, int32_t hq,
+                  int32_t hkv, int32_t d, int32_t block_size, int32_t window,
+                  double scale, double* o, double* lse, int32_t threads) {
+    if (batch < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv || block_size <= 0)
+        return -1;
+    const int32_t group = hq / hkv;
+    int64_t max_len = 1;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (seq_lens[b] < 1 || seq_lens[b] > (int64_t)max_blocks * block_size) return -1;
+        if (seq_lens[b] > max_len) max_len = seq_lens[b];
+    }
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#endif
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)max_len);
+        int64_t* key_off = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_len);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t w = 0; w < (int64_t)batch * hq; ++w) {
+            int32_t b = (int32_t)(w / hq), h = (int32_t)(w % hq), g = h / group;
+            int64_t len = seq_lens[b], i = len - 1, n = 0;
+            for (int64_t j = 0; j < len; ++j) {
+                if (!allowed(i, j, window, -1, -1)) continue;
+                int64_t blk = block_table[(int64_t)b * max_blocks + j / block_size];
+                int64_t slot = j % block_size;
+                key_off[n++] = ((blk * block_size + slot) * hkv + g) * (int64_t)d;
+            }
+            attend_row(q, qdtype, w * (int64_t)d, k_cache, v_cache, kvdtype,
+                       key_off, n, d, scale, s, o + w * (int64_t)d,
+                       lse ? lse + w : NULL);
+        }
+        free(s);
+        free(key_off);
+    }
+    return 0;
+}
+
+/* Number of threads an OpenMP region of this library runs with. */
+int oracle_num_threads(int32_t threads) {
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+#else
+    (void)threads;
+    return 1;
+#endif
+}

@@ -1,0 +1,253 @@
+"""Pins for the fp64 oracle: checks against facts that do not come from the
+oracle itself (hand-worked values, brute force, closed forms, invariants).
+
+Each function takes an optional oracle library handle so the same pins can be
+run against deliberately broken copies of the oracle (see test_oracle.py).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import bruteforce
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.json")
+
+
+def _num(x):
+    """Parse the hand-worked fixture's numbers: 3, "8/3", "2ln2", "ln(11/6)"."""
+    if isinstance(x, (int, float)):
+        return float(x)
+    s = x.replace(" ", "")
+    coef = 1.0
+    if "ln" in s:
+        head, arg = s.split("ln", 1)
+        if head:
+            coef = float(head)
+        arg = arg.strip("()")
+        return coef * math.log(float(Fraction(arg)))
+    return float(Fraction(s))
+
+
+def pin_golden(lib=None):
+    g = json.load(open(GOLDEN))
+    k1 = np.array([[_num(x) for x in row] for row in g["k"]])
+    v1 = np.array([[_num(x) for x in row] for row in g["v"]], np.float64)
+    for case in g["cases"]:
+        signs = case["q_sign"]
+        hq = len(signs)
+        q = np.zeros((3, hq, 4))
+        for h, sg in enumerate(signs):
+            q[:, h, 0] = sg
+        k = k1[:, None, :]
+        v = v1[:, None, :]
+        o, lse = oracle.prefill(q, k, v, [0, 3], window=case["window"], scale=0.5,
+                                spans=case["spans"] or None, want_lse=True, lib=lib)
+        want_o = np.array([[[_num(x) for x in head] for head in row] for row in case["o"]])
+        want_l = np.array([[_num(x) for x in row] for row in case["lse"]])
+        assert np.allclose(o, want_o, rtol=0, atol=1e-12), case["name"]
+        assert np.allclose(lse, want_l, rtol=0, atol=1e-12), case["name"]
+
+
+def _random_case(rng, lengths, hq, hkv, d, span_count=0):
+    T = sum(lengths)
+    q = rng.standard_normal((T, hq, d))
+    k = rng.standard_normal((T, hkv, d))
+    v = rng.standard_normal((T, hkv, d))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    spans = []
+    for b, L in enumerate(lengths):
+        for _ in range(span_count):
+            if L < 3:
+                continue
+            s = int(rng.integers(0, L - 2))
+            e = int(rng.integers(s + 1, L))   # ends before the sequence end
+            if all(e <= a - cu[b] or s >= c - cu[b] for a, c in spans if cu[b] <= a < cu[b + 1]):
+                spans.append((int(cu[b]) + s, int(cu[b]) + e))
+    spans.sort()
+    return q, k, v, cu, spans
+
+
+def pin_bruteforce(lib=None):
+    rng = np.random.default_rng(12345)
+    configs = [
+        ([17], 2, 1, 8, -1, 0),
+        ([5, 31, 1, 12], 4, 2, 16, 3, 1),
+        ([40, 9], 4, 4, 8, 1, 1),
+        ([33, 20, 2], 8, 1, 4, 7, 2),
+        ([64], 4, 2, 32, 100, 2),
+    ]
+    for lengths, hq, hkv, d, w, nsp in configs:
+        q, k, v, cu, spans = _random_case(rng, lengths, hq, hkv, d, nsp)
+        o, lse = oracle.prefill(q, k, v, cu, window=w, spans=spans or None, want_lse=True, lib=lib)
+        bo, bl = bruteforce.attention(q, k, v, cu, window=w, spans=spans)
+        assert np.abs(o - bo).max() <= 1e-12, (lengths, w)
+        assert np.abs(lse - bl).max() <= 1e-12, (lengths, w)
+
+
+def pin_rows_sum_to_one(lib=None):
+    rng = np.random.default_rng(7)
+    q, k, v, cu, spans = _random_case(rng, [30, 45], 4, 2, 16, 1)
+    v = np.ones_like(v)
+    for w in (-1, 1, 5):
+        o = oracle.prefill(q, k, v, cu, window=w, spans=spans, lib=lib)
+        assert np.abs(o - 1.0).max() <= 1e-13
+
+
+def pin_window_covering_sequence_is_global(lib=None):
+    rng = np.random.default_rng(8)
+    q, k, v, cu, _ = _random_case(rng, [19, 50], 2, 1, 8)
+    og = oracle.prefill(q, k, v, cu, window=-1, lib=lib)
+    for w in (50, 51, 1000):
+        assert np.array_equal(oracle.prefill(q, k, v, cu, window=w, lib=lib), og)
+
+
+def pin_one_token_returns_v(lib=None):
+    rng = np.random.default_rng(9)
+    q, k, v, cu, _ = _random_case(rng, [1, 1, 1], 4, 2, 8)
+    o = oracle.prefill(q, k, v, cu, lib=lib)
+    assert np.array_equal(o, np.repeat(v, 2, axis=1))
+    q, k, v, cu, _ = _random_case(rng, [23], 4, 2, 8)
+    o = oracle.prefill(q, k, v, cu, window=1, lib=lib)
+    assert np.array_equal(o, np.repeat(v, 2, axis=1))
+
+
+def _allowed_set(i, L, w, spans):
+    keys = set(range(0, i + 1)) if w < 0 else set(range(max(0, i - w + 1), i + 1))
+    for s, e in spans:
+        if s <= i < e:
+            keys |= set(range(s, e))
+    return keys
+
+
+def pin_zero_query_is_mean(lib=None):
+    """Q = 0: every allowed score is 0, so the output is the plain mean of V
+    over the allowed set and lse = log(count).  V_j = (j mod 256, j // 256, 1)."""
+    L, d = 300, 4
+    j = np.arange(L)
+    v = np.zeros((L, 1, d))
+    v[:, 0, 0] = j % 256
+    v[:, 0, 1] = j // 256
+    v[:, 0, 2] = 1
+    q = np.zeros((L, 2, d))
+    k = np.random.default_rng(3).standard_normal((L, 1, d))
+    spans = [(10, 40), (200, 270)]
+    for w in (-1, 1, 16, 64):
+        o, lse = oracle.prefill(q, k, v, [0, L], window=w, spans=spans, want_lse=True, lib=lib)
+        for i in range(L):
+            keys = sorted(_allowed_set(i, L, w, spans))
+            want = [np.mean([x % 256 for x in keys]), np.mean([x // 256 for x in keys]), 1.0, 0.0]
+            assert np.allclose(o[i, 0], want, rtol=0, atol=1e-12), (w, i)
+            assert np.allclose(o[i, 1], want, rtol=0, atol=1e-12), (w, i)
+            assert abs(lse[i, 0] - math.log(len(keys))) <= 1e-12, (w, i)
+
+
+def pin_dominant_key(lib=None):
+    """q_i = alpha * k_t for an allowed t: the output tends to v_t; very large
+    alpha must not overflow (the max is subtracted before exponentiation)."""
+    rng = np.random.default_rng(11)
+    L, d = 40, 16
+    k = rng.standard_normal((L, 1, d))
+    v = rng.standard_normal((L, 1, d))
+    k /= np.linalg.norm(k, axis=2, keepdims=True)
+    for alpha in (200.0, 1e5):
+        q = np.zeros((L, 1, d))
+        targets = []
+        for i in range(L):
+            t = int(rng.integers(max(0, i - 7), i + 1))   # inside window 8
+            targets.append(t)
+            q[i, 0] = alpha * k[t, 0]
+        o = oracle.prefill(q, k, v, [0, L], window=8, lib=lib)
+        for i in range(L):
+            assert np.allclose(o[i, 0], v[targets[i], 0], rtol=0, atol=1e-6), (alpha, i)
+    # a key outside the window never wins, however strong
+    q = np.zeros((L, 1, d))
+    q[20, 0] = 1e5 * k[5, 0]
+    o = oracle.prefill(q, k, v, [0, L], window=8, lib=lib)
+    assert not np.allclose(o[20, 0], v[5, 0], atol=1e-3)
+
+
+def pin_gqa_reduces_to_mha(lib=None):
+    rng = np.random.default_rng(13)
+    q, k, v, cu, spans = _random_case(rng, [25, 14], 8, 2, 8, 1)
+    o = oracle.prefill(q, k, v, cu, window=6, spans=spans, lib=lib)
+    k4 = np.repeat(k, 4, axis=1)
+    v4 = np.repeat(v, 4, axis=1)
+    assert np.array_equal(oracle.prefill(q, k4, v4, cu, window=6, spans=spans, lib=lib), o)
+
+
+def pin_packing_invariance(lib=None):
+    rng = np.random.default_rng(17)
+    q, k, v, cu, spans = _random_case(rng, [12, 30, 7], 4, 2, 8, 1)
+    full = oracle.prefill(q, k, v, cu, window=5, spans=spans, lib=lib)
+    for b in range(3):
+        a, e = cu[b], cu[b + 1]
+        local = [(s - a, t - a) for s, t in spans if a <= s < e]
+        solo = oracle.prefill(q[a:e], k[a:e], v[a:e], [0, e - a], window=5,
+                              spans=local or None, lib=lib)
+        assert np.array_equal(solo, full[a:e])
+
+
+def pin_row_subset(lib=None):
+    rng = np.random.default_rng(19)
+    q, k, v, cu, spans = _random_case(rng, [20, 33], 4, 2, 8, 1)
+    full, fl = oracle.prefill(q, k, v, cu, window=9, spans=spans, want_lse=True, lib=lib)
+    rows = np.array([[0, 0], [52, 3], [20, 1], [33, 2]])
+    sub, sl = oracle.prefill(q, k, v, cu, window=9, spans=spans, rows=rows, want_lse=True, lib=lib)
+    for n, (t, h) in enumerate(rows):
+        assert np.array_equal(sub[n], full[t, h])
+        assert sl[n] == fl[t, h]
+
+
+def _decode_inputs(rng, lengths, hq, hkv, d, bs, spare=5):
+    nblk = [(L + bs - 1) // bs for L in lengths]
+    nb = sum(nblk) + spare
+    kc = rng.standard_normal((nb, bs, hkv, d))
+    vc = rng.standard_normal((nb, bs, hkv, d))
+    perm = rng.permutation(nb)
+    bt = np.zeros((len(lengths), max(nblk)), np.int32)
+    c = 0
+    for b, n in enumerate(nblk):
+        bt[b, :n] = perm[c:c + n]
+        c += n
+    q = rng.standard_normal((len(lengths), hq, d))
+    return q, kc, vc, bt, np.array(lengths, np.int32)
+
+
+def pin_decode(lib=None):
+    """Decode equals brute force over the gathered cache, equals the last
+    prefill row of the same sequence, and ignores physical block placement."""
+    rng = np.random.default_rng(23)
+    lengths = [1, 16, 17, 50]
+    q, kc, vc, bt, sl = _decode_inputs(rng, lengths, 4, 2, 8, 16)
+    for w in (-1, 1, 10):
+        o = oracle.decode(q, kc, vc, bt, sl, window=w, lib=lib)
+        assert np.abs(o - bruteforce.decode(q, kc, vc, bt, sl, window=w)).max() <= 1e-12
+        for b, L in enumerate(lengths):
+            nb = (L + 15) // 16
+            kk = kc[bt[b, :nb]].reshape(-1, 2, 8)[:L]
+            vv = vc[bt[b, :nb]].reshape(-1, 2, 8)[:L]
+            qq = np.zeros((L, 4, 8))
+            qq[L - 1] = q[b]
+            row = oracle.prefill(qq, kk, vv, [0, L], window=w, lib=lib)[L - 1]
+            assert np.abs(row - o[b]).max() <= 1e-12
+        # move every block to a new physical id
+        nb_total = kc.shape[0]
+        perm = rng.permutation(nb_total)
+        kc2 = np.empty_like(kc)
+        vc2 = np.empty_like(vc)
+        kc2[perm] = kc
+        vc2[perm] = vc
+        bt2 = perm[bt].astype(np.int32)
+        assert np.array_equal(oracle.decode(q, kc2, vc2, bt2, sl, window=w, lib=lib), o)
+
+
+ALL_PINS = [pin_golden, pin_bruteforce, pin_rows_sum_to_one,
+            pin_window_covering_sequence_is_global, pin_one_token_returns_v,
+            pin_zero_query_is_mean, pin_dominant_key, pin_gqa_reduces_to_mha,
+            pin_packing_invariance, pin_row_subset, pin_decode]

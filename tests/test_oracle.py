@@ -1,0 +1,54 @@
+"""The oracle against its pins, and planted mistakes in the oracle against
+the same pins (each must be caught by at least one)."""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import oracle_pins
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+# (name, text in oracle.c, replacement): plausible slips in the arithmetic
+MUTANTS = [
+    ("causal edge off by one", "(j <= i)", "(j < i)"),
+    ("window edge off by one", "i - j < (int64_t)window", "i - j <= (int64_t)window"),
+    ("span end inclusive", "j < span_hi", "j <= span_hi"),
+    ("span start exclusive", "j >= span_lo", "j > span_lo"),
+    ("no max subtraction", "s[a] = exp(s[a] - m);", "s[a] = exp(s[a]);"),
+    ("wrong GQA head map", "int32_t g = h / group;", "int32_t g = h % hkv;"),
+    ("decode GQA head map", "g = h / group;\n", "g = h % hkv;\n"),
+    ("decode slot index", "int64_t slot = j % block_size;", "int64_t slot = (j + 1) % block_size;"),
+    ("V read with K operand", "out[c] += p * load_elem(v,", "out[c] += p * load_elem(k,"),
+    ("scale dropped", "s[a] = scale * dot;", "s[a] = dot;"),
+    ("first weight dropped from Z", "z += s[a];", "if (a) z += s[a];"),
+    ("lse misses max", "*lse = m + log(z);", "*lse = log(z);"),
+    ("decode window ignored", "if (!allowed(i, j, window, -1, -1)) continue;",
+     "if (!allowed(i, j, -1, -1, -1)) continue;"),
+    ("transposed query/key offset", "load_elem(q, qt, q_off + c) * load_elem(k, kvt, key_off[a] + c)",
+     "load_elem(q, qt, q_off + c) * load_elem(k, kvt, key_off[n - 1 - a] + c)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    assert src.count(old) >= 1, f"mutation site for {name!r} not found"
+    mutated = tmp_path / "oracle_mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = oracle.build(src=str(mutated), out=str(tmp_path / "liboracle_mutant.so"), werror=False)
+    lib = oracle.open_library(so)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name!r}"
