@@ -1,0 +1,190 @@
+/*
+ * invattn.h -- C ABI of the batch-invariant attention forward library
+ * (libinvattn.so, HIP for gfx950 / MI355X).
+ *
+ * Contract followed throughout ("RFC: Gemma-4-31B-it train/rollout
+ * consistency", section 4 "Numerical contract"): every reduction has a
+ * declared fp32 accumulator and an order that does not depend on batch
+ * size, batch position, packing, launch geometry, CU count or occupancy;
+ * no Split-K, Stream-K or cross-workgroup atomics (decode uses a split-KV
+ * whose chunk size and merge order are fixed constants, declared below);
+ * no fast-math; casts only at the three declared points; unsupported
+ * geometry fails closed with an error and never falls back to another path.
+ *
+ * Arithmetic, for each query row i with allowed key set A_i:
+ *   s_j  = fp32 MFMA dot product of bf16 q_i and bf16 k_j (d ascending in
+ *          16-element MFMA steps), then s_j * c with c = fl32(scale*log2(e))
+ *   m    = running max over the keys visited so far (fp32, exact)
+ *   p_j  = exp2(s_j * c - m)          (hardware exp2, fp32)
+ *   l    = l * exp2(m_old - m) + sum_j p_j        (fp32, fixed order)
+ *   acc  = acc * exp2(m_old - m) + bf16(p) . v    (bf16 MFMA, fp32 acc)
+ *   o    = bf16_rne(acc / l)          (IEEE fp32 division)
+ * KV tiles are visited in one ascending order per query row.  Declared casts:
+ * inputs are bf16 as given; p -> bf16 (round to nearest even) before the PV
+ * product; o -> bf16 (round to nearest even).
+ *
+ * Threading: stateless apart from the thread-local error text and
+ * provenance record; calls from several host threads are safe.
+ * Memory: the library allocates nothing; every buffer is caller-owned
+ * device memory.  Calls enqueue on the caller's stream and return without
+ * synchronising (except when INVATTN_VALIDATE=1, see below).
+ */
+#ifndef INVATTN_H
+#define INVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Window value meaning "no window": a global (full causal) layer. */
+#define ATTN_WINDOW_NONE (-1)
+
+/* Decode split: keys are cut into chunks of this many positions, aligned to
+ * position 0, whatever the batch; partial results merge in ascending chunk
+ * order.  A fixed constant of the library. */
+#define ATTN_DECODE_CHUNK 512
+
+/* Return codes. */
+enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = 1,        /* a required pointer is NULL */
+  ATTN_E_SHAPE = 2,       /* non-positive or inconsistent sizes */
+  ATTN_E_UNSUPPORTED = 3, /* geometry outside the strict contract */
+  ATTN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  ATTN_E_WORKSPACE = 5,   /* decode workspace too small */
+  ATTN_E_HIP = 6,         /* a HIP runtime call or launch failed */
+  ATTN_E_VALIDATE = 7     /* device-side index content failed validation */
+};
+
+/*
+ * attn_prefill_varlen -- attention forward over packed variable-length
+ * sequences (sliding-window or global layer, GQA, optional bidirectional
+ * spans).
+ *
+ * Passages: sliding and global attention cores as separate layer types
+ * ("RFC: Gemma-4-31B-it train/rollout consistency", section 3 "Architecture
+ * map" and section 6, items sliding_attention_core / global_attention_core);
+ * bidirectional vision-token spans (same page, section 1, Phase B; contiguous
+ * soft-token runs per "Gemma-4-E4B-it multimodal baseline", commit log);
+ * per-row invariance to unrelated rows and packing (section 4, items 2 and 6).
+ *
+ * Arguments (all device pointers caller-owned, bf16 = 16-bit bfloat):
+ *   q          bf16 [T, num_q_heads, head_dim], contiguous, 16-byte aligned
+ *   k, v       bf16 [T, num_kv_heads, head_dim], contiguous, 16-byte aligned
+ *   o          bf16 [T, num_q_heads, head_dim] output; rows of tokens outside
+ *              every sequence (T beyond cu_seqlens[batch]) are not written
+ *   lse_opt    fp32 [T, num_q_heads] natural-log sum of exp(scale*q.k) over
+ *              each row's allowed keys, or NULL
+ *   cu_seqlens int32 [batch+1] on the device; sequence b holds packed tokens
+ *              [cu_seqlens[b], cu_seqlens[b+1]); non-decreasing, starting at 0
+ *   batch      number of sequences (0 -> nothing enqueued, returns ATTN_OK)
+ *   max_seqlen host upper bound on every sequence length; sizes the grid only
+ *              (any bound >= the true maximum gives identical output bytes)
+ *   num_q_heads, num_kv_heads: GQA with contiguous groups, query head h reads
+ *              KV head h / (num_q_heads / num_kv_heads)
+ *   head_dim   64, 256 or 512
+ *   window     ATTN_WINDOW_NONE, or W >= 1: key j is allowed for query i of
+ *              the same sequence when 0 <= i - j < W
+ *   softmax_scale  finite and > 0 (normally 1/sqrt(head_dim))
+ *   spans_opt  int32 [num_spans][2] on the device: packed [start, end) ranges,
+ *              each inside one sequence, sorted and disjoint; every query of a
+ *              span also sees every key of the span (whatever the window).
+ *              NULL when num_spans == 0.  Malformed spans cannot make
+ *              the kernel read out of bounds (ranges are clamped to the
+ *              sequence) but give unspecified masks; INVATTN_VALIDATE=1
+ *              rejects them.
+ *   stream     HIP stream (hipStream_t) the work is enqueued on; 0 = default
+ *
+ * Supported: group size num_q_heads/num_kv_heads in {1, 2, 4, 8}.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED, ATTN_E_ALIGN,
+ * ATTN_E_HIP, ATTN_E_VALIDATE; nothing is enqueued on error and
+ * attn_last_error() names the argument.
+ */
+int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
+                        float* lse_opt, const int32_t* cu_seqlens,
+                        int32_t batch, int32_t max_seqlen,
+                        int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t window, float softmax_scale,
+                        const int32_t* spans_opt, int32_t num_spans,
+                        void* stream);
+
+/*
+ * attn_decode_workspace_size -- bytes of fp32 workspace attn_decode_paged
+ * needs for this batch: [batch, num_q_heads, ceil(max_seq_len /
+ * ATTN_DECODE_CHUNK), head_dim + 4] fp32 (per chunk record: the unnormalised
+ * accumulator, the running max, the running sum, one pad word keeping records
+ * 16-byte aligned).  Pure function; returns 0 for non-positive arguments.
+ */
+size_t attn_decode_workspace_size(int32_t batch, int32_t max_seq_len,
+                                  int32_t num_q_heads, int32_t head_dim);
+
+/*
+ * attn_decode_paged -- one query token per sequence against a paged KV
+ * cache, read in place through the block table.
+ *
+ * Passages: strict decode consumes the paged KV cache directly, with a fixed
+ * schedule ("Vime ROCm Attention operator ablation", sections "Prerequisites"
+ * and "Runtime artifacts and validation"); split-KV only with a fixed split
+ * and merge tree ("RFC: Gemma-4-31B-it train/rollout consistency", section 4,
+ * item 3); hybrid_kv_cache_contract (same page, section 6).
+ *
+ * Arguments (device pointers caller-owned):
+ *   q            bf16 [batch, num_q_heads, head_dim], contiguous
+ *   k_cache, v_cache  bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_table  int32 [batch, max_blocks_per_seq]; key j of sequence b is in
+ *                block block_table[b][j / block_size], slot j % block_size.
+ *                Entries for blocks outside the attended key range are never
+ *                read.
+ *   seq_lens     int32 [batch], each in [1, max_seq_len]; counts the current
+ *                token, whose K/V is already in the cache; the query is
+ *                position seq_lens[b] - 1
+ *   batch        >= 0 (0 -> nothing enqueued)
+ *   max_seq_len  host bound on every seq_lens entry (sizes grid/workspace)
+ *   num_blocks   number of physical blocks in each cache
+ *   block_size   must be 16
+ *   num_q_heads, num_kv_heads, head_dim, window, softmax_scale: as prefill
+ *   workspace    fp32 scratch of at least attn_decode_workspace_size(...)
+ *                bytes, 16-byte aligned; its contents need no initialisation
+ *                and are overwritten
+ *   o            bf16 [batch, num_q_heads, head_dim] output
+ *   stream       HIP stream
+ * Two kernels run on the stream: a chunk kernel (one workgroup per
+ * ATTN_DECODE_CHUNK keys of one KV head of one sequence) writes partial
+ * (max, sum, acc) records, then a merge kernel folds the chunks of each
+ * (sequence, head) in ascending chunk order.  No atomics.
+ * Errors: as prefill, plus ATTN_E_WORKSPACE.
+ */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* seq_lens, int32_t batch,
+                      int32_t max_seq_len, int32_t num_blocks,
+                      int32_t block_size, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                      float softmax_scale, void* workspace,
+                      size_t workspace_bytes, void* o, void* stream);
+
+/* Text of the last failure on this thread ("" if none).  The pointer stays
+ * valid until the next call on this thread. */
+const char* attn_last_error(void);
+
+/*
+ * Provenance record of the last successful call on this thread
+ * ("RFC: Gemma-4-31B-it train/rollout consistency", section 4, item 8):
+ * JSON with requested/actual backend, kernel id, schedule id (tile sizes),
+ * split policy, accumulator dtype, layer type, device, dtype, shape
+ * fingerprint and fallback state.  Writes at most n bytes including the
+ * terminating NUL; returns the full length, or -1 if no call succeeded yet.
+ */
+int attn_last_provenance(char* buf, size_t n);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INVATTN_H */

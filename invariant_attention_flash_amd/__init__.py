@@ -1,2 +1,195 @@
-"""Batch-invariant attention forward for MI355X (gfx950): packed varlen
-prefill and paged-KV decode behind a C-ABI library (``libinvattn.so``)."""
+"""Batch-invariant attention forward for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libinvattn.so`` (declared in
+``include/invattn.h``): argument marshalling only.  Every step of the
+attention runs in the library's HIP kernels; PyTorch supplies device memory
+and the current stream.  There is no fallback path: if the library is not
+built, or the GPU is missing, calls raise.
+
+Entry points (same names as the C ABI):
+  attn_prefill_varlen  packed variable-length prefill, sliding or global,
+                       GQA, optional bidirectional spans
+  attn_decode_paged    one query token per sequence over a paged KV cache
+  attn_decode_workspace_size
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+__all__ = ["attn_prefill_varlen", "attn_decode_paged", "attn_decode_workspace_size",
+           "last_provenance", "last_error", "AttnError", "library", "LIB_PATH",
+           "ATTN_WINDOW_NONE", "ATTN_DECODE_CHUNK", "ERROR_CODES", "EXPORTS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinvattn.so")
+ATTN_WINDOW_NONE = -1
+ATTN_DECODE_CHUNK = 512
+ERROR_CODES = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
+               4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP", 7: "ATTN_E_VALIDATE"}
+EXPORTS = ["attn_prefill_varlen", "attn_decode_workspace_size", "attn_decode_paged",
+           "attn_last_error", "attn_last_provenance", "attn_version"]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_CODES.get(code, code)}: {message}")
+        self.code = code
+        self.name = ERROR_CODES.get(code, str(code))
+
+
+_lib = None
+
+
+def library():
+    """Load ``libinvattn.so`` (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(there is no fallback path)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        lib.attn_prefill_varlen.restype = ctypes.c_int
+        lib.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, f32, vp, i32, vp]
+        lib.attn_decode_workspace_size.restype = sz
+        lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.attn_decode_paged.restype = ctypes.c_int
+        lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, f32, vp, sz, vp, vp]
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_last_error.argtypes = []
+        lib.attn_last_provenance.restype = ctypes.c_int
+        lib.attn_last_provenance.argtypes = [ctypes.c_char_p, sz]
+        lib.attn_version.restype = ctypes.c_char_p
+        lib.attn_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return library().attn_last_error().decode()
+
+
+def last_provenance():
+    """Provenance record (dict) of the last successful call on this thread."""
+    lib = library()
+    n = lib.attn_last_provenance(None, 0)
+    if n < 0:
+        return None
+    buf = ctypes.create_string_buffer(n + 1)
+    lib.attn_last_provenance(buf, n + 1)
+    return json.loads(buf.value.decode())
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise AttnError(rc, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, dtype, dim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+
+
+def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, window=ATTN_WINDOW_NONE,
+                        softmax_scale=None, spans=None, out=None, lse=None, stream=None):
+    """Packed varlen prefill.
+
+    q [T, Hq, D], k/v [T, Hkv, D] bf16 CUDA tensors; cu_seqlens int32 [B+1];
+    spans int32 [S, 2] packed [start, end) bidirectional ranges or None;
+    out bf16 [T, Hq, D] (allocated if None); lse fp32 [T, Hq] or None.
+    Returns out.
+    """
+    import torch
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k, "k", torch.bfloat16, 3)
+    _require(v, "v", torch.bfloat16, 3)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != T or k.shape[2] != d:
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 2)
+    ns = 0
+    if spans is not None:
+        _require(spans, "spans", torch.int32, 2)
+        ns = spans.shape[0]
+        if ns == 0:
+            spans = None
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    rc = library().attn_prefill_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+        cu_seqlens.shape[0] - 1, int(max_seqlen), hq, hkv, d, int(window),
+        float(softmax_scale), _ptr(spans), ns, _stream(stream))
+    _check(rc)
+    return out
+
+
+def attn_decode_workspace_size(batch, max_seq_len, num_q_heads, head_dim) -> int:
+    return int(library().attn_decode_workspace_size(batch, max_seq_len, num_q_heads, head_dim))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
+                      window=ATTN_WINDOW_NONE, softmax_scale=None, workspace=None, out=None,
+                      stream=None):
+    """Paged decode.
+
+    q [B, Hq, D] bf16; k_cache/v_cache [NB, 16, Hkv, D] bf16; block_table
+    int32 [B, MB]; seq_lens int32 [B] (current token included);
+    workspace: uint8/fp32 CUDA tensor of at least attn_decode_workspace_size
+    bytes (allocated if None); out bf16 [B, Hq, D].  Returns out.
+    """
+    import torch
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, 4)
+    _require(block_table, "block_table", torch.int32, 2)
+    _require(seq_lens, "seq_lens", torch.int32, 1)
+    B, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d:
+        raise ValueError("caches must be [NB, BS, Hkv, D] matching q")
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    need = attn_decode_workspace_size(B, int(max_seq_len), hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    wbytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", torch.bfloat16, 3)
+    rc = library().attn_decode_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), B, int(max_seq_len), nb, bs, hq, hkv, d, int(window),
+        float(softmax_scale), _ptr(workspace), wbytes, _ptr(out), _stream(stream))
+    _check(rc)
+    return out

@@ -1,0 +1,93 @@
+// device_common.h -- gfx950 building blocks shared by the prefill and decode
+// kernels: vector types, bf16 MFMA wrappers, the LDS transpose read, the
+// cross-half lane exchange and the declared conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace invattn {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr float kNegInf = -__builtin_inff();
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Operand layout (lane l): A row l%32, k 8*(l/32)+s; B column l%32, same k.
+// Result: lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Operand layout (lane l): A row l%16, k 8*(l/16)+s; B column l%16, same k.
+// Result: lane l holds column l%16, rows 4*(l/16) + i, i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte load from global memory as 8 bf16.
+__device__ __forceinline__ bf16x8 ld_global_x8(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// 16-byte load from LDS.
+__device__ __forceinline__ bf16x8 ld_lds_x8(const bf16* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4a+c receives element c of the 4-element rows addressed by lanes
+// a, a+4, a+8, a+12 of the group (as result elements 0..3).
+__device__ __forceinline__ bf16x4 ld_lds_tr(const bf16* p) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+  return __builtin_bit_cast(bf16x4, t);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Values of lanes l and l^32 as (low-half lane's value, high-half lane's
+// value), identical in both lanes.
+struct HalfPair {
+  float lo, hi;
+};
+__device__ __forceinline__ HalfPair half_pair(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return HalfPair{__builtin_bit_cast(float, (uint32_t)r[0]),
+                  __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+
+// Declared cast: fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Find the span holding packed token `tok` in a sorted, disjoint list of
+// [start, end) pairs.  Returns true and the bounds if found.
+__device__ __forceinline__ bool find_span(const int32_t* __restrict__ spans, int n, int tok,
+                                          int& s, int& e) {
+  int lo = 0, hi = n;  // first span with start > tok
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (spans[2 * mid] <= tok) lo = mid + 1; else hi = mid;
+  }
+  if (lo == 0) return false;
+  int a = spans[2 * (lo - 1)], b = spans[2 * (lo - 1) + 1];
+  if (tok < b) { s = a; e = b; return true; }
+  return false;
+}
+
+}  // namespace invattn

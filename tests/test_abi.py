@@ -1,0 +1,138 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares, and rejects unsupported geometry before touching the GPU
+(fail closed, "RFC: Gemma-4-31B-it train/rollout consistency", section 4,
+item 7).  No GPU work is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_attention_flash_amd as ia
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "invattn.h")
+
+E = {v: k for k, v in ia.ERROR_CODES.items()}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_library_builds_and_loads():
+    assert os.path.exists(ia.LIB_PATH)
+    assert ia.library().attn_version().decode().startswith("invattn")
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ia.EXPORTS), names
+    lib = ctypes.CDLL(ia.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_size_formula():
+    f = ia.attn_decode_workspace_size
+    assert f(64, 32768, 32, 512) == 64 * 32 * 64 * (512 + 4) * 4
+    assert f(1, 1, 32, 512) == 32 * 1 * 516 * 4
+    assert f(1, 513, 8, 256) == 8 * 2 * 260 * 4
+    assert f(0, 10, 8, 64) == 0
+    assert f(3, 0, 8, 64) == 0
+
+
+def call_prefill(**kw):
+    a = dict(q=1 << 20, k=1 << 20, v=1 << 20, o=1 << 20, lse=None, cu=1 << 20, batch=2,
+             max_seqlen=16, hq=4, hkv=2, d=64, window=-1, scale=0.125, spans=None, ns=0)
+    a.update(kw)
+    ptr = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = ia.library().attn_prefill_varlen(
+        ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["o"]), ptr(a["lse"]), ptr(a["cu"]),
+        a["batch"], a["max_seqlen"], a["hq"], a["hkv"], a["d"], a["window"], a["scale"],
+        ptr(a["spans"]), a["ns"], None)
+    return rc, ia.last_error()
+
+
+# Each case fails in argument checking, before any HIP call.
+PREFILL_ERRORS = [
+    (dict(q=None), "ATTN_E_NULL", "q is NULL"),
+    (dict(k=None), "ATTN_E_NULL", "k is NULL"),
+    (dict(v=None), "ATTN_E_NULL", "v is NULL"),
+    (dict(o=None), "ATTN_E_NULL", "o is NULL"),
+    (dict(cu=None), "ATTN_E_NULL", "cu_seqlens"),
+    (dict(ns=2, spans=None), "ATTN_E_NULL", "spans_opt"),
+    (dict(batch=-1), "ATTN_E_SHAPE", "batch"),
+    (dict(max_seqlen=-5), "ATTN_E_SHAPE", "max_seqlen"),
+    (dict(hq=6, hkv=4), "ATTN_E_SHAPE", "multiple"),
+    (dict(hq=0), "ATTN_E_SHAPE", "positive"),
+    (dict(hq=32, hkv=2), "ATTN_E_UNSUPPORTED", "group"),
+    (dict(hq=12, hkv=4), "ATTN_E_UNSUPPORTED", "group"),
+    (dict(d=128), "ATTN_E_UNSUPPORTED", "head_dim"),
+    (dict(d=96), "ATTN_E_UNSUPPORTED", "head_dim"),
+    (dict(window=0), "ATTN_E_UNSUPPORTED", "window"),
+    (dict(window=-7), "ATTN_E_UNSUPPORTED", "window"),
+    (dict(scale=0.0), "ATTN_E_UNSUPPORTED", "softmax_scale"),
+    (dict(scale=float("nan")), "ATTN_E_UNSUPPORTED", "softmax_scale"),
+    (dict(scale=float("inf")), "ATTN_E_UNSUPPORTED", "softmax_scale"),
+    (dict(q=(1 << 20) + 8), "ATTN_E_ALIGN", "q is not 16-byte"),
+    (dict(o=(1 << 20) + 2), "ATTN_E_ALIGN", "o is not 16-byte"),
+    (dict(cu=(1 << 20) + 2), "ATTN_E_ALIGN", "cu_seqlens"),
+]
+
+
+@pytest.mark.parametrize("kw,code,text", PREFILL_ERRORS, ids=[c[2] + str(i) for i, c in enumerate(PREFILL_ERRORS)])
+def test_prefill_rejects(kw, code, text):
+    rc, msg = call_prefill(**kw)
+    assert ia.ERROR_CODES[rc] == code, (rc, msg)
+    assert text in msg
+
+
+def call_decode(**kw):
+    a = dict(q=1 << 20, kc=1 << 20, vc=1 << 20, bt=1 << 20, mb=4, sl=1 << 20, batch=2, msl=64,
+             nb=100, bs=16, hq=32, hkv=4, d=512, window=-1, scale=0.04, ws=1 << 20,
+             wsb=1 << 30, o=1 << 20)
+    a.update(kw)
+    ptr = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = ia.library().attn_decode_paged(
+        ptr(a["q"]), ptr(a["kc"]), ptr(a["vc"]), ptr(a["bt"]), a["mb"], ptr(a["sl"]), a["batch"],
+        a["msl"], a["nb"], a["bs"], a["hq"], a["hkv"], a["d"], a["window"], a["scale"],
+        ptr(a["ws"]), a["wsb"], ptr(a["o"]), None)
+    return rc, ia.last_error()
+
+
+DECODE_ERRORS = [
+    (dict(q=None), "ATTN_E_NULL", "q is NULL"),
+    (dict(kc=None), "ATTN_E_NULL", "k_cache"),
+    (dict(vc=None), "ATTN_E_NULL", "v_cache"),
+    (dict(bt=None), "ATTN_E_NULL", "block_table"),
+    (dict(sl=None), "ATTN_E_NULL", "seq_lens"),
+    (dict(ws=None), "ATTN_E_NULL", "workspace"),
+    (dict(o=None), "ATTN_E_NULL", "o is NULL"),
+    (dict(bs=32), "ATTN_E_UNSUPPORTED", "block_size"),
+    (dict(d=128), "ATTN_E_UNSUPPORTED", "head_dim"),
+    (dict(hq=64, hkv=4), "ATTN_E_UNSUPPORTED", "group"),
+    (dict(window=0), "ATTN_E_UNSUPPORTED", "window"),
+    (dict(msl=0), "ATTN_E_SHAPE", "max_seq_len"),
+    (dict(mb=3), "ATTN_E_SHAPE", "max_blocks_per_seq"),
+    (dict(nb=0), "ATTN_E_SHAPE", "num_blocks"),
+    (dict(wsb=100), "ATTN_E_WORKSPACE", "workspace_bytes"),
+    (dict(ws=(1 << 20) + 4), "ATTN_E_ALIGN", "workspace"),
+    (dict(kc=(1 << 20) + 2), "ATTN_E_ALIGN", "k_cache"),
+]
+
+
+@pytest.mark.parametrize("kw,code,text", DECODE_ERRORS, ids=[c[2] + str(i) for i, c in enumerate(DECODE_ERRORS)])
+def test_decode_rejects(kw, code, text):
+    rc, msg = call_decode(**kw)
+    assert ia.ERROR_CODES[rc] == code, (rc, msg)
+    assert text in msg
+
+
+def test_error_text_is_per_call():
+    rc, msg = call_prefill(d=96)
+    assert rc != 0 and "head_dim" in msg
+    rc, msg = call_prefill(window=0)
+    assert "window" in msg and "head_dim" not in msg
