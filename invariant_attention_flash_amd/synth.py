@@ -270,3 +270,85 @@ def decode_case(seed=4, lengths=None, batch=64, hq=32, hkv=4, d=512, block_size=
         sl[pos] = L
     return DecodeCase(q, kc, vc, bt, sl, hq, hkv, d, block_size, window,
                       1.0 / float(np.sqrt(d)))
+
+
+# --------------------------------------------------------------------------
+# device-side generation for the full-size paged decode workload
+# --------------------------------------------------------------------------
+def decode_case_device(seed=4, lengths=None, batch=64, hq=32, hkv=4, d=512, block_size=16,
+                       std=0.5, spare_blocks=64, placement_seed=0, poison=True, device="cuda"):
+    """The paged decode batch built directly in GPU memory (torch).
+
+    Values come from torch's device generator seeded per sequence
+    (``seed * 1_000_003 + i``), so sequence i holds the same bits at any batch
+    size; they are NOT the same bits as ``decode_case`` (numpy).  Lengths and
+    physical block placement use the same numpy streams as ``decode_case``.
+    Returns a dict of device tensors plus the host block table and lengths.
+    """
+    import torch
+    if lengths is None:
+        lengths = decode_lengths(seed, batch)
+    lengths = list(lengths)[:batch]
+    nblk = [(L + block_size - 1) // block_size for L in lengths]
+    total_blocks = sum(nblk) + spare_blocks
+    mb = max(nblk)
+    fill = float("nan") if poison else 0.0
+    kc = torch.full((total_blocks, block_size, hkv, d), fill, dtype=torch.bfloat16, device=device)
+    vc = torch.full((total_blocks, block_size, hkv, d), fill, dtype=torch.bfloat16, device=device)
+    prng = np.random.default_rng([seed, 0, 11, placement_seed])
+    phys = prng.permutation(total_blocks).astype(np.int32)
+    bt = np.full((len(lengths), mb), total_blocks + 7 if poison else 0, np.int32)
+    q = torch.empty((len(lengths), hq, d), dtype=torch.bfloat16, device=device)
+    cursor = 0
+    for i, L in enumerate(lengths):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 1_000_003 + i)
+        q[i] = (torch.randn((hq, d), generator=g, device=device) * std).to(torch.bfloat16)
+        ids = phys[cursor:cursor + nblk[i]]
+        cursor += nblk[i]
+        bt[i, :nblk[i]] = ids
+        pad = nblk[i] * block_size
+        kk = torch.full((pad, hkv, d), fill, dtype=torch.bfloat16, device=device)
+        vv = torch.full((pad, hkv, d), fill, dtype=torch.bfloat16, device=device)
+        kk[:L] = (torch.randn((L, hkv, d), generator=g, device=device) * std).to(torch.bfloat16)
+        vv[:L] = (torch.randn((L, hkv, d), generator=g, device=device) * std).to(torch.bfloat16)
+        idx = torch.from_numpy(ids.astype(np.int64)).to(device)
+        kc.index_copy_(0, idx, kk.view(nblk[i], block_size, hkv, d))
+        vc.index_copy_(0, idx, vv.view(nblk[i], block_size, hkv, d))
+    return {"q": q, "k_cache": kc, "v_cache": vc, "block_table": bt,
+            "seq_lens": np.array(lengths, np.int32), "hq": hq, "hkv": hkv, "d": d,
+            "block_size": block_size, "scale": 1.0 / float(np.sqrt(d))}
+
+
+def prefill_case_device(seed, lengths, hq, hkv, d, window, std=0.5, spans=None, order=None,
+                        device="cuda"):
+    """A packed prefill batch built directly in GPU memory (torch).
+
+    Sequence i draws from torch's device generator seeded with
+    ``seed * 1_000_003 + i``, so it holds the same bits in any batch and at
+    any position (not the same bits as ``prefill_case``).  Returns a dict with
+    device tensors q, k, v, cu_seqlens (int32) and spans (int32 [S, 2] or
+    None), plus host copies of cu_seqlens and spans.
+    """
+    import torch
+    lengths = [int(L) for L in lengths]
+    order = list(range(len(lengths))) if order is None else list(order)
+    qs, ks, vs, sp = [], [], [], []
+    cu = np.zeros(len(order) + 1, np.int32)
+    for pos, i in enumerate(order):
+        L = lengths[i]
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 1_000_003 + i)
+        qs.append((torch.randn((L, hq, d), generator=g, device=device) * std).to(torch.bfloat16))
+        ks.append((torch.randn((L, hkv, d), generator=g, device=device) * std).to(torch.bfloat16))
+        vs.append((torch.randn((L, hkv, d), generator=g, device=device) * std).to(torch.bfloat16))
+        cu[pos + 1] = cu[pos] + L
+        if spans:
+            sp += [(int(cu[pos]) + a, int(cu[pos]) + b) for a, b in spans[i]]
+    spans_np = np.array(sp, np.int32).reshape(-1, 2)
+    return {"q": torch.cat(qs), "k": torch.cat(ks), "v": torch.cat(vs),
+            "cu_seqlens": torch.from_numpy(cu).to(device), "cu_host": cu,
+            "spans": torch.from_numpy(spans_np).to(device) if len(sp) else None,
+            "spans_host": spans_np, "max_seqlen": max(lengths) if lengths else 0,
+            "hq": hq, "hkv": hkv, "d": d, "window": window, "scale": 1.0 / float(np.sqrt(d)),
+            "lengths": [lengths[i] for i in order]}
