@@ -69,6 +69,33 @@ __device__ __forceinline__ HalfPair half_pair(float x) {
                   __builtin_bit_cast(float, (uint32_t)r[1])};
 }
 
+// Wait until every vector-memory load of this wave (including direct
+// HBM -> LDS loads) has completed.
+__device__ __forceinline__ void wait_vmem() {
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// acc *= a.  With one wave per SIMD the accumulators live in AGPRs; the
+// scaling is written on AGPR operands so they stay there (each element moves
+// to a VGPR, is multiplied, and moves back).
+template <int OCC>
+__device__ __forceinline__ void scale_acc(f32x16& acc, float a) {
+  if constexpr (OCC == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float t;
+      __asm__ volatile(
+          "v_accvgpr_read_b32 %1, %0\n\t"
+          "v_mul_f32 %1, %1, %2\n\t"
+          "v_accvgpr_write_b32 %0, %1"
+          : "+a"(acc[i]), "=&v"(t)
+          : "v"(a));
+    }
+  } else {
+    acc *= a;
+  }
+}
+
 // Declared cast: fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 

@@ -19,52 +19,99 @@
 // same ascending order, whatever else is in the batch.
 //
 // Per KV tile (BN keys, ascending):
+//   K and V tiles stream HBM -> LDS with direct loads (global_load_lds,
+//   16 B per lane), double-buffered so the next tile lands while this one is
+//   computed; rows are stored unpadded with an XOR swizzle of their 16-byte
+//   chunks (conflict-free MFMA operand reads).  Keys past the sequence end
+//   read the sequence's last row and are masked (p = 0).
 //   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q in
 //                registers), so each lane holds one query's scores;
 //   scale by c = fl32(scale*log2 e), mask by select (-inf);
-//   online softmax in fp32: tile max and row sums reduce first inside the
-//                lane in register order, then across the lane pair (l, l^32);
-//   P -> bf16 (RNE), O^T += V^T P^T on the same MFMA, with V^T read from a
+//   online softmax in fp32 with a per-row reference max m: m moves (and the
+//                running sum and accumulator are rescaled by 2^(m_old-m_new))
+//                only when the tile max exceeds m by more than kRescale, so
+//                p = 2^(s*c - m) <= 2^kRescale; the tile max and the row sum
+//                reduce inside the lane in register order, then across the
+//                lane pair (l, l^32);
+//   P -> bf16 (RNE), O^T += V^T P^T on the same MFMA, with V^T read from the
 //                row-major LDS tile by the LDS transpose read.
-// Fully masked tiles are exact no-ops (alpha = 1, p = 0), so a wave skips
-// the tiles outside its own key range and skips the O rescale when every
-// alpha of the wave is 1; both skips depend only on the sequence.
+// Every decision (skip a tile, move m, rescale) is a function of the row's
+// own sequence, so the bytes of a row never depend on the rest of the batch.
 #include "device_common.h"
 #include "kernels.h"
 
+
 namespace invattn {
 
-template <int D_, int G_, int BN_>
+// Reference-max hysteresis (log2 units): m moves only when a tile max
+// exceeds it by more than this.  A fixed constant of the arithmetic.
+constexpr float kRescale = 8.0f;
+
+
+
+template <int D_, int G_, int BN_, int OCC_>
 struct PrefillCfg {
-  static constexpr int D = D_, G = G_, BN = BN_;
-  static constexpr int kThreads = 256;
-  static constexpr int kRows = 128;
+  static constexpr int D = D_, G = G_, BN = BN_, OCC = OCC_;
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = 32 * kWaves;
   static constexpr int kPositions = kRows / G;
   static constexpr int kPosPerWave = 32 / G;
-  static constexpr int kStrideK = D + 8;  // LDS row stride (elements)
-  static constexpr int kStrideV = D + 8;
-  static constexpr int kLdsElems = BN * (kStrideK + kStrideV);
+  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
+  static constexpr int kTile = BN * D;   // elements per K (or V) tile
+  static constexpr int kLdsElems = 2 * 2 * kTile;  // two buffers of K and V
+  static constexpr int kLoads = BN * kChunks / 64 / kWaves;  // direct loads per wave per tensor
   static constexpr int kSteps = D / 16;  // MFMA k-steps over the head dim
   static constexpr int kSBlk = BN / 32;  // 32-key score blocks per tile
   static constexpr int kDBlk = D / 32;   // 32-wide output blocks
   static constexpr int kKK = BN / 16;    // 16-key PV k-steps per tile
-  static constexpr int kChunkPerRow = D / 8;
-  static constexpr int kChunksPerThread = BN * D / 8 / kThreads;
+  static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
+  static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(BN * D / 8 % kThreads == 0, "tile load split");
+  static_assert(BN * kChunks % (64 * kWaves) == 0, "tile load split");
 };
 
+// Swizzled element offset of logical 16-byte chunk `lc` of LDS row `row`.
 template <class C>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__device__ __forceinline__ int k_off(int row, int lc) {
+  return row * C::D + ((lc ^ (row & C::kSwK)) << 3);
+}
+template <class C>
+__device__ __forceinline__ int v_off(int row, int lc) {
+  return row * C::D + ((lc ^ ((row << 1) & C::kSwV)) << 3);
+}
+
+// Direct HBM -> LDS loads of one K and one V tile (keys k0 .. k0+BN-1) into
+// buffer `buf`.  Lane offsets (elements, 32-bit; one sequence's K or V stays
+// below 4 GiB) are row*stride + swizzled chunk; keys past the sequence end
+// clamp to its last row (offset last_row).
+template <class C>
+__device__ __forceinline__ void issue_tile(bf16* smem, int buf, int k0, uint32_t rs,
+                                           uint32_t last_row, const uint32_t* ld_row,
+                                           const uint32_t* ld_ck, const uint32_t* ld_cv,
+                                           const bf16* kbase, const bf16* vbase, int wave) {
+  bf16* ks = smem + buf * 2 * C::kTile;
+  bf16* vs = ks + C::kTile;
+  const uint32_t base = (uint32_t)k0 * rs;
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    const int cbase = (wave * C::kLoads + i) * 64;
+    const uint32_t off = min(base + ld_row[i], last_row);
+    __builtin_amdgcn_global_load_lds(kbase + (off + ld_ck[i]), LDS_PTR(void, ks + cbase * 8), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + (off + ld_cv[i]), LDS_PTR(void, vs + cbase * 8), 16, 0, 0);
+  }
+}
+
+template <class C>
+__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads),
+                          amdgpu_waves_per_eu(C::OCC, C::OCC)))
 void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ v, bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                     const int32_t* __restrict__ spans, int num_spans, int hq, int hkv,
                     int window, float c2) {
   constexpr int D = C::D, G = C::G, BN = C::BN;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::kLdsElems];
-  bf16* Ks = smem;
-  bf16* Vs = smem + BN * C::kStrideK;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[C::kLdsElems];
 
   const int b = blockIdx.z, g = blockIdx.y;
   const int t = gridDim.x - 1 - blockIdx.x;  // longest causal tiles first
@@ -74,15 +121,18 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   if (p0 >= L) return;
   const int p1 = min(p0 + C::kPositions, L);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int n = lane & 31, hh = lane >> 5;
   const bool windowed = window > 0;
+  const int wlim = windowed ? window : 0x7fffffff;
 
   // This lane's query row.
   const int r = 32 * wave + n;
   const int qpos = p0 + r / G;
   const int qhead = g * G + (r % G);
   const bool qvalid = qpos < L;
+  const int qpos_m = qvalid ? qpos : -1;  // an invalid row admits no key
 
   int ss, se;
   // Key range of the workgroup: the window below its first row, the span
@@ -114,6 +164,29 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     my_se = min(se - seq0, L);
   }
 
+  const size_t row_stride = (size_t)hkv * D;
+  const bf16* kbase = k + ((size_t)seq0 * hkv + g) * D;
+  const bf16* vbase = v + ((size_t)seq0 * hkv + g) * D;
+
+  // Direct HBM -> LDS loads of one K and one V tile into buffer `buf`.
+  // Lane offsets (elements, 32-bit; one sequence's K or V stays below 4 GiB)
+  // are row*stride + swizzled chunk; keys past the sequence end clamp to its
+  // last row.
+  const uint32_t rs = (uint32_t)row_stride;
+  const uint32_t last_row = (uint32_t)(L - 1) * rs;
+  uint32_t ld_row[C::kLoads], ld_ck[C::kLoads], ld_cv[C::kLoads];
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    const int pch = (wave * C::kLoads + i) * 64 + lane;
+    const int row = pch / C::kChunks;
+    const int pc = pch % C::kChunks;
+    ld_row[i] = (uint32_t)row * rs;
+    ld_ck[i] = (uint32_t)((pc ^ (row & C::kSwK)) << 3);
+    ld_cv[i] = (uint32_t)((pc ^ ((row << 1) & C::kSwV)) << 3);
+  }
+  const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
+  issue_tile<C>(smem, 0, kt0 * BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase, vbase, wave);
+
   // Q^T operand: lane holds q[row][16*s + 8*hh .. +7] for every k-step s.
   bf16x8 qr[C::kSteps];
   {
@@ -130,101 +203,134 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (int db = 0; db < C::kDBlk; ++db) oacc[db] = f32x16{};
   float m = kNegInf, l = 0.f;
 
-  const size_t row_stride = (size_t)hkv * D;
-  const bf16* kbase = k + ((size_t)seq0 * hkv + g) * D;
-  const bf16* vbase = v + ((size_t)seq0 * hkv + g) * D;
+  // Per-lane LDS offsets that do not change across tiles.  K: this lane's
+  // row is n (+32*blk), logical chunk 2*s + hh, physical chunk
+  // (2*s + hh) ^ (n & kSwK) = 2*s ^ kx.  V: the transpose read of this lane
+  // starts at row vrow0 (+16*kk, +8), logical chunk 4*db + vc1, physical
+  // chunk (4*db + vc1) ^ (2*vrow0 & kSwV) = 4*db ^ vx.
+  const int kx = hh ^ (n & C::kSwK);
   const int qg = lane >> 4, lg = lane & 15;
+  const int vrow0 = 4 * (qg >> 1) + (lg >> 2);
+  const int vx = (2 * (qg & 1) + ((lg & 3) >> 1)) ^ ((vrow0 << 1) & C::kSwV);
+  const int vsub = (lg & 1) * 4;
 
-  const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
   for (int kt = kt0; kt < kt1; ++kt) {
     const int k0 = kt * BN;
+    const int buf = (kt - kt0) & 1;
+    // Tile kt landed once every wave has waited for its own direct loads;
+    // after the barrier nobody reads buffer buf^1 any more.
+    wait_vmem();
     __syncthreads();
-    // K and V tiles -> LDS, row-major; keys past the sequence end are zero.
-#pragma unroll
-    for (int i = 0; i < C::kChunksPerThread; ++i) {
-      const int c = tid + i * C::kThreads;
-      const int row = c / C::kChunkPerRow;
-      const int col = (c % C::kChunkPerRow) * 8;
-      const int key = k0 + row;
-      u32x4 kx = u32x4{}, vx = u32x4{};
-      if (key < L) {
-        kx = *reinterpret_cast<const u32x4*>(kbase + key * row_stride + col);
-        vx = *reinterpret_cast<const u32x4*>(vbase + key * row_stride + col);
-      }
-      *reinterpret_cast<u32x4*>(Ks + row * C::kStrideK + col) = kx;
-      *reinterpret_cast<u32x4*>(Vs + row * C::kStrideV + col) = vx;
-    }
-    __syncthreads();
+    if (kt + 1 < kt1)
+      issue_tile<C>(smem, buf ^ 1, k0 + BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase, vbase, wave);
     if (!wave_has_rows || k0 >= hi_w || k0 + BN <= lo_w) continue;
+    const bf16* ks = smem + buf * 2 * C::kTile;
+    const bf16* vs = ks + C::kTile;
 
-    // S^T = K Q^T: score block `blk` holds keys k0 + 32*blk + [0, 32).
-    f32x16 sacc[C::kSBlk];
-#pragma unroll
-    for (int blk = 0; blk < C::kSBlk; ++blk) {
-      sacc[blk] = f32x16{};
-      const bf16* krow = Ks + (32 * blk + n) * C::kStrideK + 8 * hh;
-#pragma unroll
-      for (int s = 0; s < C::kSteps; ++s)
-        sacc[blk] = mfma32(ld_lds_x8(krow + 16 * s), qr[s], sacc[blk]);
-    }
-
-    // Scale, mask by select, tile max.
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
-    float tmax = kNegInf;
+    // One tile: scores, masked or not (both bodies are the same arithmetic;
+    // the unmasked one omits selects that would keep every score).
+    {
+      // S^T = K Q^T: score block `blk` holds keys k0 + 32*blk + [0, 32).
+      f32x16 sacc[C::kSBlk];
 #pragma unroll
-    for (int blk = 0; blk < C::kSBlk; ++blk) {
+      for (int blk = 0; blk < C::kSBlk; ++blk) {
+        sacc[blk] = f32x16{};
+        const bf16* krow = ks + (32 * blk + n) * D;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = sacc[blk][i] * c2;
-        if (need_mask) {
-          const int j = k0 + 32 * blk + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const bool ok = qvalid && ((j <= qpos && (!windowed || qpos - j < window)) ||
-                                     (j >= my_ss && j < my_se));
-          x = ok ? x : kNegInf;
+        for (int s = 0; s < C::kSteps; ++s)
+          sacc[blk] = mfma32(ld_lds_x8(krow + (((2 * s) ^ kx) << 3)), qr[s], sacc[blk]);
+      }
+      {
+        constexpr int kN = C::kSBlk * C::kSteps, kAhead = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < kN - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        sacc[blk][i] = x;
-        tmax = fmaxf(tmax, x);
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
       }
-    }
-    HalfPair hp = half_pair(tmax);
-    tmax = fmaxf(hp.lo, hp.hi);
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
-    const float msub = (m_new == kNegInf) ? 0.f : m_new;
 
-    // p = exp2(s - m), row sum in register order, P -> bf16 operands.
-    float psum = 0.f;
-    bf16x8 pb[C::kKK];
+      // Scale, mask by select, tile max.  Interior tiles skip the selects
+      // (they would keep every score).
+      float tmax = kNegInf;
+      if (need_mask) {
 #pragma unroll
-    for (int blk = 0; blk < C::kSBlk; ++blk) {
+        for (int blk = 0; blk < C::kSBlk; ++blk) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(sacc[blk][i] - msub);
-        psum += p;
-        pb[2 * blk + (i >> 3)][i & 7] = to_bf16(p);
+          for (int i = 0; i < 16; ++i) {
+            const int j = k0 + 32 * blk + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const bool ok =
+                ((j <= qpos_m) & (qpos_m - j < wlim)) | ((j >= my_ss) & (j < my_se));
+            const float x = ok ? sacc[blk][i] * c2 : kNegInf;
+            sacc[blk][i] = x;
+            tmax = fmaxf(tmax, x);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < C::kSBlk; ++blk) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = sacc[blk][i] * c2;
+            sacc[blk][i] = x;
+            tmax = fmaxf(tmax, x);
+          }
+        }
       }
-    }
-    hp = half_pair(psum);
-    psum = hp.lo + hp.hi;
-    l = l * alpha + psum;
-    m = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < C::kDBlk; ++db) oacc[db] *= alpha;
-    }
+      HalfPair hp = half_pair(tmax);
+      tmax = fmaxf(hp.lo, hp.hi);
+      // Move the reference max only on a jump of more than kRescale.
+      const bool move = tmax > m + kRescale || (m == kNegInf && tmax != kNegInf);
+      const float m_new = move ? tmax : m;
+      const float alpha = move ? fast_exp2(m - m_new) : 1.f;
+      const float msub = (m_new == kNegInf) ? 0.f : m_new;
 
-    // O^T += V^T P^T.  PV k-step kk covers keys 16*kk + 8*(e/4) + 4*hh + e%4
-    // in operand slot e; the transpose read gathers exactly those rows.
+      // p = exp2(s - m), row sum in register order, P -> bf16 operands.
+      float psum = 0.f;
+      bf16x8 pb[C::kKK];
 #pragma unroll
-    for (int kk = 0; kk < C::kKK; ++kk) {
-      const bf16* vrow = Vs + (16 * kk + 4 * (qg >> 1) + (lg >> 2)) * C::kStrideV +
-                         16 * (qg & 1) + 4 * (lg & 3);
+      for (int blk = 0; blk < C::kSBlk; ++blk) {
 #pragma unroll
-      for (int db = 0; db < C::kDBlk; ++db) {
-        const bf16x4 lo4 = ld_lds_tr(vrow + 32 * db);
-        const bf16x4 hi4 = ld_lds_tr(vrow + 8 * C::kStrideV + 32 * db);
-        oacc[db] = mfma32(cat8(lo4, hi4), pb[kk], oacc[db]);
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(sacc[blk][i] - msub);
+          psum += p;
+          pb[2 * blk + (i >> 3)][i & 7] = to_bf16(p);
+        }
+      }
+      hp = half_pair(psum);
+      psum = hp.lo + hp.hi;
+      l = l * alpha + psum;
+      m = m_new;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < C::kDBlk; ++db) scale_acc<C::OCC>(oacc[db], alpha);
+      }
+
+      // O^T += V^T P^T.  PV k-step kk covers keys 16*kk + 8*(e/4) + 4*hh + e%4
+      // in operand slot e; the transpose read gathers exactly those rows.
+#pragma unroll
+      for (int kk = 0; kk < C::kKK; ++kk) {
+        const bf16* vrow = vs + (16 * kk + vrow0) * D + vsub;
+#pragma unroll
+        for (int db = 0; db < C::kDBlk; ++db) {
+          const int col = ((4 * db) ^ vx) << 3;
+          const bf16x4 lo4 = ld_lds_tr(vrow + col);
+          const bf16x4 hi4 = ld_lds_tr(vrow + 8 * D + col);
+          oacc[db] = mfma32(cat8(lo4, hi4), pb[kk], oacc[db]);
+        }
+      }
+      {
+        constexpr int kN = C::kKK * C::kDBlk, kAhead = 3;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
+#pragma unroll
+        for (int i = 0; i < kN - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 1);
       }
     }
   }
@@ -247,9 +353,9 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
-template <int D, int G, int BN>
+template <int D, int G, int BN, int OCC>
 static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-  using C = PrefillCfg<D, G, BN>;
+  using C = PrefillCfg<D, G, BN, OCC>;
   const int tiles = (a.max_seqlen + C::kPositions - 1) / C::kPositions;
   dim3 grid(tiles, a.hkv, a.batch);
   hipLaunchKernelGGL(prefill_kernel<C>, grid, dim3(C::kThreads), 0, stream,
@@ -258,14 +364,15 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One kernel instance per (head_dim, group); BN is fixed per instance.
-#define INVATTN_PREFILL_TABLE(X) \
-  X(64, 1, 64) X(64, 2, 64) X(64, 4, 64) X(64, 8, 64)      \
-  X(256, 1, 32) X(256, 2, 32) X(256, 4, 32) X(256, 8, 32)  \
-  X(512, 1, 32) X(512, 2, 32) X(512, 4, 32) X(512, 8, 32)
+// One kernel instance per (head_dim, group): keys per tile and waves per SIMD
+// are fixed per instance.
+#define INVATTN_PREFILL_TABLE(X)                                              \
+  X(64, 1, 64, 2) X(64, 2, 64, 2) X(64, 4, 64, 2) X(64, 8, 64, 2)             \
+  X(256, 1, 32, 2) X(256, 2, 32, 2) X(256, 4, 32, 2) X(256, 8, 32, 2)         \
+  X(512, 1, 32, 1) X(512, 2, 32, 1) X(512, 4, 32, 1) X(512, 8, 32, 1)
 
 bool prefill_schedule(int d, int group, PrefillSchedule* s) {
-#define X(D, G, BN)                                         \
+#define X(D, G, BN, OCC)                                    \
   if (d == D && group == G) {                               \
     *s = PrefillSchedule{128, 128 / G, BN, 256};            \
     return true;                                            \
@@ -277,8 +384,8 @@ bool prefill_schedule(int d, int group, PrefillSchedule* s) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
-#define X(D, G, BN) \
-  if (a.d == D && group == G) return launch_one<D, G, BN>(a, stream);
+#define X(D, G, BN, OCC) \
+  if (a.d == D && group == G) return launch_one<D, G, BN, OCC>(a, stream);
   INVATTN_PREFILL_TABLE(X)
 #undef X
   return hipErrorInvalidValue;
