@@ -49,26 +49,33 @@ constexpr float kRescale = 8.0f;
 
 
 
-template <int D_, int G_, int BN_, int OCC_>
+template <int D_, int G_, int BN_, int OCC_, int DSPLIT_>
 struct PrefillCfg {
-  static constexpr int D = D_, G = G_, BN = BN_, OCC = OCC_;
-  static constexpr int kWaves = 4;
+  static constexpr int D = D_, G = G_, BN = BN_, OCC = OCC_, DSPLIT = DSPLIT_;
+  static constexpr int kRowBlocks = 4;                 // 32-row blocks per workgroup
+  static constexpr int kWaves = kRowBlocks * DSPLIT;   // DSPLIT waves share a row block
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kRows = 32 * kWaves;
+  static constexpr int kRows = 32 * kRowBlocks;
   static constexpr int kPositions = kRows / G;
-  static constexpr int kPosPerWave = 32 / G;
-  static constexpr int kChunks = D / 8;  // 16-byte chunks per row
-  static constexpr int kTile = BN * D;   // elements per K (or V) tile
-  static constexpr int kLdsElems = 2 * 2 * kTile;  // two buffers of K and V
+  static constexpr int kPosPerBlock = 32 / G;
+  static constexpr int DW = D / DSPLIT;   // head-dim slice of one wave
+  static constexpr int kChunks = D / 8;   // 16-byte chunks per row
+  static constexpr int kTile = BN * D;    // elements per K (or V) tile
+  static constexpr int kKVElems = 2 * 2 * kTile;  // two buffers of K and V
+  // Partial-score exchange between the waves of a row block: fp32, one
+  // 16-float record per lane per wave.
+  static constexpr int kXchgFloats = DSPLIT > 1 ? kWaves * 64 * 16 * (BN / 32) : 0;
   static constexpr int kLoads = BN * kChunks / 64 / kWaves;  // direct loads per wave per tensor
-  static constexpr int kSteps = D / 16;  // MFMA k-steps over the head dim
-  static constexpr int kSBlk = BN / 32;  // 32-key score blocks per tile
-  static constexpr int kDBlk = D / 32;   // 32-wide output blocks
-  static constexpr int kKK = BN / 16;    // 16-key PV k-steps per tile
+  static constexpr int kSteps = DW / 16;  // MFMA k-steps over this wave's head-dim slice
+  static constexpr int kSBlk = BN / 32;   // 32-key score blocks per tile
+  static constexpr int kDBlk = DW / 32;   // 32-wide output blocks of this wave
+  static constexpr int kKK = BN / 16;     // 16-key PV k-steps per tile
   static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
   static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(BN % 32 == 0 && DW % 32 == 0, "tile shape");
   static_assert(BN * kChunks % (64 * kWaves) == 0, "tile load split");
+  static_assert(DSPLIT == 1 || DW / 8 >= 32, "head-dim slices start on a swizzle boundary");
+  static_assert(kKVElems * 2 + kXchgFloats * 4 <= 163840, "LDS budget");
 };
 
 // Swizzled element offset of logical 16-byte chunk `lc` of LDS row `row`.
@@ -110,8 +117,9 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                     const int32_t* __restrict__ spans, int num_spans, int hq, int hkv,
                     int window, float c2) {
-  constexpr int D = C::D, G = C::G, BN = C::BN;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[C::kLdsElems];
+  constexpr int D = C::D, G = C::G, BN = C::BN, DW = C::DW;
+  __shared__ __attribute__((aligned(1024))) bf16 smem[C::kKVElems + 2 * C::kXchgFloats];
+  float* xchg = reinterpret_cast<float*>(smem + C::kKVElems);
 
   const int b = blockIdx.z, g = blockIdx.y;
   const int t = gridDim.x - 1 - blockIdx.x;  // longest causal tiles first
@@ -123,12 +131,14 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int rb = wave / C::DSPLIT;   // row block of this wave
+  const int dh = wave % C::DSPLIT;   // head-dim slice of this wave
   const int n = lane & 31, hh = lane >> 5;
   const bool windowed = window > 0;
   const int wlim = windowed ? window : 0x7fffffff;
 
   // This lane's query row.
-  const int r = 32 * wave + n;
+  const int r = 32 * rb + n;
   const int qpos = p0 + r / G;
   const int qhead = g * G + (r % G);
   const bool qvalid = qpos < L;
@@ -144,10 +154,10 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (find_span(spans, num_spans, seq0 + p1 - 1, ss, se)) hi = max(hi, min(se - seq0, L));
   }
   // Key range of this wave's rows (used only to skip no-op tiles).
-  const int pw0 = p0 + wave * C::kPosPerWave;
-  const int pw1 = min(pw0 + C::kPosPerWave, L);
+  const int pw0 = p0 + rb * C::kPosPerBlock;
+  const int pw1 = min(pw0 + C::kPosPerBlock, L);
   const bool wave_has_rows = pw0 < L;
-  const bool wave_full = pw0 + C::kPosPerWave <= L;
+  const bool wave_full = pw0 + C::kPosPerBlock <= L;
   int lo_w = 0, hi_w = 0;
   if (wave_has_rows) {
     lo_w = windowed ? max(0, pw0 - window + 1) : 0;
@@ -190,7 +200,8 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Q^T operand: lane holds q[row][16*s + 8*hh .. +7] for every k-step s.
   bf16x8 qr[C::kSteps];
   {
-    const bf16* qrow = q + ((size_t)(seq0 + (qvalid ? qpos : 0)) * hq + qhead) * D + 8 * hh;
+    const bf16* qrow =
+        q + ((size_t)(seq0 + (qvalid ? qpos : 0)) * hq + qhead) * D + dh * DW + 8 * hh;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
       bf16x8 x = ld_global_x8(qrow + 16 * s);
@@ -223,35 +234,56 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     __syncthreads();
     if (kt + 1 < kt1)
       issue_tile<C>(smem, buf ^ 1, k0 + BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase, vbase, wave);
-    if (!wave_has_rows || k0 >= hi_w || k0 + BN <= lo_w) continue;
-    const bf16* ks = smem + buf * 2 * C::kTile;
-    const bf16* vs = ks + C::kTile;
-
+    const bool active = wave_has_rows && k0 < hi_w && k0 + BN > lo_w;
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
-    // One tile: scores, masked or not (both bodies are the same arithmetic;
-    // the unmasked one omits selects that would keep every score).
+    const bf16* ks = smem + buf * 2 * C::kTile;
+    const bf16* vs = ks + C::kTile;
     {
-      // S^T = K Q^T: score block `blk` holds keys k0 + 32*blk + [0, 32).
+      // S^T = K Q^T over this wave's head-dim slice: score block `blk` holds
+      // keys k0 + 32*blk + [0, 32).
       f32x16 sacc[C::kSBlk];
+      if (active) {
 #pragma unroll
-      for (int blk = 0; blk < C::kSBlk; ++blk) {
-        sacc[blk] = f32x16{};
-        const bf16* krow = ks + (32 * blk + n) * D;
+        for (int blk = 0; blk < C::kSBlk; ++blk) {
+          sacc[blk] = f32x16{};
+          const bf16* krow = ks + (32 * blk + n) * D + dh * DW;
 #pragma unroll
-        for (int s = 0; s < C::kSteps; ++s)
-          sacc[blk] = mfma32(ld_lds_x8(krow + (((2 * s) ^ kx) << 3)), qr[s], sacc[blk]);
-      }
-      {
-        constexpr int kN = C::kSBlk * C::kSteps, kAhead = 4;
-        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-        for (int i = 0; i < kN - kAhead; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int s = 0; s < C::kSteps; ++s)
+            sacc[blk] = mfma32(ld_lds_x8(krow + (((2 * s) ^ kx) << 3)), qr[s], sacc[blk]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        {
+          constexpr int kN = C::kSBlk * C::kSteps, kAhead = 4;
+          __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+          for (int i = 0; i < kN - kAhead; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+        }
+        if constexpr (C::DSPLIT > 1) {
+#pragma unroll
+          for (int blk = 0; blk < C::kSBlk; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              xchg[((wave * C::kSBlk + blk) * 16 + i) * 64 + lane] = sacc[blk][i];
+        }
       }
+      if constexpr (C::DSPLIT > 1) {
+        // Full scores = slice 0 + slice 1, added in that order by both waves.
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int blk = 0; blk < C::kSBlk; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float other = xchg[(((wave ^ 1) * C::kSBlk + blk) * 16 + i) * 64 + lane];
+              sacc[blk][i] = dh == 0 ? sacc[blk][i] + other : other + sacc[blk][i];
+            }
+        }
+      }
+      if (!active) continue;
 
       // Scale, mask by select, tile max.  Interior tiles skip the selects
       // (they would keep every score).
@@ -313,7 +345,7 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       // in operand slot e; the transpose read gathers exactly those rows.
 #pragma unroll
       for (int kk = 0; kk < C::kKK; ++kk) {
-        const bf16* vrow = vs + (16 * kk + vrow0) * D + vsub;
+        const bf16* vrow = vs + (16 * kk + vrow0) * D + dh * DW + vsub;
 #pragma unroll
         for (int db = 0; db < C::kDBlk; ++db) {
           const int col = ((4 * db) ^ vx) << 3;
@@ -337,7 +369,7 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // Epilogue: o = acc / l (IEEE fp32 division), bf16 RNE, store.
   if (qvalid) {
-    bf16* orow = o + ((size_t)(seq0 + qpos) * hq + qhead) * D + 4 * hh;
+    bf16* orow = o + ((size_t)(seq0 + qpos) * hq + qhead) * D + dh * DW + 4 * hh;
 #pragma unroll
     for (int db = 0; db < C::kDBlk; ++db) {
 #pragma unroll
@@ -348,14 +380,14 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * gi) = w;
       }
     }
-    if (lse != nullptr && hh == 0)
+    if (lse != nullptr && hh == 0 && dh == 0)
       lse[(size_t)(seq0 + qpos) * hq + qhead] = (m + fast_log2(l)) * 0.693147180559945309f;
   }
 }
 
-template <int D, int G, int BN, int OCC>
+template <int D, int G, int BN, int OCC, int DSPLIT>
 static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-  using C = PrefillCfg<D, G, BN, OCC>;
+  using C = PrefillCfg<D, G, BN, OCC, DSPLIT>;
   const int tiles = (a.max_seqlen + C::kPositions - 1) / C::kPositions;
   dim3 grid(tiles, a.hkv, a.batch);
   hipLaunchKernelGGL(prefill_kernel<C>, grid, dim3(C::kThreads), 0, stream,
@@ -364,18 +396,19 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One kernel instance per (head_dim, group): keys per tile and waves per SIMD
-// are fixed per instance.
-#define INVATTN_PREFILL_TABLE(X)                                              \
-  X(64, 1, 64, 2) X(64, 2, 64, 2) X(64, 4, 64, 2) X(64, 8, 64, 2)             \
-  X(256, 1, 32, 2) X(256, 2, 32, 2) X(256, 4, 32, 2) X(256, 8, 32, 2)         \
-  X(512, 1, 32, 1) X(512, 2, 32, 1) X(512, 4, 32, 1) X(512, 8, 32, 1)
+// One kernel instance per (head_dim, group): keys per tile, waves per SIMD
+// and the head-dim split are fixed per instance.
+#define INVATTN_PREFILL_TABLE(X)                                                          \
+  X(64, 1, 64, 2, 1) X(64, 2, 64, 2, 1) X(64, 4, 64, 2, 1) X(64, 8, 64, 2, 1)             \
+  X(256, 1, 32, 2, 1) X(256, 2, 32, 2, 1) X(256, 4, 32, 2, 1) X(256, 8, 32, 2, 1)         \
+  X(512, 1, 32, 2, 2) X(512, 2, 32, 2, 2) X(512, 4, 32, 2, 2) X(512, 8, 32, 2, 2)
 
 bool prefill_schedule(int d, int group, PrefillSchedule* s) {
-#define X(D, G, BN, OCC)                                    \
-  if (d == D && group == G) {                               \
-    *s = PrefillSchedule{128, 128 / G, BN, 256};            \
-    return true;                                            \
+#define X(D, G, BN, OCC, DSPLIT)                                        \
+  if (d == D && group == G) {                                           \
+    using C = PrefillCfg<D, G, BN, OCC, DSPLIT>;                        \
+    *s = PrefillSchedule{C::kRows, C::kPositions, BN, C::kThreads};     \
+    return true;                                                        \
   }
   INVATTN_PREFILL_TABLE(X)
 #undef X
@@ -384,8 +417,8 @@ bool prefill_schedule(int d, int group, PrefillSchedule* s) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
-#define X(D, G, BN, OCC) \
-  if (a.d == D && group == G) return launch_one<D, G, BN, OCC>(a, stream);
+#define X(D, G, BN, OCC, DSPLIT) \
+  if (a.d == D && group == G) return launch_one<D, G, BN, OCC, DSPLIT>(a, stream);
   INVATTN_PREFILL_TABLE(X)
 #undef X
   return hipErrorInvalidValue;
