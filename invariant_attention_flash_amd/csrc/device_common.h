@@ -96,6 +96,26 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float a) {
   }
 }
 
+// Wait until at most `n` vector-memory loads of this wave are outstanding
+// (the newest ones); N is the pipeline depth minus two (0 = wait for all).
+template <int N>
+__device__ __forceinline__ void wait_vmem_keep(int n) {
+  if constexpr (N == 0) {
+    wait_vmem();
+  } else {
+    // vmcnt(n) with n = loads issued per tile times the tiles allowed in
+    // flight; the encodings are immediates, so pick from a small table.
+    switch (n * N) {
+      case 2: __asm__ volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+      case 4: __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      case 8: __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 16: __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+      case 32: __asm__ volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+      default: wait_vmem(); break;
+    }
+  }
+}
+
 // Declared cast: fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 
