@@ -12,13 +12,16 @@
 // the bytes of its output -- do not depend on the batch it is decoded in.
 //
 // Chunk kernel: one workgroup per (chunk, KV head, sequence).  It walks the
-// chunk in 32-key sub-tiles, ascending.  K and V of a sub-tile go to LDS
-// (keys outside [kv_lo, L) are zero and their block-table entries are never
-// read).  Every wave computes the same S^T = K Q^T (v_mfma_f32_16x16x32_bf16,
-// the G query heads of the group padded to 16 columns) and so the same
-// online-softmax state; each wave owns a quarter of the head dim for
-// O^T += V^T P^T.  The record (acc[D], m, l) of the chunk goes to the
-// workspace.
+// chunk one 16-token cache block at a time, ascending.  The K and V rows of
+// a block stream HBM -> LDS with direct loads (16 B per lane) into a ring of
+// kStages buffers, so several blocks are in flight while one is computed;
+// only blocks that hold attended keys are read, and slots past the sequence
+// end read its last key (then masked, p = 0).  Every wave computes the same
+// S^T = K Q^T (v_mfma_f32_16x16x32_bf16; the G query heads of the group are
+// the 16 MFMA columns, padded with zero queries) and so the same online
+// softmax state; each wave owns a quarter of the head dim for
+// O^T += V^T P^T (v_mfma_f32_16x16x16_bf16, V^T by the LDS transpose read).
+// The record (acc[D], m, l) of the chunk goes to the workspace.
 //
 // Merge kernel: one workgroup per (query head, sequence) folds the chunk
 // records in ascending chunk order (m' = max(m, m_c); acc = acc*2^(m-m') +
@@ -28,35 +31,68 @@
 
 namespace invattn {
 
-template <int D_, int G_>
+// Reference-max hysteresis inside a chunk (log2 units), as in prefill.
+constexpr float kDecodeRescale = 8.0f;
+
+template <int D_, int G_, int NST_>
 struct DecodeCfg {
   static constexpr int D = D_, G = G_;
-  static constexpr int kThreads = 256;
-  static constexpr int kSub = kDecodeSub;
-  static constexpr int kStrideK = D + 8;
-  static constexpr int kStrideV = D + 8;
-  static constexpr int kLdsElems = kSub * (kStrideK + kStrideV);
-  static constexpr int kSteps = D / 32;        // 16x16x32 k-steps over d
-  static constexpr int kDPerWave = D / 4;
-  static constexpr int kDBlk = kDPerWave / 16;  // 16-wide output blocks per wave
-  static constexpr int kChunkPerRow = D / 8;
-  static constexpr int kChunksPerThread = kSub * D / 8 / kThreads;
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kStages = NST_;
+  static constexpr int kKeys = 16;                  // keys per stage = one cache block
+  static constexpr int kTile = kKeys * D;           // elements per K (or V) stage
+  static constexpr int kChunks = D / 8;             // 16-byte chunks per row
+  static constexpr int kLoadsTotal = kKeys * kChunks / 64;  // direct loads per tensor per stage
+  static constexpr int kLoadWaves = kLoadsTotal < kWaves ? kLoadsTotal : kWaves;
+  static constexpr int kLoads = kLoadsTotal / kLoadWaves;   // per loading wave
+  static constexpr int kSteps = D / 32;             // 16x16x32 k-steps over d
+  static constexpr int kDPerWave = D / kWaves;
+  static constexpr int kDBlk = kDPerWave / 16;      // 16-wide output blocks per wave
   static constexpr int kRec = decode_record_floats(D);
+  static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
+  static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
   static_assert(G <= 16, "group fits one MFMA column block");
-  static_assert(kSub * D / 8 % kThreads == 0, "sub-tile load split");
+  static_assert(kLoadsTotal * 64 == kKeys * kChunks, "stage load split");
+  static_assert(kStages >= 2 && kStages <= 4, "ring depth");
+  static_assert(kDPerWave % 16 == 0, "head-dim quarter");
 };
 
+// Direct loads of cache block `blk` (keys k0 .. k0+15) into stage buffer kv
+// (K rows then V rows).  Slots at or past the sequence end read slot
+// `last_slot` (the last key) instead; they are masked.
 template <class C>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+__device__ __forceinline__ void issue_block(bf16* kv, const bf16* kc, const bf16* vc,
+                                           size_t blk_base, int k0, int L, uint32_t slot_stride,
+                                           uint32_t head_off, int wave, int lane) {
+  if (wave >= C::kLoadWaves) return;
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    const int cbase = (wave * C::kLoads + i) * 64;
+    const int pch = cbase + lane;
+    const int row = pch / C::kChunks;
+    const int pc = pch % C::kChunks;
+    const int slot = (k0 + row < L) ? row : (L - 1 - k0);
+    const uint32_t off = (uint32_t)slot * slot_stride + head_off;
+    __builtin_amdgcn_global_load_lds(kc + blk_base + off + ((pc ^ (row & C::kSwK)) << 3),
+                                     LDS_PTR(void, kv + cbase * 8), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vc + blk_base + off + ((pc ^ ((row << 1) & C::kSwV)) << 3),
+                                     LDS_PTR(void, kv + C::kTile + cbase * 8), 16, 0, 0);
+  }
+}
+
+template <class C>
+__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads)))
 void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                          const bf16* __restrict__ vc, const int32_t* __restrict__ bt,
                          int max_blocks, const int32_t* __restrict__ seq_lens, int max_seq_len,
                          int num_blocks, int hq, int hkv, int window, float c2,
                          float* __restrict__ ws, int n_chunks) {
   constexpr int D = C::D, G = C::G;
-  __shared__ __attribute__((aligned(16))) bf16 smem[C::kLdsElems];
-  bf16* Ks = smem;
-  bf16* Vs = smem + C::kSub * C::kStrideK;
+  __shared__ __attribute__((aligned(1024))) bf16 kv0[2 * C::kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 kv1[2 * C::kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 kv2[C::kStages > 2 ? 2 * C::kTile : 8];
+  __shared__ __attribute__((aligned(1024))) bf16 kv3[C::kStages > 3 ? 2 * C::kTile : 8];
 
   const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
   int L = seq_lens[b];
@@ -67,83 +103,93 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
   const int c1 = min(c0 + kDecodeChunk, L);
   const int a0 = max(c0, kv_lo);
   if (a0 >= c1) return;
+  const int kb0 = a0 / C::kKeys, kb1 = (c1 - 1) / C::kKeys + 1;  // cache blocks [kb0, kb1)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const bool qv = col < G;
   const int head = g * G + (qv ? col : 0);
 
-  // Q^T operand: column col = query head g*G+col, k = d = 32*s + 8*grp + e.
+  const int32_t* table = bt + (size_t)b * max_blocks;
+  const uint32_t slot_stride = (uint32_t)hkv * D;
+  const uint32_t head_off = (uint32_t)g * D;
+  const size_t block_elems = (size_t)C::kKeys * hkv * D;
+  auto block_base = [&](int kb) {
+    int id = table[kb];
+    id = min(max(id, 0), num_blocks - 1);  // a bad id reads some block, never out of bounds
+    return (size_t)id * block_elems;
+  };
+  issue_block<C>(kv0, kc, vc, block_base(kb0), kb0 * C::kKeys, L, slot_stride, head_off, wave,
+                 lane);
+  if (C::kStages > 2 && kb0 + 1 < kb1)
+    issue_block<C>(kv1, kc, vc, block_base(kb0 + 1), (kb0 + 1) * C::kKeys, L, slot_stride,
+                   head_off, wave, lane);
+  if (C::kStages > 3 && kb0 + 2 < kb1)
+    issue_block<C>(kv2, kc, vc, block_base(kb0 + 2), (kb0 + 2) * C::kKeys, L, slot_stride,
+                   head_off, wave, lane);
+
+  // Q^T operand: column col = query head g*G+col, k = d = 32*t + 8*grp + e.
   bf16x8 qr[C::kSteps];
   {
     const bf16* qrow = q + ((size_t)b * hq + head) * D + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) {
-      bf16x8 x = ld_global_x8(qrow + 32 * s);
-      qr[s] = qv ? x : bf16x8{};
+    for (int t = 0; t < C::kSteps; ++t) {
+      bf16x8 x = ld_global_x8(qrow + 32 * t);
+      qr[t] = qv ? x : bf16x8{};
     }
   }
-
   f32x4 oacc[C::kDBlk];
 #pragma unroll
   for (int db = 0; db < C::kDBlk; ++db) oacc[db] = f32x4{};
   float m = kNegInf, l = 0.f;
 
-  const int32_t* table = bt + (size_t)b * max_blocks;
-  const size_t slot_stride = (size_t)hkv * D;
-  const int st0 = a0 / C::kSub, st1 = (c1 + C::kSub - 1) / C::kSub;
-  for (int st = st0; st < st1; ++st) {
-    const int k0 = st * C::kSub;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < C::kChunksPerThread; ++i) {
-      const int cc = tid + i * C::kThreads;
-      const int row = cc / C::kChunkPerRow;
-      const int cx = (cc % C::kChunkPerRow) * 8;
-      const int key = k0 + row;
-      u32x4 kx = u32x4{}, vx = u32x4{};
-      if (key >= kv_lo && key < L) {
-        const int blk = table[key >> 4];
-        if (blk >= 0 && blk < num_blocks) {
-          const size_t off = ((size_t)blk * 16 + (key & 15)) * slot_stride + (size_t)g * D + cx;
-          kx = *reinterpret_cast<const u32x4*>(kc + off);
-          vx = *reinterpret_cast<const u32x4*>(vc + off);
-        }
-      }
-      *reinterpret_cast<u32x4*>(Ks + row * C::kStrideK + cx) = kx;
-      *reinterpret_cast<u32x4*>(Vs + row * C::kStrideV + cx) = vx;
-    }
-    __syncthreads();
+  // Per-lane LDS offsets.  K: row col, logical chunk 4*t + grp.  V (transpose
+  // read): row 4*grp + lg/4, logical chunk 2*db + (lg&3)/2 of this wave's
+  // quarter, in-chunk offset 4*(lg&1).
+  const int lg = lane & 15;
+  const int vrow = 4 * grp + (lg >> 2);
+  const int vc1 = wave * C::kDPerWave / 8 + ((lg & 3) >> 1);
+  const int vsw = (vrow << 1) & C::kSwV;
 
-    // S^T for keys k0 + [0,16) (s0) and k0 + [16,32) (s1).
-    f32x4 s0 = f32x4{}, s1 = f32x4{};
-    const bf16* krow = Ks + col * C::kStrideK + 8 * grp;
+  auto step = [&] __device__(const bf16* cur, bf16* pre, int kb) {
+    if (kb + C::kStages - 2 < kb1) wait_vmem_keep<C::kStages - 2>(2 * C::kLoads);
+    else wait_vmem();
+    __syncthreads();
+    const int nb = kb + C::kStages - 1;
+    if (nb < kb1)
+      issue_block<C>(pre, kc, vc, block_base(nb), nb * C::kKeys, L, slot_stride, head_off, wave,
+                     lane);
+    const bf16* ks = cur;
+    const bf16* vs = cur + C::kTile;
+    const int k0 = kb * C::kKeys;
+    // S^T for keys k0 + [0, 16): lane holds head col, keys 4*grp + i.
+    f32x4 sacc = f32x4{};
+    const bf16* krow = ks + col * D;
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) {
-      s0 = mfma16(ld_lds_x8(krow + 32 * s), qr[s], s0);
-      s1 = mfma16(ld_lds_x8(krow + 16 * C::kStrideK + 32 * s), qr[s], s1);
-    }
-    float x[8];
+    for (int t = 0; t < C::kSteps; ++t)
+      sacc = mfma16(ld_lds_x8(krow + (((4 * t + grp) ^ (col & C::kSwK)) << 3)), qr[t], sacc);
+    float x[4];
     float tmax = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = k0 + (i < 4 ? 0 : 16) + 4 * grp + (i & 3);
-      const float sv = (i < 4 ? s0[i] : s1[i - 4]) * c2;
-      const bool ok = qv && j >= kv_lo && j < L;
-      x[i] = ok ? sv : kNegInf;
+    for (int i = 0; i < 4; ++i) {
+      const int j = k0 + 4 * grp + i;
+      x[i] = (qv && j >= kv_lo && j < L) ? sacc[i] : kNegInf;
       tmax = fmaxf(tmax, x[i]);
     }
     // Reduce over the four lane groups holding the same query (xor 16, 32).
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m - m_new);
+    tmax *= c2;
+    const bool move = tmax > m + kDecodeRescale || (m == kNegInf && tmax != kNegInf);
+    const float m_new = move ? tmax : m;
+    const float alpha = move ? fast_exp2(m - m_new) : 1.f;
     const float msub = (m_new == kNegInf) ? 0.f : m_new;
     float psum = 0.f;
-    bf16x8 pb;
+    bf16x4 pb;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = fast_exp2(x[i] - msub);
+    for (int i = 0; i < 4; ++i) {
+      const float p = fast_exp2(__builtin_fmaf(x[i], c2, -msub));
       psum += p;
       pb[i] = to_bf16(p);
     }
@@ -155,15 +201,32 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
 #pragma unroll
       for (int db = 0; db < C::kDBlk; ++db) oacc[db] *= alpha;
     }
-    // O^T += V^T P^T for this wave's quarter of the head dim.  Operand slot
-    // e covers key (e < 4 ? 0 : 16) + 4*grp + e%4 on both sides.
-    const bf16* vrow = Vs + (4 * grp + (col >> 2)) * C::kStrideV + wave * C::kDPerWave +
-                       4 * (col & 3);
+    // O^T += V^T P^T for this wave's quarter of the head dim; operand slot
+    // s covers key 4*grp + s on both sides.
+    const bf16* vr = vs + vrow * D + 4 * (lg & 1);
 #pragma unroll
-    for (int db = 0; db < C::kDBlk; ++db) {
-      const bf16x4 lo4 = ld_lds_tr(vrow + 16 * db);
-      const bf16x4 hi4 = ld_lds_tr(vrow + 16 * C::kStrideV + 16 * db);
-      oacc[db] = mfma16(cat8(lo4, hi4), pb, oacc[db]);
+    for (int db = 0; db < C::kDBlk; ++db)
+      oacc[db] = mfma16k16(ld_lds_tr(vr + (((vc1 + 2 * db) ^ vsw) << 3)), pb, oacc[db]);
+  };
+  for (int kb = kb0; kb < kb1;) {
+    if constexpr (C::kStages == 2) {
+      step(kv0, kv1, kb++);
+      if (kb >= kb1) break;
+      step(kv1, kv0, kb++);
+    } else if constexpr (C::kStages == 3) {
+      step(kv0, kv2, kb++);
+      if (kb >= kb1) break;
+      step(kv1, kv0, kb++);
+      if (kb >= kb1) break;
+      step(kv2, kv1, kb++);
+    } else {
+      step(kv0, kv3, kb++);
+      if (kb >= kb1) break;
+      step(kv1, kv0, kb++);
+      if (kb >= kb1) break;
+      step(kv2, kv1, kb++);
+      if (kb >= kb1) break;
+      step(kv3, kv2, kb++);
     }
   }
 
@@ -216,9 +279,8 @@ void decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict
   for (int e = 0; e < kPer; ++e) orow[e] = to_bf16(acc[e] / l);
 }
 
-template <int D, int G>
+template <class C>
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-  using C = DecodeCfg<D, G>;
   dim3 grid(a.n_chunks, a.hkv, a.batch);
   hipLaunchKernelGGL(decode_chunk_kernel<C>, grid, dim3(C::kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
@@ -226,12 +288,15 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
                      a.hkv, a.window, a.c2, a.workspace, a.n_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.hq, a.batch), dim3(64), 0, stream,
+  hipLaunchKernelGGL(decode_merge_kernel<C::D>, dim3(a.hq, a.batch), dim3(64), 0, stream,
                      (const float*)a.workspace, a.seq_lens, a.max_seq_len, a.max_blocks, a.hq,
                      a.window, a.n_chunks, (bf16*)a.o);
   return hipGetLastError();
 }
 
+#ifndef DC_NST
+#define DC_NST 4
+#endif
 #define INVATTN_DECODE_TABLE(X) \
   X(64, 1) X(64, 2) X(64, 4) X(64, 8)     \
   X(256, 1) X(256, 2) X(256, 4) X(256, 8) \
@@ -240,7 +305,7 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
 #define X(D, G) \
-  if (a.d == D && group == G) return launch_one<D, G>(a, stream);
+  if (a.d == D && group == G) return launch_one<DecodeCfg<D, G, DC_NST>>(a, stream);
   INVATTN_DECODE_TABLE(X)
 #undef X
   return hipErrorInvalidValue;

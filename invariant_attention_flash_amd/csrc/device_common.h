@@ -35,6 +35,16 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+// D(16x16, fp32) += A(16x16, bf16) * B(16x16, bf16).
+// Operand layout (lane l): A row l%16, k 4*(l/16)+s; B column l%16, same k.
+// Result: lane l holds column l%16, rows 4*(l/16) + i, i = 0..3.
+__device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                  __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
 // 16-byte load from global memory as 8 bf16.
 __device__ __forceinline__ bf16x8 ld_global_x8(const bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
