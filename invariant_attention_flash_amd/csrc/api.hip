@@ -234,8 +234,8 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   if (batch > 65535) return fail(ATTN_E_UNSUPPORTED, "batch=%d exceeds 65535", batch);
   const int group = num_q_heads / num_kv_heads;
   char sid[128];
-  snprintf(sid, sizeof sid, "decode_d%d_g%d_chunk%d_sub%d_t256+merge_t64", head_dim, group,
-           kDecodeChunk, kDecodeSub);
+  snprintf(sid, sizeof sid, "decode_d%d_g%d_chunk%d_stage%d_t256+merge_t64", head_dim, group,
+           kDecodeChunk, kDecodeStage);
   char split[128];
   snprintf(split, sizeof split, "fixed chunks of %d keys from position 0; ascending merge",
            kDecodeChunk);

@@ -34,10 +34,10 @@ namespace invattn {
 // Reference-max hysteresis inside a chunk (log2 units), as in prefill.
 constexpr float kDecodeRescale = 8.0f;
 
-template <int D_, int G_, int NST_>
+template <int D_, int G_, int NST_, int WAVES_>
 struct DecodeCfg {
   static constexpr int D = D_, G = G_;
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = WAVES_;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kStages = NST_;
   static constexpr int kKeys = 16;                  // keys per stage = one cache block
@@ -55,7 +55,7 @@ struct DecodeCfg {
   static_assert(G <= 16, "group fits one MFMA column block");
   static_assert(kLoadsTotal * 64 == kKeys * kChunks, "stage load split");
   static_assert(kStages >= 2 && kStages <= 4, "ring depth");
-  static_assert(kDPerWave % 16 == 0, "head-dim quarter");
+  static_assert(kDPerWave % 16 == 0, "head-dim slice per wave");
 };
 
 // Direct loads of cache block `blk` (keys k0 .. k0+15) into stage buffer kv
@@ -94,7 +94,10 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
   __shared__ __attribute__((aligned(1024))) bf16 kv2[C::kStages > 2 ? 2 * C::kTile : 8];
   __shared__ __attribute__((aligned(1024))) bf16 kv3[C::kStages > 3 ? 2 * C::kTile : 8];
 
-  const int b = blockIdx.z, g = blockIdx.y, c = blockIdx.x;
+  // Grid (KV head, chunk, sequence): the KV heads of one chunk are
+  // neighbours in dispatch order, so the rows they read from each cache block
+  // (interleaved by head) are fetched together.
+  const int b = blockIdx.z, g = blockIdx.x, c = blockIdx.y;
   int L = seq_lens[b];
   L = min(L, min(max_seq_len, max_blocks * 16));
   if (L <= 0) return;
@@ -281,7 +284,7 @@ void decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict
 
 template <class C>
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_chunks, a.hkv, a.batch);
+  dim3 grid(a.hkv, a.n_chunks, a.batch);
   hipLaunchKernelGGL(decode_chunk_kernel<C>, grid, dim3(C::kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
                      a.block_table, a.max_blocks, a.seq_lens, a.max_seq_len, a.num_blocks, a.hq,
@@ -294,8 +297,12 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Ring depth and waves per workgroup: fixed constants.
 #ifndef DC_NST
-#define DC_NST 4
+#define DC_NST 3
+#endif
+#ifndef DC_WAVES
+#define DC_WAVES 4
 #endif
 #define INVATTN_DECODE_TABLE(X) \
   X(64, 1) X(64, 2) X(64, 4) X(64, 8)     \
@@ -305,7 +312,7 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
 #define X(D, G) \
-  if (a.d == D && group == G) return launch_one<DecodeCfg<D, G, DC_NST>>(a, stream);
+  if (a.d == D && group == G) return launch_one<DecodeCfg<D, G, DC_NST, (DC_WAVES < D / 16 ? DC_WAVES : D / 16)>>(a, stream);
   INVATTN_DECODE_TABLE(X)
 #undef X
   return hipErrorInvalidValue;

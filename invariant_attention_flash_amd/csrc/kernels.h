@@ -58,8 +58,8 @@ struct PrefillSchedule {
 bool prefill_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-constexpr int kDecodeChunk = 512;  // keys per split chunk (fixed)
-constexpr int kDecodeSub = 32;     // keys per sub-tile inside a chunk
+constexpr int kDecodeChunk = 512;  // keys per split chunk (fixed; ATTN_DECODE_CHUNK)
+constexpr int kDecodeStage = 16;   // keys per pipeline stage inside a chunk (one cache block)
 constexpr int decode_record_floats(int d) { return d + 4; }  // acc[d], m, l, pad
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
