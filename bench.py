@@ -90,6 +90,53 @@ def load_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
+CALIBRATION_BYTES = 1 << 30   # plain streaming kernel used to scale the HBM byte counters
+
+
+def write_traffic(fetch_dir, write_dir):
+    """Turn two rocprofv3 counter runs of `bench.py --calibrate` (FETCH_SIZE,
+    then WRITE_SIZE, KiB per dispatch) into profiles/traffic.json: per-launch
+    HBM bytes of the prefill and decode kernels, each counter scaled so the
+    calibration copy of CALIBRATION_BYTES reads (writes) exactly that much."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"]), int(r["Grid_Size"])))
+        return rows
+
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = load(d, counter)
+        # the calibration pass: an elementwise negation reading and writing 1 GiB
+        calib = [v for k, v, g in rows if "neg_kernel" in k]
+        if not calib:
+            raise SystemExit(f"no calibration kernel found in {d}")
+        scale = CALIBRATION_BYTES / (1024.0 * float(np.median(calib)))
+        for key, match, first in (("prefill_kernel<256,2>", "prefill_kernel<invattn::PrefillCfg<256, 2",
+                                   "prefill_kernel"),
+                                  ("decode_chunk_kernel+decode_merge_kernel<512,8>", "decode_",
+                                   "decode_chunk_kernel")):
+            vals = [v for k, v, g in rows if match in k]
+            launches = sum(1 for k, v, g in rows if match in k and first in k)
+            if not vals or not launches:
+                continue
+            per_launch = 1024.0 * scale * sum(vals) / launches
+            rec = out.setdefault(key, {"sources_hash": kernel_sources_hash()})
+            rec[counter.lower() + "_bytes"] = per_launch
+            rec[counter.lower() + "_scale"] = scale
+    for rec in out.values():
+        rec["bytes_per_launch"] = rec.get("fetch_size_bytes", 0.0) + rec.get("write_size_bytes", 0.0)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,7 +145,14 @@ def main():
     ap.add_argument("--decode-batch", type=int, default=64)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 1 GiB copy (scale for the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: build profiles/traffic.json from two counter runs")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1])
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -142,6 +196,15 @@ def main():
     def decode():
         ia.attn_decode_paged(dc["q"], dc["k_cache"], dc["v_cache"], d_bt, d_sl, d_max,
                              softmax_scale=dc["scale"], workspace=ws, out=d_out)
+
+    if args.calibrate:
+        # plain streaming kernel of known traffic: reads and writes 1 GiB
+        src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         prefill()
