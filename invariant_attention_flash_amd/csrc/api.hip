@@ -176,6 +176,10 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, fl
   if (spans_opt && !aligned4(spans_opt)) return fail(ATTN_E_ALIGN, "spans_opt is not 4-byte aligned");
   const long long tiles = ((long long)max_seqlen + sched.positions - 1) / sched.positions;
   if (tiles > 0x7fffffffLL) return fail(ATTN_E_UNSUPPORTED, "max_seqlen=%d too large", max_seqlen);
+  // One sequence's rows of one KV head are addressed with 32-bit byte offsets.
+  if ((long long)max_seqlen * num_kv_heads * head_dim * 2 > 0x7fffffffLL)
+    return fail(ATTN_E_UNSUPPORTED, "max_seqlen=%d x num_kv_heads=%d x head_dim=%d spans 2 GiB or more",
+                max_seqlen, num_kv_heads, head_dim);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   long long tokens = -1;

@@ -21,6 +21,10 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 constexpr float kNegInf = -__builtin_inff();
 
+// Word 3 of a raw buffer resource (gfx9 family): 32-bit data format, no
+// swizzle, no index stride.  Loads past num_records return zeros.
+constexpr int kBufferFlags = 0x00020000;
+
 // D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
 // Operand layout (lane l): A row l%32, k 8*(l/32)+s; B column l%32, same k.
 // Result: lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15.
@@ -77,6 +81,67 @@ __device__ __forceinline__ HalfPair half_pair(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return HalfPair{__builtin_bit_cast(float, (uint32_t)r[0]),
                   __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+
+// Values of lanes l and l^16 as (even 16-lane row's value, odd row's value),
+// identical in both lanes.
+__device__ __forceinline__ HalfPair row_pair(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return HalfPair{__builtin_bit_cast(float, (uint32_t)r[0]),
+                  __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// acc *= a for a 16x16 accumulator held in AGPRs (one wave per SIMD): each
+// element moves to a VGPR, is multiplied, and moves back.
+__device__ __forceinline__ void scale_acc4(f32x4& acc, float a) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float t;
+    __asm__ volatile(
+        "v_accvgpr_read_b32 %1, %0\n\t"
+        "v_mul_f32 %1, %1, %2\n\t"
+        "v_accvgpr_write_b32 %0, %1"
+        : "+a"(acc[i]), "=&v"(t)
+        : "v"(a));
+  }
+}
+
+// acc (=|+=) A * B on v_mfma_f32_16x16x32_bf16 with the accumulator pinned
+// to AGPRs (one wave per SIMD keeps large accumulators there).  Written as
+// volatile inline asm so the register allocator never moves accumulators
+// through VGPRs and LDS reads keep their source order around the MFMAs (the
+// caller places operand reads ahead by hand).  Hazard distances are the
+// caller's: no VALU write of a or b in the two cycles before, no VALU read
+// of acc within 18 cycles after.
+__device__ __forceinline__ void mfma16_agpr_first(f32x4& acc, bf16x8 a, bf16x8 b) {
+  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_agpr(f32x4& acc, bf16x8 a, bf16x8 b) {
+  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between the last accumulator MFMA and VALU reads of it.
+__device__ __forceinline__ void mfma_drain() {
+  __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
+}
+
+// A zero accumulator created in AGPRs (a 16x16x32 MFMA of zero operands with
+// an inline-constant zero addend), so a loop-carried accumulator is AGPR from
+// its first definition on.
+__device__ __forceinline__ f32x4 agpr_zero4() {
+  f32x4 r;
+  const bf16x8 z = {};
+  // The nop keeps the zero operand's VALU writes three wait states away.
+  __asm__("s_nop 2\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(r) : "v"(z));
+  return r;
 }
 
 // Wait until every vector-memory load of this wave (including direct

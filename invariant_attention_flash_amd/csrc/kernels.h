@@ -55,8 +55,34 @@ struct PrefillSchedule {
   int threads;
 };
 
+// Prefill block order.  The hardware hands consecutive workgroups to the 8
+// XCDs in turn (each XCD has its own L2); workgroups that read the same K/V
+// rows (consecutive position tiles of one sequence and KV head) should share
+// an L2.  Block i therefore takes logical work item
+//   chunk (i/8)/kXcdChunk * 8 + i%8, item (i/8) % kXcdChunk of that chunk,
+// so each XCD walks runs of kXcdChunk consecutive tiles.  The grid is padded
+// to a multiple of 8*kXcdChunk; items past the end exit at once.  Only the
+// placement changes: a row's arithmetic never depends on its block.
+constexpr int kXcds = 8;
+constexpr int kXcdChunk = 32;
+
+__host__ __device__ inline long long xcd_padded_blocks(long long n) {
+  const long long q = (long long)kXcds * kXcdChunk;
+  return (n + q - 1) / q * q;
+}
+
+__device__ inline long long xcd_logical_block(long long i) {
+  const long long x = i % kXcds, j = i / kXcds;
+  return ((j / kXcdChunk) * kXcds + x) * kXcdChunk + j % kXcdChunk;
+}
+
 bool prefill_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Head dim 512 (prefill_wide.hip); prefill_schedule / launch_prefill
+// dispatch to these.
+bool prefill_wide_schedule(int d, int group, PrefillSchedule* s);
+hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t stream);
 
 constexpr int kDecodeChunk = 512;  // keys per split chunk (fixed; ATTN_DECODE_CHUNK)
 constexpr int kDecodeStage = 16;   // keys per pipeline stage inside a chunk (one cache block)

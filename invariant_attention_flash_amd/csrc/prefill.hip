@@ -1,6 +1,7 @@
 // prefill.hip -- batch-invariant attention forward over packed
 // variable-length sequences (sliding-window and global layers, GQA,
-// bidirectional spans), bf16 MFMA on gfx950.
+// bidirectional spans), bf16 MFMA on gfx950.  Head dims 64 and 256 run the
+// kernel below; head dim 512 runs prefill_wide.hip.
 //
 // Sources: sliding and global attention cores are separate layer types with
 // their own head geometry and masks ("RFC: Gemma-4-31B-it train/rollout
@@ -11,41 +12,45 @@
 // bidirectional soft-token spans (section 1, Phase B; contiguous soft-token
 // runs in "Gemma-4-E4B-it multimodal baseline").
 //
-// Work map.  A workgroup owns `positions` consecutive positions of ONE
-// sequence (aligned to the sequence start, never to the packed buffer) for
-// the G query heads of one KV head.  Its query rows are ordered
-// position-major (row r = position*G + head) and cut into 32-row blocks; a
-// wave owns RBW row blocks (and, when DSPLIT = 2, one half of the head dim,
-// its partner wave the other half).  A row therefore always lands in the same
-// wave, lane and MFMA slot, and visits the same KV tiles in the same ascending
-// order, whatever else is in the batch.
+// Work map.  A workgroup (4 waves, one per SIMD) owns `positions`
+// consecutive positions of ONE sequence, aligned to the sequence start, for
+// the G query heads of one KV head.  Its rows are ordered position-major
+// (row = position*G + head); wave w owns rows [16*RB*w, 16*RB*(w+1)) as RB
+// blocks of 16.  A row therefore always lands in the same wave, lane and
+// MFMA slot and visits the same KV tiles in the same ascending order,
+// whatever else is in the batch.
 //
-// Per KV tile (BN keys, ascending):
-//   K and V tiles stream HBM -> LDS with direct loads (global_load_lds,
-//   16 B per lane) into a ring of NST stage buffers, so later tiles land
-//   while this one is computed; rows are stored unpadded with an XOR swizzle
-//   of their 16-byte chunks (conflict-free MFMA operand reads).  Keys past
-//   the sequence end read the sequence's last row and are masked (p = 0).
-//   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, read once
-//                and used by every row block of the wave; B = Q in
-//                registers), so each lane holds one query's scores; with
-//                DSPLIT = 2 each wave of a pair forms the partial sum over its
-//                half of the head dim and the pair adds them through LDS in a
-//                fixed order (half 0 + half 1);
-//   mask by select (-inf) on boundary tiles;
-//   online softmax in fp32 with a per-row reference max m (scaled units):
-//                m moves (and the running sum and accumulator are rescaled by
-//                2^(m_old-m_new)) only when the tile max exceeds m by more than
-//                kRescale, so p = 2^(fma(s, c, -m)) <= 2^kRescale, with
-//                c = fl32(scale*log2 e); the tile max and the row sum reduce
-//                inside the lane in register order, then across the lane pair
-//                (l, l^32);
-//   P -> bf16 (RNE), O^T += V^T P^T on the same MFMA, with V^T read from the
-//                row-major LDS tile by the LDS transpose read (once, used by
-//                every row block of the wave).
+// Operand reuse.  Every K and V operand read from LDS feeds RB MFMAs (one
+// per row block), so LDS traffic per MFMA falls as RB grows; RB is bounded by
+// the accumulators: O (D/16 blocks of 4 fp32 per row block) and two tiles of
+// scores stay in the 256 accumulation registers of the wave.
+//
+// Per KV tile of 32 keys (ascending), software-pipelined by one tile:
+//   K and V tiles stream HBM -> LDS with direct loads (16 B per lane) into a
+//   ring of NST stage buffers (distinct LDS objects), issued NST-1 tiles
+//   ahead; rows are stored unpadded with an XOR swizzle of their 16-byte
+//   chunks.  Keys past the sequence end load as zeros and are masked.
+//   S^T(t+1) = K Q^T on v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 head-dim
+//               elements from LDS, B = Q^T in registers): lane l holds keys
+//               4*(l/16) + i of query row l%16, for 16-key halves kb = 0, 1;
+//   meanwhile the softmax of tile t (fp32, raw scores masked by select on
+//               boundary tiles):
+//               reference max m (scaled units) moves only when the tile max
+//               exceeds it by more than kRescale; then the running sum and
+//               the accumulator are scaled by 2^(m_old - m_new);
+//               p = 2^(fma(s, c, -m)), c = fl32(scale * log2 e);
+//               tile max and row sum reduce in-lane in slot order (kb, i),
+//               then across lanes l^32 and l^16, each step adding (lower
+//               lane's value) + (upper lane's value);
+//   O^T += V^T P^T on the same MFMA: P^T (bf16, round to nearest even) is
+//               the lane's own 8 probabilities, k-slot 8*(l/16) + s meaning
+//               key 16*(s/4) + 4*(l/16) + s%4; V^T comes from the row-major
+//               LDS tile through the transpose read.
 // Fully masked tiles are exact no-ops for a row (p = 0, alpha = 1), and every
-// decision (mask, move m, rescale) is a function of the row's own sequence,
-// so the bytes of a row never depend on the rest of the batch.
+// decision (mask, moving m, rescaling) is a function of the row's own
+// sequence, so the bytes of a row never depend on the rest of the batch.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -55,224 +60,287 @@ namespace invattn {
 // exceeds it by more than this.  A fixed constant of the arithmetic.
 constexpr float kRescale = 8.0f;
 
-template <int D_, int G_, int BN_, int DSPLIT_, int RBW_, int WAVES_, int NST_, int OCC_>
-struct PrefillCfg {
-  static constexpr int D = D_, G = G_, BN = BN_, DSPLIT = DSPLIT_, RBW = RBW_, OCC = OCC_;
-  static constexpr int kWaves = WAVES_;
-  static constexpr int kStages = NST_;                 // K/V tile buffers in flight
+template <int D_, int G_, int RB_, int NST_>
+struct Pf16Cfg {
+  static constexpr int D = D_, G = G_, RB = RB_, NST = NST_;
+  static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kWaveGroups = kWaves / DSPLIT;  // waves sharing row blocks
-  static constexpr int kRowBlocks = kWaveGroups * RBW; // 32-row blocks per workgroup
-  static constexpr int kRows = 32 * kRowBlocks;
+  static constexpr int BN = 32;                       // keys per KV tile
+  static constexpr int kRowsPerWave = 16 * RB;
+  static constexpr int kRows = kWaves * kRowsPerWave;
   static constexpr int kPositions = kRows / G;
-  static constexpr int kPosPerWave = 32 * RBW / G;
-  static constexpr int DW = D / DSPLIT;   // head-dim slice of one wave
-  static constexpr int kChunks = D / 8;   // 16-byte chunks per row
-  static constexpr int kTile = BN * D;    // elements per K (or V) tile
-  static constexpr int kSteps = DW / 16;  // MFMA k-steps over this wave's head-dim slice
-  static constexpr int kSBlk = BN / 32;   // 32-key score blocks per tile
-  static constexpr int kDBlk = DW / 32;   // 32-wide output blocks of this wave
-  static constexpr int kKK = BN / 16;     // 16-key PV k-steps per tile
-  // Partial-score exchange of a wave pair: fp32, 16 floats per lane per
-  // score block per row block.
-  static constexpr int kXchgFloats = DSPLIT > 1 ? kWaves * RBW * kSBlk * 16 * 64 : 0;
-  static constexpr int kLoads = BN * kChunks / 64 / kWaves;  // direct loads per wave per tensor
+  static constexpr int kPosPerWave = kRowsPerWave / G;
+  static constexpr int kSt = D / 32;       // QK k-steps (32 head-dim elements)
+  static constexpr int kDb = D / 16;       // PV output blocks (16 head-dim elements)
+  static constexpr int kChunks = D / 8;    // 16-byte chunks per row
+  static constexpr int kTile = BN * D;     // elements of one K (or V) tile
+  static constexpr int kLoads = BN * kChunks / (64 * kWaves);  // per lane per tensor
   static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
   static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
-  static_assert(BN % 32 == 0 && DW % 32 == 0, "tile shape");
-  static_assert(kWaves % DSPLIT == 0 && 32 % G == 0, "wave map");
-  static_assert(BN * kChunks % (64 * kWaves) == 0, "tile load split");
-  static_assert(DSPLIT == 1 || DW / 8 >= 32, "head-dim slices start on a swizzle boundary");
-  static_assert(kStages == 2 || kStages == 3, "double or triple buffering");
-  static_assert(kStages * 2 * kTile * 2 + kXchgFloats * 4 <= 163840, "LDS budget");
+  static_assert(D % 32 == 0 && kRowsPerWave % G == 0, "row map");
+  static_assert(kLoads >= 1 && BN * kChunks % (64 * kWaves) == 0, "tile load split");
+  static_assert(NST == 5, "stage ring: tiles t-1 .. t+3");
+  static_assert(NST * 2 * kTile * 2 <= 163840, "LDS budget");
+  static_assert(RB * kDb * 4 + 2 * RB * 8 <= 256, "accumulators fit the AGPR file");
 };
 
-// Direct HBM -> LDS loads of one K and one V tile (keys k0 .. k0+BN-1) into
-// the stage buffer `kv` (K tile, then V tile).  Lane offsets (elements,
-// 32-bit; one sequence's K or V stays below 4 GiB) are row*stride + swizzled
-// chunk; keys past the sequence end clamp to its last row (offset last_row).
+// Per-lane constants.  LDS operand addresses are byte offsets: a lane base
+// plus (lane xor ^ step constant); the xors are laundered once per tile step
+// (opaque) so the compiler forms each address next to its read instead of
+// keeping one register per (buffer, step) alive across the loop.
+struct Lane16 {
+  int x, gq;           // lane = 16*gq + x
+  uint32_t krow;       // K operand: byte offset of key row x
+  uint32_t kq16;       // K operand: (logical chunk ^ physical chunk) of k-step 0, in bytes
+  uint32_t vrow;       // V transpose read: byte offset of row 4*gq + x/4, element 4*(x%2)
+  uint32_t vc16;       // V transpose read: physical chunk of block 0, in bytes
+  int wlim;            // window (or a huge value for global layers)
+  float c2;            // fl32(scale * log2 e)
+};
+
+template <class T>
+__device__ __forceinline__ T opaque(T x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
+// Direct HBM -> LDS loads (raw buffer loads with the LDS bit, 16 B per lane)
+// of the K and V tiles of keys k0 .. k0+31 into the stage buffer kv (K tile,
+// then V tile).  The buffer resources span exactly the sequence's rows of
+// this KV head, so keys past the sequence end are out of range and land as
+// zeros (masked later).  Buffer rather than global loads: the compiler then
+// tracks them on the vector-memory counter alone, and LDS reads that follow
+// keep their partial waits.
 template <class C>
-__device__ __forceinline__ void issue_tile(bf16* kv, int k0, uint32_t rs, uint32_t last_row,
-                                           const uint32_t* ld_row, const uint32_t* ld_ck,
-                                           const uint32_t* ld_cv, const bf16* kbase,
-                                           const bf16* vbase, int wave) {
-  const uint32_t base = (uint32_t)k0 * rs;
+__device__ __forceinline__ void issue16(bf16* kv, int k0, uint32_t rs_bytes,
+                                        __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                        int wave, int lane) {
+  // Per-lane offsets are recomputed each tile (a few VALU) rather than held
+  // in registers across the loop.
+  const int lane_o = opaque(lane);
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
-    const int cbase = (wave * C::kLoads + i) * 64;
-    const uint32_t off = min(base + ld_row[i], last_row);
-    __builtin_amdgcn_global_load_lds(kbase + (off + ld_ck[i]), LDS_PTR(void, kv + cbase * 8), 16,
-                                     0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + (off + ld_cv[i]),
-                                     LDS_PTR(void, kv + C::kTile + cbase * 8), 16, 0, 0);
+    const int slot = (wave * C::kLoads + i) * 64;  // first 16-byte slot of this load
+    const int pch = slot + lane_o;
+    const int row = pch / C::kChunks;
+    const int pc = pch % C::kChunks;
+    const uint32_t roff = (uint32_t)(k0 + row) * rs_bytes;
+    const uint32_t ck = (uint32_t)((pc ^ (row & C::kSwK)) << 4);
+    const uint32_t cv = (uint32_t)((pc ^ ((row << 1) & C::kSwV)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kv + slot * 8), 16, roff + ck, 0,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, kv + C::kTile + slot * 8), 16,
+                                             roff + cv, 0, 0, 0);
   }
 }
 
-// Per-lane constants of the tile computation.
-template <class C>
-struct Lane {
-  int lane, wave, n, hh, dh;
-  int kx;                 // K operand: physical chunk of k-step s is 2*s ^ kx
-  int vrow0, vx, vsub;    // V transpose read: row, chunk xor, in-chunk offset
-  int wlim;               // window (or a huge value for global layers)
-  float c2;               // fl32(scale * log2 e)
-  int qpos_m[C::RBW];     // row position (-1 for rows past the sequence end)
-  int my_ss[C::RBW], my_se[C::RBW];  // the row's own span (empty when none)
-};
-
-// One KV tile (keys k0 .. k0+BN-1) for the rows of this wave: scores,
-// online softmax, P.V.  ks/vs: the stage buffer holding the tile.
-template <class C>
-__device__ __forceinline__ void compute_tile(const bf16* __restrict__ ks,
-                                             const bf16* __restrict__ vs, float* xchg, int k0,
-                                             bool need_mask, const Lane<C>& ln,
-                                             const bf16x8 (*qr)[C::kSteps],
-                                             f32x16 (*oacc)[C::kDBlk], float* m, float* l) {
-  constexpr int D = C::D, DW = C::DW, RBW = C::RBW;
-  const int lane = ln.lane, wave = ln.wave, hh = ln.hh, dh = ln.dh;
-  // S^T = K Q^T over this wave's head-dim slice: score block `blk` holds keys
-  // k0 + 32*blk + [0, 32); each K operand read serves every row block.
-  f32x16 sacc[RBW][C::kSBlk];
+// Row statistics of one tile, fast path: probabilities against the current
+// reference max (no dependency on this tile's max), their sum, and the
+// scaled tile max that decides whether the reference max must move.
+// Mask of key j for a row at position qp: allowed when 0 <= qp - j < wlim
+// (causal, window) or j lies in the row's span [ss, se); both tests are one
+// unsigned compare each: wbase = qp - k0 - 4*gq, sbase = k0 + 4*gq - ss.
+template <class C, bool MASK>
+__device__ __forceinline__ void tile_values(const f32x4 (*s)[2], int rb, int k0, const Lane16& ln,
+                                            const int* qpos, const int* ss, const int* se,
+                                            float* v) {
 #pragma unroll
-  for (int blk = 0; blk < C::kSBlk; ++blk) {
+  for (int e = 0; e < 8; ++e) v[e] = s[rb][e >> 2][e & 3];
+  if constexpr (MASK) {
+    const int wbase = qpos[rb] - k0 - 4 * ln.gq;
+    const int sbase = k0 + 4 * ln.gq - ss[rb];
+    const uint32_t slen = (uint32_t)(se[rb] - ss[rb]);
 #pragma unroll
-    for (int r = 0; r < RBW; ++r) sacc[r][blk] = f32x16{};
-    const bf16* krow = ks + (32 * blk + ln.n) * D + dh * DW;
-#pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) {
-      const bf16x8 kop = ld_lds_x8(krow + (((2 * s) ^ ln.kx) << 3));
-#pragma unroll
-      for (int r = 0; r < RBW; ++r) sacc[r][blk] = mfma32(kop, qr[r][s], sacc[r][blk]);
+    for (int e = 0; e < 8; ++e) {
+      const int c = 16 * (e >> 2) + (e & 3);  // key j = k0 + 4*gq + c
+      const bool ok = ((uint32_t)(wbase - c) < (uint32_t)ln.wlim) | ((uint32_t)(sbase + c) < slen);
+      v[e] = ok ? v[e] : kNegInf;
     }
   }
-  {
-    constexpr int kN = C::kSBlk * C::kSteps, kAhead = 3;
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+}
+
+// p = exp2(fma(s, c, -msub)) for the 8 slots of a row block, their sum in
+// the fixed pairwise order ((p0+p1)+(p2+p3)) + ((p4+p5)+(p6+p7)), then across
+// lanes l^32 and l^16 (each step: lower lane's value + upper lane's value),
+// and the bf16 operand.
+__device__ __forceinline__ float probs(const float* v, float c2, float msub, bf16x8& pb) {
+  float p[8];
 #pragma unroll
-    for (int i = 0; i < kN - kAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, RBW, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(v[e], c2, -msub));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pb[e] = to_bf16(p[e]);
+  float sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  HalfPair hp = half_pair(sum);
+  sum = hp.lo + hp.hi;
+  hp = row_pair(sum);
+  return hp.lo + hp.hi;
+}
+
+// Scaled tile max of a row (max over the 8 slots, then lanes l^32, l^16).
+__device__ __forceinline__ float row_max_scaled(const float* v, float c2) {
+  float t = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                  fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+  HalfPair hp = half_pair(t);
+  t = fmaxf(hp.lo, hp.hi);
+  hp = row_pair(t);
+  return fmaxf(hp.lo, hp.hi) * c2;
+}
+
+// Softmax of tile t for every row block, fast path.  Returns true when some
+// row's reference max must move (tile max > m + kRescale, or the first
+// allowed keys); then softmax_move() redoes the tile.  Otherwise p used m,
+// alpha = 1 and l += sum -- bitwise what the moving rule gives.
+template <class C, bool MASK>
+__device__ __forceinline__ bool softmax_fast(const f32x4 (*s)[2], int k0, const Lane16& ln,
+                                             const int* qpos, const int* ss, const int* se,
+                                             const float* m, float* l, bf16x8* pb) {
+  bool any = false;
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    float v[8];
+    tile_values<C, MASK>(s, rb, k0, ln, qpos, ss, se, v);
+    const float m_old = m[rb];
+    const float sum = probs(v, ln.c2, m_old == kNegInf ? 0.f : m_old, pb[rb]);
+    const float tmax = row_max_scaled(v, ln.c2);
+    const bool move = (tmax > m_old + kRescale) | ((m_old == kNegInf) & (tmax != kNegInf));
+    any |= move;
+    l[rb] = move ? l[rb] : l[rb] + sum;
+  }
+  return __builtin_amdgcn_ballot_w64(any) != 0;
+}
+
+// The rare path: rows whose tile max exceeds m + kRescale (or whose first
+// allowed keys are in this tile) move m to the tile max, scale l and the
+// accumulator by alpha = 2^(m_old - m_new) (1 when m_old = -inf: the
+// accumulator and sum are still exact zeros) and recompute p with the new m.
+template <class C, bool MASK, bool SCALE>
+__device__ __forceinline__ void softmax_move(const f32x4 (*s)[2], int k0, const Lane16& ln,
+                                             const int* qpos, const int* ss, const int* se,
+                                             float* m, float* l, bf16x8* pb,
+                                             f32x4 (*o)[C::kDb]) {
+#pragma unroll
+  for (int rb = 0; rb < C::RB; ++rb) {
+    float v[8];
+    tile_values<C, MASK>(s, rb, k0, ln, qpos, ss, se, v);
+    const float m_old = m[rb];
+    const float tmax = row_max_scaled(v, ln.c2);
+    const bool move = (tmax > m_old + kRescale) | ((m_old == kNegInf) & (tmax != kNegInf));
+    if (__builtin_amdgcn_ballot_w64(move) == 0) continue;
+    const float m_new = move ? tmax : m_old;
+    const float alpha = (move & (m_old != kNegInf)) ? fast_exp2(m_old - m_new) : 1.f;
+    bf16x8 pnew;
+    const float sum = probs(v, ln.c2, m_new == kNegInf ? 0.f : m_new, pnew);
+    if (move) {
+      pb[rb] = pnew;
+      l[rb] = l[rb] * alpha + sum;
+      m[rb] = m_new;
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, RBW * kAhead, 0);
-  }
-  if constexpr (C::DSPLIT > 1) {
-    // Full scores = slice 0 + slice 1, added in that order by both waves.
-    constexpr int kRec = RBW * C::kSBlk * 16;
+    if constexpr (SCALE) {
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int r = 0; r < RBW; ++r)
-#pragma unroll
-      for (int blk = 0; blk < C::kSBlk; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          xchg[(wave * kRec + (r * C::kSBlk + blk) * 16 + i) * 64 + lane] = sacc[r][blk][i];
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < RBW; ++r)
-#pragma unroll
-      for (int blk = 0; blk < C::kSBlk; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float other = xchg[((wave ^ 1) * kRec + (r * C::kSBlk + blk) * 16 + i) * 64 + lane];
-          sacc[r][blk][i] = dh == 0 ? sacc[r][blk][i] + other : other + sacc[r][blk][i];
-        }
-  }
-
-  // Mask by select (raw scores) on boundary tiles.
-  if (need_mask) {
-#pragma unroll
-    for (int r = 0; r < RBW; ++r)
-#pragma unroll
-      for (int blk = 0; blk < C::kSBlk; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = k0 + 32 * blk + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const int qp = ln.qpos_m[r];
-          const bool ok = ((j <= qp) & (qp - j < ln.wlim)) | ((j >= ln.my_ss[r]) & (j < ln.my_se[r]));
-          sacc[r][blk][i] = ok ? sacc[r][blk][i] : kNegInf;
-        }
-  }
-
-  bf16x8 pb[RBW][C::kKK];
-#pragma unroll
-  for (int r = 0; r < RBW; ++r) {
-    // Tile max of the raw scores; the scaled max is fl(max * c) (rounding is
-    // monotone, so it equals the max of the scaled scores).
-    float tmax = kNegInf;
-#pragma unroll
-    for (int blk = 0; blk < C::kSBlk; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[r][blk][i]);
-    HalfPair hp = half_pair(tmax);
-    tmax = fmaxf(hp.lo, hp.hi) * ln.c2;
-    // Move the reference max only on a jump of more than kRescale.
-    const bool move = tmax > m[r] + kRescale || (m[r] == kNegInf && tmax != kNegInf);
-    const float m_new = move ? tmax : m[r];
-    const float alpha = move ? fast_exp2(m[r] - m_new) : 1.f;
-    const float msub = (m_new == kNegInf) ? 0.f : m_new;
-    // p = exp2(fma(s, c, -m)), row sum in register order, P -> bf16 operands.
-    float psum = 0.f;
-#pragma unroll
-    for (int blk = 0; blk < C::kSBlk; ++blk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[r][blk][i], ln.c2, -msub));
-        psum += p;
-        pb[r][2 * blk + (i >> 3)][i & 7] = to_bf16(p);
+        for (int db = 0; db < C::kDb; ++db) o[rb][db] *= alpha;
       }
     }
-    hp = half_pair(psum);
-    psum = hp.lo + hp.hi;
-    l[r] = l[r] * alpha + psum;
-    m[r] = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < C::kDBlk; ++db) scale_acc<C::OCC>(oacc[r][db], alpha);
-    }
   }
+}
 
-  // O^T += V^T P^T.  PV k-step kk covers keys 16*kk + 8*(e/4) + 4*hh + e%4 in
-  // operand slot e; the transpose read gathers exactly those rows.
+// One pipelined tile step: S^T(t+1) = K Q^T on the K tile `ks` and
+// (PV) O^T += V^T P^T(t-1) on the V tile `vs`, on 16x16x32 MFMAs; the
+// softmax VALU of tile t (formed by the caller in the same block) fills the
+// MFMA shadow.  FIRST: the step forming the first PV product, which starts
+// the accumulator (zero addend) instead of adding to it.
+//   K operand (k-step st, half kb): key row 16*kb + x, logical chunk
+//     4*st + gq, physical chunk (4*st + gq) ^ (x & kSwK);
+//   V operand (output block db): rows 4*gq + x/4 and +16, logical chunk
+//     2*db + (x%4)/2, physical chunk ^ ((2*row) & kSwV), element 4*(x%2).
+template <class C, bool PV, bool FIRST>
+__device__ __forceinline__ void mfma_phase(const bf16* __restrict__ ks,
+                                           const bf16* __restrict__ vs, uint32_t krow,
+                                           uint32_t kq16, uint32_t vrow, uint32_t vc16,
+                                           const bf16x8 (*q)[C::kSt], f32x4 (*s)[2],
+                                           const bf16x8* pprev, f32x4 (*o)[C::kDb]) {
+  constexpr int kN = 2 * C::kSt;  // K operand groups = V operand groups (= D/16)
+  static_assert(kN == C::kDb, "one K group per V group");
+  const char* kb0 = reinterpret_cast<const char*>(ks) + krow;
+  const char* vb0 = reinterpret_cast<const char*>(vs) + vrow;
+  auto kread = [&](int i) {
+    return ld_lds_x8(reinterpret_cast<const bf16*>(
+        kb0 + (kq16 ^ (uint32_t)((i >> 1) << 6)) + (i & 1) * 32 * C::D));
+  };
+  auto vread = [&](int i) {
+    const bf16* p = reinterpret_cast<const bf16*>(vb0 + (vc16 ^ (uint32_t)(i << 5)));
+    return cat8(ld_lds_tr(p), ld_lds_tr(p + 16 * C::D));
+  };
+  // LDS reads run kAhead groups ahead of their MFMAs.  The order of reads
+  // and MFMAs is pinned by scheduling fences that only VALU and SALU
+  // instructions may cross, so the softmax VALU fills the gaps while the
+  // reads stay early.
+  constexpr int kAhead = 3;
+  bf16x8 kop[kAhead], vop[kAhead];
 #pragma unroll
-  for (int kk = 0; kk < C::kKK; ++kk) {
-    const bf16* vrow = vs + (16 * kk + ln.vrow0) * D + dh * DW + ln.vsub;
-#pragma unroll
-    for (int db = 0; db < C::kDBlk; ++db) {
-      const int col = ((4 * db) ^ ln.vx) << 3;
-      const bf16x8 vop = cat8(ld_lds_tr(vrow + col), ld_lds_tr(vrow + 8 * D + col));
-#pragma unroll
-      for (int r = 0; r < RBW; ++r) oacc[r][db] = mfma32(vop, pb[r][kk], oacc[r][db]);
-    }
+  for (int i = 0; i < kAhead; ++i) {
+    kop[i] = kread(i);
+    if constexpr (PV) vop[i] = vread(i);
   }
-  {
-    constexpr int kN = C::kKK * C::kDBlk, kAhead = 3;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
 #pragma unroll
-    for (int i = 0; i < kN - kAhead; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, RBW, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  for (int rb = 0; rb < C::RB; ++rb) s[rb][0] = s[rb][1] = f32x4{};
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const int st = i >> 1, kb = i & 1;
+    const bf16x8 a = kop[i % kAhead];
+    bf16x8 b;
+    if constexpr (PV) b = vop[i % kAhead];
+    if (i + kAhead < kN) {
+      kop[i % kAhead] = kread(i + kAhead);
+      if constexpr (PV) vop[i % kAhead] = vread(i + kAhead);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, RBW * kAhead, 1);
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) s[rb][kb] = mfma16(a, q[rb][st], s[rb][kb]);
+    if constexpr (PV) {
+#pragma unroll
+      for (int rb = 0; rb < C::RB; ++rb)
+        o[rb][i] = mfma16(b, pprev[rb], FIRST ? f32x4{} : o[rb][i]);
+    }
+    __builtin_amdgcn_sched_barrier(0x0006);
+  }
+}
+
+// O^T += V^T P^T for the last tile (no scores left to form).
+template <class C, bool FIRST>
+__device__ __forceinline__ void pv_last(const bf16* __restrict__ vs, uint32_t vrow, uint32_t vc16,
+                                        const bf16x8* pprev, f32x4 (*o)[C::kDb]) {
+  const char* vb0 = reinterpret_cast<const char*>(vs) + vrow;
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db) {
+    const bf16* p = reinterpret_cast<const bf16*>(vb0 + (vc16 ^ (uint32_t)(db << 5)));
+    const bf16x8 b = cat8(ld_lds_tr(p), ld_lds_tr(p + 16 * C::D));
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb)
+      o[rb][db] = mfma16(b, pprev[rb], FIRST ? f32x4{} : o[rb][db]);
   }
 }
 
 template <class C>
 __global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads),
-                          amdgpu_waves_per_eu(C::OCC, C::OCC)))
+                          amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ v, bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                     const int32_t* __restrict__ spans, int num_spans, int hq, int hkv,
-                    int window, float c2) {
-  constexpr int D = C::D, G = C::G, BN = C::BN, DW = C::DW, RBW = C::RBW;
-  // One LDS object per pipeline stage (K tile then V tile), so the compiler
-  // can tell that direct loads into one stage never alias reads of another.
-  __shared__ __attribute__((aligned(1024))) bf16 kv0[2 * C::kTile];
-  __shared__ __attribute__((aligned(1024))) bf16 kv1[2 * C::kTile];
-  __shared__ __attribute__((aligned(1024))) bf16 kv2[C::kStages > 2 ? 2 * C::kTile : 8];
-  __shared__ __attribute__((aligned(16))) float xchg[C::kXchgFloats > 0 ? C::kXchgFloats : 4];
+                    int window, float c2, int tiles, int nseq) {
+  constexpr int D = C::D, G = C::G, RB = C::RB, BN = C::BN, NST = C::NST;
+  // Stage ring: NST buffers of (K tile, V tile); tile kt lives in buffer
+  // (kt - kt0) % NST.  While step kt runs, tiles kt-1 (V read), kt, kt+1 (K
+  // read), kt+2 (landing) and kt+3 (issued) occupy the five buffers.
+  __shared__ __attribute__((aligned(1024))) bf16 kvs[NST][2 * C::kTile];
 
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int t = gridDim.x - 1 - blockIdx.x;  // longest causal tiles first
+  // Logical item = (tile, KV head, sequence), tile fastest; tiles run from
+  // the end of the sequence (longest causal rows first).
+  const long long item = xcd_logical_block(blockIdx.x);
+  if (item >= (long long)tiles * hkv * nseq) return;
+  const int t = tiles - 1 - (int)(item % tiles);
+  const int g = (int)((item / tiles) % hkv);
+  const int b = (int)(item / ((long long)tiles * hkv));
   const int seq0 = cu_seqlens[b];
   const int L = cu_seqlens[b + 1] - seq0;
   const int p0 = t * C::kPositions;
@@ -281,9 +349,6 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wg = wave / C::DSPLIT;  // wave group (shares row blocks)
-  const int dh = wave % C::DSPLIT;  // head-dim slice of this wave
-  const int n = lane & 31, hh = lane >> 5;
   const bool windowed = window > 0;
 
   int ss, se;
@@ -295,185 +360,209 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (find_span(spans, num_spans, seq0 + p0, ss, se)) lo = min(lo, max(ss - seq0, 0));
     if (find_span(spans, num_spans, seq0 + p1 - 1, ss, se)) hi = max(hi, min(se - seq0, L));
   }
-  // Positions of this wave's rows (masks are needed on tiles that are not
-  // fully allowed for every one of them).
-  const int pw0 = p0 + wg * C::kPosPerWave;
+  // Positions of this wave's rows (a tile needs masks unless it is fully
+  // allowed for every one of them).
+  const int pw0 = p0 + wave * C::kPosPerWave;
   const int pw1 = min(pw0 + C::kPosPerWave, L);
   const bool wave_full = pw0 + C::kPosPerWave <= L;
 
-  Lane<C> ln;
-  ln.lane = lane;
-  ln.wave = wave;
-  ln.n = n;
-  ln.hh = hh;
-  ln.dh = dh;
-  ln.kx = hh ^ (n & C::kSwK);
+  Lane16 ln;
+  ln.x = lane & 15;
+  ln.gq = lane >> 4;
+  ln.krow = (uint32_t)(ln.x * D * 2);
+  ln.kq16 = (uint32_t)((ln.gq ^ (ln.x & C::kSwK)) << 4);
   {
-    // V transpose read of this lane: row vrow0 (+16*kk, +8), logical chunk
-    // 4*db + c1, physical chunk (4*db + c1) ^ (2*vrow0 & kSwV) = 4*db ^ vx.
-    const int qg = lane >> 4, lg = lane & 15;
-    ln.vrow0 = 4 * (qg >> 1) + (lg >> 2);
-    ln.vx = (2 * (qg & 1) + ((lg & 3) >> 1)) ^ ((ln.vrow0 << 1) & C::kSwV);
-    ln.vsub = (lg & 1) * 4;
+    const int y = ln.x, vr = 4 * ln.gq + (y >> 2);
+    ln.vrow = (uint32_t)(vr * D * 2 + 8 * (y & 1));
+    ln.vc16 = (uint32_t)((((y & 3) >> 1) ^ ((2 * vr) & C::kSwV)) << 4);
   }
   ln.wlim = windowed ? window : 0x7fffffff;
   ln.c2 = c2;
-  int qpos[RBW], qhead[RBW];
+
+  int qpos[RB], qhead[RB], my_ss[RB], my_se[RB];
 #pragma unroll
-  for (int r = 0; r < RBW; ++r) {
-    const int row = 32 * (wg * RBW + r) + n;
-    qpos[r] = p0 + row / G;
-    qhead[r] = g * G + row % G;
-    const bool valid = qpos[r] < L;
-    ln.qpos_m[r] = valid ? qpos[r] : -1;  // an invalid row admits no key
-    ln.my_ss[r] = 0;
-    ln.my_se[r] = 0;
-    if (num_spans > 0 && valid && find_span(spans, num_spans, seq0 + qpos[r], ss, se)) {
-      ln.my_ss[r] = ss - seq0;
-      ln.my_se[r] = min(se - seq0, L);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = C::kRowsPerWave * wave + 16 * rb + ln.x;
+    const int pos = p0 + row / G;
+    qhead[rb] = g * G + row % G;
+    const bool valid = pos < L;
+    qpos[rb] = valid ? pos : -1;  // an invalid row admits no key
+    my_ss[rb] = 0;
+    my_se[rb] = 0;
+    if (num_spans > 0 && valid && find_span(spans, num_spans, seq0 + pos, ss, se)) {
+      my_ss[rb] = ss - seq0;
+      my_se[rb] = min(se - seq0, L);
     }
   }
 
-  const uint32_t rs = (uint32_t)hkv * D;
-  const bf16* kbase = k + ((size_t)seq0 * hkv + g) * D;
-  const bf16* vbase = v + ((size_t)seq0 * hkv + g) * D;
-  const uint32_t last_row = (uint32_t)(L - 1) * rs;
-  uint32_t ld_row[C::kLoads], ld_ck[C::kLoads], ld_cv[C::kLoads];
+  // Q^T operands: lane holds q[row][32*st + 8*gq .. +7] for every st.  Rows
+  // past the sequence end load its first row instead; every key is masked
+  // for them (qpos = -1) and they are never stored.
+  bf16x8 qr[RB][C::kSt];
 #pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    const int pch = (wave * C::kLoads + i) * 64 + lane;
-    const int row = pch / C::kChunks;
-    const int pc = pch % C::kChunks;
-    ld_row[i] = (uint32_t)row * rs;
-    ld_ck[i] = (uint32_t)((pc ^ (row & C::kSwK)) << 3);
-    ld_cv[i] = (uint32_t)((pc ^ ((row << 1) & C::kSwV)) << 3);
-  }
-  const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
-  issue_tile<C>(kv0, kt0 * BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase, vbase, wave);
-  if (C::kStages > 2 && kt0 + 1 < kt1)
-    issue_tile<C>(kv1, (kt0 + 1) * BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase, vbase, wave);
-
-  // Q^T operands: lane holds q[row][dh*DW + 16*s + 8*hh .. +7] for every s.
-  bf16x8 qr[RBW][C::kSteps];
-#pragma unroll
-  for (int r = 0; r < RBW; ++r) {
-    const bool valid = ln.qpos_m[r] >= 0;
+  for (int rb = 0; rb < RB; ++rb) {
     const bf16* qrow =
-        q + ((size_t)(seq0 + (valid ? qpos[r] : 0)) * hq + qhead[r]) * D + dh * DW + 8 * hh;
+        q + ((size_t)(seq0 + max(qpos[rb], 0)) * hq + qhead[rb]) * D + 8 * ln.gq;
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) {
-      bf16x8 x = ld_global_x8(qrow + 16 * s);
-      qr[r][s] = valid ? x : bf16x8{};
-    }
+    for (int st = 0; st < C::kSt; ++st) qr[rb][st] = ld_global_x8(qrow + 32 * st);
   }
 
-  f32x16 oacc[RBW][C::kDBlk];
-  float m[RBW], l[RBW];
+  const uint32_t rs_bytes = (uint32_t)hkv * D * 2;
+  // Buffer resources over this KV head's rows of the sequence (the host
+  // rejects inputs whose rows span 2 GiB or more).
+  const int nbytes = (int)((uint32_t)L * rs_bytes);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(k + ((size_t)seq0 * hkv + g) * D), (short)0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(v + ((size_t)seq0 * hkv + g) * D), (short)0, nbytes, kBufferFlags);
+  const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
+  constexpr int kPerTile = 2 * C::kLoads;  // direct loads per lane per tile
+
+  // Accumulators: O starts at the first PV product (zero addend).
+  f32x4 oacc[RB][C::kDb];
+  float m[RB], l[RB];
 #pragma unroll
-  for (int r = 0; r < RBW; ++r) {
-    m[r] = kNegInf;
-    l[r] = 0.f;
-#pragma unroll
-    for (int db = 0; db < C::kDBlk; ++db) oacc[r][db] = f32x16{};
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = kNegInf;
+    l[rb] = 0.f;
   }
 
-  // One step: wait for tile kt (later tiles may stay in flight), barrier
-  // (after it nobody reads the buffer of tile kt-1), prefetch tile
-  // kt + kStages - 1 into `pre` (the buffer of tile kt-1), compute tile kt
-  // from `cur`.  The loop is unrolled by the stage count so every buffer is a
-  // distinct LDS object at every step.
-  auto step = [&] __device__(const bf16* cur, bf16* pre, int kt) {
-    const int k0 = kt * BN;
-    if (kt + C::kStages - 2 < kt1) wait_vmem_keep<C::kStages - 2>(2 * C::kLoads);
+  // Prologue: tiles kt0 .. kt0+2 in flight; wait for Q and tile kt0.
+  issue16<C>(kvs[0], kt0 * BN, rs_bytes, krs, vrs, wave, lane);
+  if (kt0 + 1 < kt1) issue16<C>(kvs[1], (kt0 + 1) * BN, rs_bytes, krs, vrs, wave, lane);
+  if (kt0 + 2 < kt1) issue16<C>(kvs[2], (kt0 + 2) * BN, rs_bytes, krs, vrs, wave, lane);
+  {
+    const int newer = min(2, kt1 - 1 - kt0);  // tiles issued after kt0
+    if (newer >= 2) wait_vmcnt<2 * kPerTile>();
+    else if (newer == 1) wait_vmcnt<kPerTile>();
     else wait_vmem();
-    __syncthreads();
-    if (kt + C::kStages - 1 < kt1)
-      issue_tile<C>(pre, (kt + C::kStages - 1) * BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase,
-                    vbase, wave);
+  }
+  __syncthreads();
+
+  // Scores and probabilities of consecutive tiles alternate between two
+  // arrays each (steps are unrolled by two), so nothing is copied.
+  f32x4 sa[RB][2], sb[RB][2];
+  bf16x8 pa[RB], pbb[RB];
+  mfma_phase<C, false, false>(kvs[0], kvs[0], ln.krow, ln.kq16, ln.vrow, ln.vc16, qr, sa, pa,
+                              oacc);
+
+  // Step kt: wait for tile kt+1 and issue tile kt+3 (into the buffer of tile
+  // kt-2, free once every wave is past the barrier), then S(kt+1) and
+  // PV(kt-1) on the MFMAs while the VALU takes the softmax of tile kt; the
+  // rare reference-max moves are handled after the MFMAs are issued.  After
+  // the last tile the scores formed are never used (the K buffer holds an
+  // older tile); forming them keeps the step branch-free.  MODE 0: first
+  // tile (no PV yet); 1: first PV (starts O); 2: steady state.
+  auto step = [&] __device__(int kt, f32x4(&sc)[RB][2], f32x4(&sn)[RB][2], bf16x8(&pc)[RB],
+                             const bf16x8(&pp)[RB], auto mode) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr bool PV = MODE > 0, FIRST = MODE == 1;
+    const int r = (kt - kt0) % NST;
+    const bf16* __restrict__ kbuf = kvs[(r + 1) % NST];
+    const bf16* __restrict__ vbuf = kvs[(r + NST - 1) % NST] + C::kTile;  // V tile of kt-1
+    bf16* __restrict__ pre = kvs[(r + 3) % NST];
+    const int k0 = kt * BN;
+    if (kt + 1 < kt1) {
+      // Tile kt+1 must have landed; tile kt+2 may still be in flight.
+      if (kt + 2 < kt1) wait_vmcnt<kPerTile>();
+      else wait_vmem();
+      __syncthreads();
+      if (kt + 3 < kt1) issue16<C>(pre, (kt + 3) * BN, rs_bytes, krs, vrs, wave, lane);
+    }
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
-    compute_tile<C>(cur, cur + C::kTile, xchg, k0, need_mask, ln, qr, oacc, m, l);
-  };
-  for (int kt = kt0; kt < kt1;) {
-    step(kv0, C::kStages == 2 ? kv1 : kv2, kt++);
-    if (kt >= kt1) break;
-    step(kv1, kv0, kt++);
-    if (kt >= kt1) break;
-    if constexpr (C::kStages == 3) {
-      step(kv2, kv1, kt++);
-      if (kt >= kt1) break;
+    const uint32_t kq16 = opaque(ln.kq16), vc16 = opaque(ln.vc16);
+    if (need_mask) {
+      const bool moved = softmax_fast<C, true>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
+      mfma_phase<C, PV, FIRST>(kbuf, vbuf, ln.krow, kq16, ln.vrow, vc16, qr, sn, pp, oacc);
+      if (moved) softmax_move<C, true, PV>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, oacc);
+    } else {
+      const bool moved = softmax_fast<C, false>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
+      mfma_phase<C, PV, FIRST>(kbuf, vbuf, ln.krow, kq16, ln.vrow, vc16, qr, sn, pp, oacc);
+      if (moved) softmax_move<C, false, PV>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, oacc);
     }
+  };
+  using Mode0 = std::integral_constant<int, 0>;
+  using Mode1 = std::integral_constant<int, 1>;
+  using Mode2 = std::integral_constant<int, 2>;
+  step(kt0, sa, sb, pa, pbb, Mode0{});
+  if (kt0 + 1 < kt1) step(kt0 + 1, sb, sa, pbb, pa, Mode1{});
+  int kt = kt0 + 2;
+  for (; kt + 1 < kt1; kt += 2) {
+    step(kt, sa, sb, pa, pbb, Mode2{});
+    step(kt + 1, sb, sa, pbb, pa, Mode2{});
+  }
+  if (kt < kt1) {
+    step(kt, sa, sb, pa, pbb, Mode2{});
+    pv_last<C, false>(kvs[(kt - kt0) % NST] + C::kTile, ln.vrow, ln.vc16, pa, oacc);
+  } else if (kt1 - kt0 >= 2) {
+    pv_last<C, false>(kvs[(kt - 1 - kt0) % NST] + C::kTile, ln.vrow, ln.vc16, pbb, oacc);
+  } else {
+    pv_last<C, true>(kvs[0] + C::kTile, ln.vrow, ln.vc16, pa, oacc);
   }
 
   // Epilogue: o = acc / l (IEEE fp32 division), bf16 RNE, store.
 #pragma unroll
-  for (int r = 0; r < RBW; ++r) {
-    if (ln.qpos_m[r] < 0) continue;
-    bf16* orow = o + ((size_t)(seq0 + qpos[r]) * hq + qhead[r]) * D + dh * DW + 4 * hh;
+  for (int rb = 0; rb < RB; ++rb) {
+    if (qpos[rb] < 0) continue;
+    bf16* orow = o + ((size_t)(seq0 + qpos[rb]) * hq + qhead[rb]) * D + 4 * ln.gq;
 #pragma unroll
-    for (int db = 0; db < C::kDBlk; ++db) {
+    for (int db = 0; db < C::kDb; ++db) {
+      bf16x4 w;
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = to_bf16(oacc[r][db][4 * gi + e] / l[r]);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * gi) = w;
-      }
+      for (int i = 0; i < 4; ++i) w[i] = to_bf16(oacc[rb][db][i] / l[rb]);
+      *reinterpret_cast<bf16x4*>(orow + 16 * db) = w;
     }
-    if (lse != nullptr && hh == 0 && dh == 0)
-      lse[(size_t)(seq0 + qpos[r]) * hq + qhead[r]] =
-          (m[r] + fast_log2(l[r])) * 0.693147180559945309f;
+    if (lse != nullptr && ln.gq == 0)
+      lse[(size_t)(seq0 + qpos[rb]) * hq + qhead[rb]] =
+          (m[rb] + fast_log2(l[rb])) * 0.693147180559945309f;
   }
 }
 
 template <class C>
 static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   const int tiles = (a.max_seqlen + C::kPositions - 1) / C::kPositions;
-  dim3 grid(tiles, a.hkv, a.batch);
-  hipLaunchKernelGGL(prefill_kernel<C>, grid, dim3(C::kThreads), 0, stream,
+  const long long blocks = xcd_padded_blocks((long long)tiles * a.hkv * a.batch);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(prefill_kernel<C>, dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
-                     a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2);
+                     a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2, tiles,
+                     a.batch);
   return hipGetLastError();
 }
 
-// One kernel instance per (head_dim, group).  Parameters after (D, G): keys
-// per tile, head-dim split, row blocks per wave, waves, stages, waves per
-// SIMD.  All fixed per instance.
+// One kernel instance per (head_dim, group).  Parameters after (D, G): row
+// blocks of 16 per wave, stage ring depth.  All fixed per instance.
 #ifndef PF_CFG64
-#define PF_CFG64 64, 1, 2, 4, 2, 1
+#define PF_CFG64 4, 5
 #endif
 #ifndef PF_CFG256
-#define PF_CFG256 64, 1, 1, 4, 2, 1
-#endif
-#ifndef PF_CFG512
-#define PF_CFG512 32, 2, 1, 4, 2, 1
+#define PF_CFG256 2, 5
 #endif
 #define INVATTN_PREFILL_TABLE(X)                                              \
   X(64, 1, PF_CFG64) X(64, 2, PF_CFG64) X(64, 4, PF_CFG64) X(64, 8, PF_CFG64) \
   X(256, 1, PF_CFG256) X(256, 2, PF_CFG256) X(256, 4, PF_CFG256)              \
-  X(256, 8, PF_CFG256)                                                        \
-  X(512, 1, PF_CFG512) X(512, 2, PF_CFG512) X(512, 4, PF_CFG512)              \
-  X(512, 8, PF_CFG512)
+  X(256, 8, PF_CFG256)
 
 bool prefill_schedule(int d, int group, PrefillSchedule* s) {
 #define X(D, G, ...)                                                          \
   if (d == D && group == G) {                                                 \
-    using C = PrefillCfg<D, G, __VA_ARGS__>;                                  \
+    using C = Pf16Cfg<D, G, __VA_ARGS__>;                                     \
     *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads};        \
     return true;                                                              \
   }
   INVATTN_PREFILL_TABLE(X)
 #undef X
-  return false;
+  return prefill_wide_schedule(d, group, s);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
 #define X(D, G, ...) \
-  if (a.d == D && group == G) return launch_one<PrefillCfg<D, G, __VA_ARGS__>>(a, stream);
+  if (a.d == D && group == G) return launch_one<Pf16Cfg<D, G, __VA_ARGS__>>(a, stream);
   INVATTN_PREFILL_TABLE(X)
 #undef X
-  return hipErrorInvalidValue;
+  return launch_prefill_wide(a, stream);
 }
 
 }  // namespace invattn

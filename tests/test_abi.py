@@ -80,6 +80,7 @@ PREFILL_ERRORS = [
     (dict(q=(1 << 20) + 8), "ATTN_E_ALIGN", "q is not 16-byte"),
     (dict(o=(1 << 20) + 2), "ATTN_E_ALIGN", "o is not 16-byte"),
     (dict(cu=(1 << 20) + 2), "ATTN_E_ALIGN", "cu_seqlens"),
+    (dict(max_seqlen=1 << 22, hq=32, hkv=16, d=256), "ATTN_E_UNSUPPORTED", "2 GiB"),
 ]
 
 
