@@ -105,33 +105,49 @@ __device__ __forceinline__ T opaque(T x) {
 }
 
 // Direct HBM -> LDS loads (raw buffer loads with the LDS bit, 16 B per lane)
-// of the K and V tiles of keys k0 .. k0+31 into the stage buffer kv (K tile,
-// then V tile).  The buffer resources span exactly the sequence's rows of
-// this KV head, so keys past the sequence end are out of range and land as
-// zeros (masked later).  Buffer rather than global loads: the compiler then
-// tracks them on the vector-memory counter alone, and LDS reads that follow
-// keep their partial waits.
+// of the K and V tiles of keys k0 .. k0+31 into a stage buffer (K tile, then
+// V tile).  The buffer resources span exactly the sequence's rows of this
+// KV head, so keys past the sequence end are out of range and land as zeros
+// (masked later); a zero-length resource loads nothing and writes zeros
+// (used where no tile is left, so the code stays branch-free).  Buffer
+// rather than global loads: the compiler then tracks them on the
+// vector-memory counter alone, and LDS reads that follow keep their partial
+// waits.
+// Load j of this lane's 2*kLoads loads of the tile starting at key k0 (even
+// j: K, odd j: V) from the rows [kb, kb + nbytes) and [vb, vb + nbytes);
+// nbytes = 0 when there is no tile (the loads then write zeros).
 template <class C>
-__device__ __forceinline__ void issue16(bf16* kv, int k0, uint32_t rs_bytes,
-                                        __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
-                                        int wave, int lane) {
-  // Per-lane offsets are recomputed each tile (a few VALU) rather than held
-  // in registers across the loop.
-  const int lane_o = opaque(lane);
-#pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    const int slot = (wave * C::kLoads + i) * 64;  // first 16-byte slot of this load
-    const int pch = slot + lane_o;
-    const int row = pch / C::kChunks;
-    const int pc = pch % C::kChunks;
-    const uint32_t roff = (uint32_t)(k0 + row) * rs_bytes;
-    const uint32_t ck = (uint32_t)((pc ^ (row & C::kSwK)) << 4);
-    const uint32_t cv = (uint32_t)((pc ^ ((row << 1) & C::kSwV)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kv + slot * 8), 16, roff + ck, 0,
-                                             0, 0);
+__device__ __forceinline__ void dma_load(bf16* __restrict__ kv, const bf16* kb, const bf16* vb,
+                                         int nbytes, int k0, int j, uint32_t rs_bytes, int wave,
+                                         int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type the buffer builtins here
+  const int i = j >> 1;
+  const int slot = (wave * C::kLoads + i) * 64;  // first 16-byte slot of this load
+  const int pch = slot + lane;
+  const int row = pch / C::kChunks;
+  const int pc = pch % C::kChunks;
+  const uint32_t roff = (uint32_t)(k0 + row) * rs_bytes;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, nbytes, kBufferFlags);
+  if ((j & 1) == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kv + slot * 8), 16,
+                                             roff + ((pc ^ (row & C::kSwK)) << 4), 0, 0, 0);
+  else
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, kv + C::kTile + slot * 8), 16,
-                                             roff + cv, 0, 0, 0);
-  }
+                                             roff + ((pc ^ ((row << 1) & C::kSwV)) << 4), 0, 0,
+                                             0);
+#endif
+}
+
+template <class C>
+__device__ __forceinline__ void issue16(bf16* __restrict__ kv, const bf16* kb, const bf16* vb,
+                                        int nbytes, int k0, uint32_t rs_bytes, int wave,
+                                        int lane) {
+#pragma unroll
+  for (int j = 0; j < 2 * C::kLoads; ++j)
+    dma_load<C>(kv, kb, vb, nbytes, k0, j, rs_bytes, wave, lane);
 }
 
 // Row statistics of one tile, fast path: probabilities against the current
@@ -253,12 +269,15 @@ __device__ __forceinline__ void softmax_move(const f32x4 (*s)[2], int k0, const 
 //     4*st + gq, physical chunk (4*st + gq) ^ (x & kSwK);
 //   V operand (output block db): rows 4*gq + x/4 and +16, logical chunk
 //     2*db + (x%4)/2, physical chunk ^ ((2*row) & kSwV), element 4*(x%2).
-template <class C, bool PV, bool FIRST>
+template <class C, bool PV, bool FIRST, bool DMA>
 __device__ __forceinline__ void mfma_phase(const bf16* __restrict__ ks,
-                                           const bf16* __restrict__ vs, uint32_t krow,
-                                           uint32_t kq16, uint32_t vrow, uint32_t vc16,
-                                           const bf16x8 (*q)[C::kSt], f32x4 (*s)[2],
-                                           const bf16x8* pprev, f32x4 (*o)[C::kDb]) {
+                                           const bf16* __restrict__ vs, bf16* __restrict__ pre,
+                                           const bf16* kseq, const bf16* vseq, int nbytes, int nk0,
+                                           uint32_t rs_bytes, int wave,
+                                           int lane, uint32_t krow, uint32_t kq16, uint32_t vrow,
+                                           uint32_t vc16, const bf16x8 (*q)[C::kSt],
+                                           f32x4 (*s)[2], const bf16x8* pprev,
+                                           f32x4 (*o)[C::kDb]) {
   constexpr int kN = 2 * C::kSt;  // K operand groups = V operand groups (= D/16)
   static_assert(kN == C::kDb, "one K group per V group");
   const char* kb0 = reinterpret_cast<const char*>(ks) + krow;
@@ -293,6 +312,12 @@ __device__ __forceinline__ void mfma_phase(const bf16* __restrict__ ks,
     if (i + kAhead < kN) {
       kop[i % kAhead] = kread(i + kAhead);
       if constexpr (PV) vop[i % kAhead] = vread(i + kAhead);
+    }
+    // The next tile's loads (into `pre`) are spread over the groups.
+    if constexpr (DMA) {
+      constexpr int kEvery = kN / (2 * C::kLoads);
+      if (i % kEvery == 0)
+        dma_load<C>(pre, kseq, vseq, nbytes, nk0, i / kEvery, rs_bytes, wave, lane);
     }
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) s[rb][kb] = mfma16(a, q[rb][st], s[rb][kb]);
@@ -408,15 +433,16 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 
   const uint32_t rs_bytes = (uint32_t)hkv * D * 2;
-  // Buffer resources over this KV head's rows of the sequence (the host
-  // rejects inputs whose rows span 2 GiB or more).
+  // This KV head's rows of the sequence, loaded through buffer resources of
+  // exactly that extent (the host rejects inputs whose rows span 2 GiB or
+  // more).
+  const bf16* kb = k + ((size_t)seq0 * hkv + g) * D;
+  const bf16* vb = v + ((size_t)seq0 * hkv + g) * D;
   const int nbytes = (int)((uint32_t)L * rs_bytes);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(k + ((size_t)seq0 * hkv + g) * D), (short)0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(v + ((size_t)seq0 * hkv + g) * D), (short)0, nbytes, kBufferFlags);
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
   constexpr int kPerTile = 2 * C::kLoads;  // direct loads per lane per tile
+  // Extent for tile kt (zero past the last tile).
+  auto extent = [&](int kt) { return kt < kt1 ? nbytes : 0; };
 
   // Accumulators: O starts at the first PV product (zero addend).
   f32x4 oacc[RB][C::kDb];
@@ -428,27 +454,23 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 
   // Prologue: tiles kt0 .. kt0+2 in flight; wait for Q and tile kt0.
-  issue16<C>(kvs[0], kt0 * BN, rs_bytes, krs, vrs, wave, lane);
-  if (kt0 + 1 < kt1) issue16<C>(kvs[1], (kt0 + 1) * BN, rs_bytes, krs, vrs, wave, lane);
-  if (kt0 + 2 < kt1) issue16<C>(kvs[2], (kt0 + 2) * BN, rs_bytes, krs, vrs, wave, lane);
-  {
-    const int newer = min(2, kt1 - 1 - kt0);  // tiles issued after kt0
-    if (newer >= 2) wait_vmcnt<2 * kPerTile>();
-    else if (newer == 1) wait_vmcnt<kPerTile>();
-    else wait_vmem();
-  }
+  issue16<C>(kvs[0], kb, vb, extent(kt0), kt0 * BN, rs_bytes, wave, lane);
+  issue16<C>(kvs[1], kb, vb, extent(kt0 + 1), (kt0 + 1) * BN, rs_bytes, wave, lane);
+  issue16<C>(kvs[2], kb, vb, extent(kt0 + 2), (kt0 + 2) * BN, rs_bytes, wave, lane);
+  wait_vmcnt<2 * kPerTile>();
   __syncthreads();
 
   // Scores and probabilities of consecutive tiles alternate between two
   // arrays each (steps are unrolled by two), so nothing is copied.
   f32x4 sa[RB][2], sb[RB][2];
   bf16x8 pa[RB], pbb[RB];
-  mfma_phase<C, false, false>(kvs[0], kvs[0], ln.krow, ln.kq16, ln.vrow, ln.vc16, qr, sa, pa,
-                              oacc);
+  mfma_phase<C, false, false, false>(kvs[0], kvs[0], kvs[1], kb, vb, 0, 0, rs_bytes, wave, lane,
+                                     ln.krow, ln.kq16, ln.vrow, ln.vc16, qr, sa, pa, oacc);
 
-  // Step kt: wait for tile kt+1 and issue tile kt+3 (into the buffer of tile
-  // kt-2, free once every wave is past the barrier), then S(kt+1) and
-  // PV(kt-1) on the MFMAs while the VALU takes the softmax of tile kt; the
+  // Step kt: wait for tile kt+1, then S(kt+1) and PV(kt-1) on the MFMAs,
+  // the loads of tile kt+3 spread among them (into the buffer of tile kt-2,
+  // free once every wave is past the barrier), while the VALU takes the
+  // softmax of tile kt; the
   // rare reference-max moves are handled after the MFMAs are issued.  After
   // the last tile the scores formed are never used (the K buffer holds an
   // older tile); forming them keeps the step branch-free.  MODE 0: first
@@ -462,23 +484,27 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bf16* __restrict__ vbuf = kvs[(r + NST - 1) % NST] + C::kTile;  // V tile of kt-1
     bf16* __restrict__ pre = kvs[(r + 3) % NST];
     const int k0 = kt * BN;
-    if (kt + 1 < kt1) {
-      // Tile kt+1 must have landed; tile kt+2 may still be in flight.
-      if (kt + 2 < kt1) wait_vmcnt<kPerTile>();
-      else wait_vmem();
-      __syncthreads();
-      if (kt + 3 < kt1) issue16<C>(pre, (kt + 3) * BN, rs_bytes, krs, vrs, wave, lane);
-    }
+    // Tile kt+1 must have landed; tile kt+2 may still be in flight (every
+    // step issues one tile's loads, real or zero-length).
+    wait_vmcnt<kPerTile>();
+    __syncthreads();
+    const int next_bytes = extent(kt + 3);
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
     const uint32_t kq16 = opaque(ln.kq16), vc16 = opaque(ln.vc16);
     if (need_mask) {
       const bool moved = softmax_fast<C, true>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
-      mfma_phase<C, PV, FIRST>(kbuf, vbuf, ln.krow, kq16, ln.vrow, vc16, qr, sn, pp, oacc);
+      mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, kb, vb, next_bytes, (kt + 3) * BN, rs_bytes,
+                                     wave,
+                                     lane, ln.krow, kq16,
+                                     ln.vrow, vc16, qr, sn, pp, oacc);
       if (moved) softmax_move<C, true, PV>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, oacc);
     } else {
       const bool moved = softmax_fast<C, false>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
-      mfma_phase<C, PV, FIRST>(kbuf, vbuf, ln.krow, kq16, ln.vrow, vc16, qr, sn, pp, oacc);
+      mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, kb, vb, next_bytes, (kt + 3) * BN, rs_bytes,
+                                     wave,
+                                     lane, ln.krow, kq16,
+                                     ln.vrow, vc16, qr, sn, pp, oacc);
       if (moved) softmax_move<C, false, PV>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, oacc);
     }
   };
