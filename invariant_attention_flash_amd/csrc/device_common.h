@@ -92,6 +92,15 @@ __device__ __forceinline__ HalfPair row_pair(float x) {
                   __builtin_bit_cast(float, (uint32_t)r[1])};
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes
+// complete, then s_barrier.  Unlike __syncthreads() (a release/acquire fence
+// at workgroup scope), it leaves direct HBM -> LDS loads in flight: the
+// caller waits for the ones the next step reads (wait_vmcnt) before it.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -100,8 +109,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // acc *= a for a 16x16 accumulator held in AGPRs (one wave per SIMD): each
-// element moves to a VGPR, is multiplied, and moves back.
+// element moves to a VGPR, is multiplied, and moves back.  The elements are
+// taken apart and put back so the vector itself never needs an address.
 __device__ __forceinline__ void scale_acc4(f32x4& acc, float a) {
+  float e[4] = {acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float t;
@@ -109,9 +120,26 @@ __device__ __forceinline__ void scale_acc4(f32x4& acc, float a) {
         "v_accvgpr_read_b32 %1, %0\n\t"
         "v_mul_f32 %1, %1, %2\n\t"
         "v_accvgpr_write_b32 %0, %1"
-        : "+a"(acc[i]), "=&v"(t)
+        : "+a"(e[i]), "=&v"(t)
         : "v"(a));
   }
+  acc = f32x4{e[0], e[1], e[2], e[3]};
+}
+
+// acc (=|+=) A * B on v_mfma_f32_16x16x32_bf16 with the accumulator in
+// VGPRs.  With one wave per SIMD the compiler puts every builtin MFMA
+// accumulator in AGPRs, and on gfx950 a read of an AGPR (v_accvgpr_read)
+// while MFMAs are in flight stalls for about ten cycles, so accumulators
+// that VALU code reads (attention scores) are formed here instead.  Hazards
+// are the caller's: A and B are not rewritten during the MFMA's first
+// passes (they come from LDS reads waited for before, or stay fixed), acc is
+// only chained through these MFMAs, and the caller waits (mfma_drain) before
+// VALU code reads it.
+__device__ __forceinline__ void mfma16_vacc_first(f32x4& acc, bf16x8 a, bf16x8 b) {
+  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_vacc(f32x4& acc, bf16x8 a, bf16x8 b) {
+  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
 // acc (=|+=) A * B on v_mfma_f32_16x16x32_bf16 with the accumulator pinned

@@ -84,6 +84,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 bool prefill_wide_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t stream);
 
+// Head dim 256 (prefill_split.hip): the PV product split over head-dim
+// columns across the waves of a workgroup.
+bool prefill_split_schedule(int d, int group, PrefillSchedule* s);
+hipError_t launch_prefill_split(const PrefillArgs& a, hipStream_t stream);
+
 constexpr int kDecodeChunk = 512;  // keys per split chunk (fixed; ATTN_DECODE_CHUNK)
 constexpr int kDecodeStage = 16;   // keys per pipeline stage inside a chunk (one cache block)
 constexpr int decode_record_floats(int d) { return d + 4; }  // acc[d], m, l, pad

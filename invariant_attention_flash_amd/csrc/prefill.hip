@@ -53,12 +53,9 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "prefill_common.h"
 
 namespace invattn {
-
-// Reference-max hysteresis (log2 units): m moves only when a tile max
-// exceeds it by more than this.  A fixed constant of the arithmetic.
-constexpr float kRescale = 8.0f;
 
 template <int D_, int G_, int RB_, int NST_>
 struct Pf16Cfg {
@@ -84,61 +81,20 @@ struct Pf16Cfg {
   static_assert(RB * kDb * 4 + 2 * RB * 8 <= 256, "accumulators fit the AGPR file");
 };
 
-// Per-lane constants.  LDS operand addresses are byte offsets: a lane base
-// plus (lane xor ^ step constant); the xors are laundered once per tile step
-// (opaque) so the compiler forms each address next to its read instead of
-// keeping one register per (buffer, step) alive across the loop.
-struct Lane16 {
-  int x, gq;           // lane = 16*gq + x
-  uint32_t krow;       // K operand: byte offset of key row x
-  uint32_t kq16;       // K operand: (logical chunk ^ physical chunk) of k-step 0, in bytes
-  uint32_t vrow;       // V transpose read: byte offset of row 4*gq + x/4, element 4*(x%2)
-  uint32_t vc16;       // V transpose read: physical chunk of block 0, in bytes
-  int wlim;            // window (or a huge value for global layers)
-  float c2;            // fl32(scale * log2 e)
-};
 
-template <class T>
-__device__ __forceinline__ T opaque(T x) {
-  __asm__ volatile("" : "+v"(x));
-  return x;
-}
-
-// Direct HBM -> LDS loads (raw buffer loads with the LDS bit, 16 B per lane)
-// of the K and V tiles of keys k0 .. k0+31 into a stage buffer (K tile, then
-// V tile).  The buffer resources span exactly the sequence's rows of this
-// KV head, so keys past the sequence end are out of range and land as zeros
-// (masked later); a zero-length resource loads nothing and writes zeros
-// (used where no tile is left, so the code stays branch-free).  Buffer
-// rather than global loads: the compiler then tracks them on the
-// vector-memory counter alone, and LDS reads that follow keep their partial
-// waits.
-// Load j of this lane's 2*kLoads loads of the tile starting at key k0 (even
-// j: K, odd j: V) from the rows [kb, kb + nbytes) and [vb, vb + nbytes);
-// nbytes = 0 when there is no tile (the loads then write zeros).
+// Load j of this lane's 2*kLoads direct loads of the tile starting at key
+// k0 into a stage buffer (even j: K rows from kb, odd j: V rows from vb,
+// after the K tile); nbytes = 0 when there is no tile (zeros land).
 template <class C>
 __device__ __forceinline__ void dma_load(bf16* __restrict__ kv, const bf16* kb, const bf16* vb,
                                          int nbytes, int k0, int j, uint32_t rs_bytes, int wave,
                                          int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot type the buffer builtins here
-  const int i = j >> 1;
-  const int slot = (wave * C::kLoads + i) * 64;  // first 16-byte slot of this load
-  const int pch = slot + lane;
-  const int row = pch / C::kChunks;
-  const int pc = pch % C::kChunks;
-  const uint32_t roff = (uint32_t)(k0 + row) * rs_bytes;
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nbytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, nbytes, kBufferFlags);
   if ((j & 1) == 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, LDS_PTR(void, kv + slot * 8), 16,
-                                             roff + ((pc ^ (row & C::kSwK)) << 4), 0, 0, 0);
+    dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(lds_addr(kv), buffer_rsrc(kb, nbytes), k0, j >> 1,
+                                                 rs_bytes, wave, lane);
   else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, LDS_PTR(void, kv + C::kTile + slot * 8), 16,
-                                             roff + ((pc ^ ((row << 1) & C::kSwV)) << 4), 0, 0,
-                                             0);
-#endif
+    dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(lds_addr(kv + C::kTile), buffer_rsrc(vb, nbytes),
+                                                 k0, j >> 1, rs_bytes, wave, lane);
 }
 
 template <class C>
@@ -148,116 +104,6 @@ __device__ __forceinline__ void issue16(bf16* __restrict__ kv, const bf16* kb, c
 #pragma unroll
   for (int j = 0; j < 2 * C::kLoads; ++j)
     dma_load<C>(kv, kb, vb, nbytes, k0, j, rs_bytes, wave, lane);
-}
-
-// Row statistics of one tile, fast path: probabilities against the current
-// reference max (no dependency on this tile's max), their sum, and the
-// scaled tile max that decides whether the reference max must move.
-// Mask of key j for a row at position qp: allowed when 0 <= qp - j < wlim
-// (causal, window) or j lies in the row's span [ss, se); both tests are one
-// unsigned compare each: wbase = qp - k0 - 4*gq, sbase = k0 + 4*gq - ss.
-template <class C, bool MASK>
-__device__ __forceinline__ void tile_values(const f32x4 (*s)[2], int rb, int k0, const Lane16& ln,
-                                            const int* qpos, const int* ss, const int* se,
-                                            float* v) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = s[rb][e >> 2][e & 3];
-  if constexpr (MASK) {
-    const int wbase = qpos[rb] - k0 - 4 * ln.gq;
-    const int sbase = k0 + 4 * ln.gq - ss[rb];
-    const uint32_t slen = (uint32_t)(se[rb] - ss[rb]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = 16 * (e >> 2) + (e & 3);  // key j = k0 + 4*gq + c
-      const bool ok = ((uint32_t)(wbase - c) < (uint32_t)ln.wlim) | ((uint32_t)(sbase + c) < slen);
-      v[e] = ok ? v[e] : kNegInf;
-    }
-  }
-}
-
-// p = exp2(fma(s, c, -msub)) for the 8 slots of a row block, their sum in
-// the fixed pairwise order ((p0+p1)+(p2+p3)) + ((p4+p5)+(p6+p7)), then across
-// lanes l^32 and l^16 (each step: lower lane's value + upper lane's value),
-// and the bf16 operand.
-__device__ __forceinline__ float probs(const float* v, float c2, float msub, bf16x8& pb) {
-  float p[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(v[e], c2, -msub));
-#pragma unroll
-  for (int e = 0; e < 8; ++e) pb[e] = to_bf16(p[e]);
-  float sum = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-  HalfPair hp = half_pair(sum);
-  sum = hp.lo + hp.hi;
-  hp = row_pair(sum);
-  return hp.lo + hp.hi;
-}
-
-// Scaled tile max of a row (max over the 8 slots, then lanes l^32, l^16).
-__device__ __forceinline__ float row_max_scaled(const float* v, float c2) {
-  float t = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                  fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-  HalfPair hp = half_pair(t);
-  t = fmaxf(hp.lo, hp.hi);
-  hp = row_pair(t);
-  return fmaxf(hp.lo, hp.hi) * c2;
-}
-
-// Softmax of tile t for every row block, fast path.  Returns true when some
-// row's reference max must move (tile max > m + kRescale, or the first
-// allowed keys); then softmax_move() redoes the tile.  Otherwise p used m,
-// alpha = 1 and l += sum -- bitwise what the moving rule gives.
-template <class C, bool MASK>
-__device__ __forceinline__ bool softmax_fast(const f32x4 (*s)[2], int k0, const Lane16& ln,
-                                             const int* qpos, const int* ss, const int* se,
-                                             const float* m, float* l, bf16x8* pb) {
-  bool any = false;
-#pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) {
-    float v[8];
-    tile_values<C, MASK>(s, rb, k0, ln, qpos, ss, se, v);
-    const float m_old = m[rb];
-    const float sum = probs(v, ln.c2, m_old == kNegInf ? 0.f : m_old, pb[rb]);
-    const float tmax = row_max_scaled(v, ln.c2);
-    const bool move = (tmax > m_old + kRescale) | ((m_old == kNegInf) & (tmax != kNegInf));
-    any |= move;
-    l[rb] = move ? l[rb] : l[rb] + sum;
-  }
-  return __builtin_amdgcn_ballot_w64(any) != 0;
-}
-
-// The rare path: rows whose tile max exceeds m + kRescale (or whose first
-// allowed keys are in this tile) move m to the tile max, scale l and the
-// accumulator by alpha = 2^(m_old - m_new) (1 when m_old = -inf: the
-// accumulator and sum are still exact zeros) and recompute p with the new m.
-template <class C, bool MASK, bool SCALE>
-__device__ __forceinline__ void softmax_move(const f32x4 (*s)[2], int k0, const Lane16& ln,
-                                             const int* qpos, const int* ss, const int* se,
-                                             float* m, float* l, bf16x8* pb,
-                                             f32x4 (*o)[C::kDb]) {
-#pragma unroll
-  for (int rb = 0; rb < C::RB; ++rb) {
-    float v[8];
-    tile_values<C, MASK>(s, rb, k0, ln, qpos, ss, se, v);
-    const float m_old = m[rb];
-    const float tmax = row_max_scaled(v, ln.c2);
-    const bool move = (tmax > m_old + kRescale) | ((m_old == kNegInf) & (tmax != kNegInf));
-    if (__builtin_amdgcn_ballot_w64(move) == 0) continue;
-    const float m_new = move ? tmax : m_old;
-    const float alpha = (move & (m_old != kNegInf)) ? fast_exp2(m_old - m_new) : 1.f;
-    bf16x8 pnew;
-    const float sum = probs(v, ln.c2, m_new == kNegInf ? 0.f : m_new, pnew);
-    if (move) {
-      pb[rb] = pnew;
-      l[rb] = l[rb] * alpha + sum;
-      m[rb] = m_new;
-    }
-    if constexpr (SCALE) {
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < C::kDb; ++db) o[rb][db] *= alpha;
-      }
-    }
-  }
 }
 
 // One pipelined tile step: S^T(t+1) = K Q^T on the K tile `ks` and
@@ -458,7 +304,7 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   issue16<C>(kvs[1], kb, vb, extent(kt0 + 1), (kt0 + 1) * BN, rs_bytes, wave, lane);
   issue16<C>(kvs[2], kb, vb, extent(kt0 + 2), (kt0 + 2) * BN, rs_bytes, wave, lane);
   wait_vmcnt<2 * kPerTile>();
-  __syncthreads();
+  lds_barrier();
 
   // Scores and probabilities of consecutive tiles alternate between two
   // arrays each (steps are unrolled by two), so nothing is copied.
@@ -487,25 +333,38 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // Tile kt+1 must have landed; tile kt+2 may still be in flight (every
     // step issues one tile's loads, real or zero-length).
     wait_vmcnt<kPerTile>();
-    __syncthreads();
+    lds_barrier();
     const int next_bytes = extent(kt + 3);
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
     const uint32_t kq16 = opaque(ln.kq16), vc16 = opaque(ln.vc16);
+    // Scale the accumulator blocks whose rows moved their reference max
+    // (after PV(kt-1) is in: it belongs to the old reference).
+    float alpha[RB];
+    auto rescale = [&](uint32_t mask) {
+      if constexpr (PV) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (mask & (1u << rb)) {
+#pragma unroll
+            for (int db = 0; db < C::kDb; ++db) oacc[rb][db] *= alpha[rb];
+          }
+      }
+    };
     if (need_mask) {
-      const bool moved = softmax_fast<C, true>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
+      const bool moved = softmax_fast<RB, true>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
       mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, kb, vb, next_bytes, (kt + 3) * BN, rs_bytes,
                                      wave,
                                      lane, ln.krow, kq16,
                                      ln.vrow, vc16, qr, sn, pp, oacc);
-      if (moved) softmax_move<C, true, PV>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, oacc);
+      if (moved) rescale(softmax_move<RB, true>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, alpha));
     } else {
-      const bool moved = softmax_fast<C, false>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
+      const bool moved = softmax_fast<RB, false>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
       mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, kb, vb, next_bytes, (kt + 3) * BN, rs_bytes,
                                      wave,
                                      lane, ln.krow, kq16,
                                      ln.vrow, vc16, qr, sn, pp, oacc);
-      if (moved) softmax_move<C, false, PV>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, oacc);
+      if (moved) rescale(softmax_move<RB, false>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, alpha));
     }
   };
   using Mode0 = std::integral_constant<int, 0>;
@@ -570,7 +429,12 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   X(256, 1, PF_CFG256) X(256, 2, PF_CFG256) X(256, 4, PF_CFG256)              \
   X(256, 8, PF_CFG256)
 
+#ifndef PF_SPLIT256
+#define PF_SPLIT256 1
+#endif
+
 bool prefill_schedule(int d, int group, PrefillSchedule* s) {
+  if (PF_SPLIT256 && prefill_split_schedule(d, group, s)) return true;
 #define X(D, G, ...)                                                          \
   if (d == D && group == G) {                                                 \
     using C = Pf16Cfg<D, G, __VA_ARGS__>;                                     \
@@ -584,6 +448,8 @@ bool prefill_schedule(int d, int group, PrefillSchedule* s) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
+  PrefillSchedule sp;
+  if (PF_SPLIT256 && prefill_split_schedule(a.d, group, &sp)) return launch_prefill_split(a, stream);
 #define X(D, G, ...) \
   if (a.d == D && group == G) return launch_one<Pf16Cfg<D, G, __VA_ARGS__>>(a, stream);
   INVATTN_PREFILL_TABLE(X)
