@@ -21,11 +21,11 @@
 // order, whatever else is in the batch.
 //
 // Per KV tile (BN keys, ascending):
-//   K and V tiles stream HBM -> LDS with direct loads (global_load_lds,
-//   16 B per lane) into a ring of NST stage buffers, so later tiles land
-//   while this one is computed; rows are stored unpadded with an XOR swizzle
-//   of their 16-byte chunks (conflict-free MFMA operand reads).  Keys past
-//   the sequence end read the sequence's last row and are masked (p = 0).
+//   K and V tiles stream HBM -> LDS with direct loads (buffer loads with the
+//   LDS bit, 16 B per lane) into a ring of NST stage buffers, so later tiles
+//   land while this one is computed; rows are stored unpadded with an XOR
+//   swizzle of their 16-byte chunks (conflict-free MFMA operand reads).  Keys
+//   past the sequence end land as zeros and are masked (p = 0).
 //   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, read once
 //                and used by every row block of the wave; B = Q in
 //                registers), so each lane holds one query's scores; with
@@ -48,12 +48,9 @@
 // so the bytes of a row never depend on the rest of the batch.
 #include "device_common.h"
 #include "kernels.h"
+#include "prefill_common.h"
 
 namespace invattn {
-
-// Reference-max hysteresis (log2 units): m moves only when a tile max
-// exceeds it by more than this.  A fixed constant of the arithmetic.
-constexpr float kRescale = 8.0f;
 #ifndef PF_AHEAD_QK
 #define PF_AHEAD_QK 3
 #endif
@@ -94,23 +91,17 @@ struct PrefillCfg {
 };
 
 // Direct HBM -> LDS loads of one K and one V tile (keys k0 .. k0+BN-1) into
-// the stage buffer `kv` (K tile, then V tile).  Lane offsets (elements,
-// 32-bit; one sequence's K or V stays below 4 GiB) are row*stride + swizzled
-// chunk; keys past the sequence end clamp to its last row (offset last_row).
+// the stage buffer `kv` (K tile, then V tile), through buffer resources that
+// span exactly the sequence's rows of this KV head: keys past the sequence
+// end land as zeros (and are masked).
 template <class C>
-__device__ __forceinline__ void issue_tile(bf16* kv, int k0, uint32_t rs, uint32_t last_row,
-                                           const uint32_t* ld_row, const uint32_t* ld_ck,
-                                           const uint32_t* ld_cv, const bf16* kbase,
-                                           const bf16* vbase, int wave) {
-  const uint32_t base = (uint32_t)k0 * rs;
+__device__ __forceinline__ void issue_tile(bf16* kv, int k0, uint32_t rs_bytes, const u32x4& krs,
+                                           const u32x4& vrs, int wave, int lane) {
+  const uint32_t kl = lds_addr(kv), vl = lds_addr(kv + C::kTile);
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
-    const int cbase = (wave * C::kLoads + i) * 64;
-    const uint32_t off = min(base + ld_row[i], last_row);
-    __builtin_amdgcn_global_load_lds(kbase + (off + ld_ck[i]), LDS_PTR(void, kv + cbase * 8), 16,
-                                     0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + (off + ld_cv[i]),
-                                     LDS_PTR(void, kv + C::kTile + cbase * 8), 16, 0, 0);
+    dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kl, krs, k0, i, rs_bytes, wave, lane);
+    dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vl, vrs, k0, i, rs_bytes, wave, lane);
   }
 }
 
@@ -171,7 +162,7 @@ __device__ __forceinline__ void compute_tile(const bf16* __restrict__ ks,
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           xchg[(wave * kRec + (r * C::kSBlk + blk) * 16 + i) * 64 + lane] = sacc[r][blk][i];
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int r = 0; r < RBW; ++r)
 #pragma unroll
@@ -340,24 +331,16 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   }
 
-  const uint32_t rs = (uint32_t)hkv * D;
-  const bf16* kbase = k + ((size_t)seq0 * hkv + g) * D;
-  const bf16* vbase = v + ((size_t)seq0 * hkv + g) * D;
-  const uint32_t last_row = (uint32_t)(L - 1) * rs;
-  uint32_t ld_row[C::kLoads], ld_ck[C::kLoads], ld_cv[C::kLoads];
-#pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    const int pch = (wave * C::kLoads + i) * 64 + lane;
-    const int row = pch / C::kChunks;
-    const int pc = pch % C::kChunks;
-    ld_row[i] = (uint32_t)row * rs;
-    ld_ck[i] = (uint32_t)((pc ^ (row & C::kSwK)) << 3);
-    ld_cv[i] = (uint32_t)((pc ^ ((row << 1) & C::kSwV)) << 3);
-  }
+  // This KV head's rows of the sequence, loaded through buffer resources of
+  // exactly that extent (the host rejects inputs whose rows span 2 GiB or
+  // more).
+  const uint32_t rs_bytes = (uint32_t)hkv * D * 2;
+  const int nbytes = (int)((uint32_t)L * rs_bytes);
+  const u32x4 krs = buffer_rsrc(k + ((size_t)seq0 * hkv + g) * D, nbytes);
+  const u32x4 vrs = buffer_rsrc(v + ((size_t)seq0 * hkv + g) * D, nbytes);
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
-  issue_tile<C>(kv0, kt0 * BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase, vbase, wave);
-  if (C::kStages > 2 && kt0 + 1 < kt1)
-    issue_tile<C>(kv1, (kt0 + 1) * BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase, vbase, wave);
+  issue_tile<C>(kv0, kt0 * BN, rs_bytes, krs, vrs, wave, lane);
+  if (C::kStages > 2 && kt0 + 1 < kt1) issue_tile<C>(kv1, (kt0 + 1) * BN, rs_bytes, krs, vrs, wave, lane);
 
   // Q^T operands: lane holds q[row][dh*DW + 16*s + 8*hh .. +7] for every s.
   bf16x8 qr[RBW][C::kSteps];
@@ -392,10 +375,9 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int k0 = kt * BN;
     if (kt + C::kStages - 2 < kt1) wait_vmem_keep<C::kStages - 2>(2 * C::kLoads);
     else wait_vmem();
-    __syncthreads();
+    lds_barrier();
     if (kt + C::kStages - 1 < kt1)
-      issue_tile<C>(pre, (kt + C::kStages - 1) * BN, rs, last_row, ld_row, ld_ck, ld_cv, kbase,
-                    vbase, wave);
+      issue_tile<C>(pre, (kt + C::kStages - 1) * BN, rs_bytes, krs, vrs, wave, lane);
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
     compute_tile<C>(cur, cur + C::kTile, xchg, k0, need_mask, ln, qr, oacc, m, l);

@@ -1,0 +1,57 @@
+"""Static checks on the compiled gfx950 prefill kernels (CPU only: hipcc
+cross-compiles to assembly here).
+
+The direct HBM -> LDS tile loads are issued from inline assembly that sets
+M0 (the LDS address of the load) without saving it: that is only sound while
+the compiler emits no M0 use of its own in these kernels.  This test compiles
+the kernels that issue such loads and checks that every M0 reference sits
+inside an inline-assembly block.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from invariant_attention_flash_amd import build as ia_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "invariant_attention_flash_amd", "csrc")
+HIPCC = "/opt/rocm/bin/hipcc"
+
+
+def _compile_asm(src, tmp_path):
+    out = os.path.join(str(tmp_path), os.path.basename(src) + ".s")
+    cmd = [HIPCC, "--offload-arch=gfx950", "--cuda-device-only", "-S", "-O3", "-std=c++17",
+           "-fno-fast-math", "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-Wno-unused-command-line-argument",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return open(out).read()
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("name", ["prefill.hip", "prefill_split.hip", "prefill_wide.hip"])
+def test_m0_only_in_direct_loads(name, tmp_path):
+    assert name in ia_build.SOURCES
+    text = _compile_asm(os.path.join(CSRC, name), tmp_path)
+    inside = False
+    loads = 0
+    for line in text.splitlines():
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        if t.startswith(";") or t.startswith("."):
+            continue
+        code = t.split(";")[0]
+        if re.search(r"\bm0\b", code):
+            assert inside, f"compiler-emitted M0 use in {name}: {t}"
+        if inside and "buffer_load_dwordx4" in code and code.rstrip().endswith("lds"):
+            loads += 1
+    assert loads > 0, "no direct loads found"
