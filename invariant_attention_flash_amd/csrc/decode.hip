@@ -28,6 +28,7 @@
 // acc_c*2^(m_c-m'); l likewise), then o = bf16_rne(acc / l).
 #include "device_common.h"
 #include "kernels.h"
+#include "prefill_common.h"
 
 namespace invattn {
 
@@ -59,25 +60,23 @@ struct DecodeCfg {
 };
 
 // Direct loads of cache block `blk` (keys k0 .. k0+15) into stage buffer kv
-// (K rows then V rows).  Slots at or past the sequence end read slot
-// `last_slot` (the last key) instead; they are masked.
+// (K rows then V rows), through buffer resources that end at the sequence's
+// last key: slots at or past the sequence end land as zeros (and are masked).
 template <class C>
 __device__ __forceinline__ void issue_block(bf16* kv, const bf16* kc, const bf16* vc,
                                            size_t blk_base, int k0, int L, uint32_t slot_stride,
                                            uint32_t head_off, int wave, int lane) {
   if (wave >= C::kLoadWaves) return;
+  const uint32_t row_bytes = slot_stride * 2;
+  const int rows = max(min(C::kKeys, L - k0), 0);
+  const int nbytes = (int)((uint32_t)rows * row_bytes);
+  const u32x4 krs = buffer_rsrc(kc + blk_base + head_off, nbytes);
+  const u32x4 vrs = buffer_rsrc(vc + blk_base + head_off, nbytes);
+  const uint32_t kl = lds_addr(kv), vl = lds_addr(kv + C::kTile);
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
-    const int cbase = (wave * C::kLoads + i) * 64;
-    const int pch = cbase + lane;
-    const int row = pch / C::kChunks;
-    const int pc = pch % C::kChunks;
-    const int slot = (k0 + row < L) ? row : (L - 1 - k0);
-    const uint32_t off = (uint32_t)slot * slot_stride + head_off;
-    __builtin_amdgcn_global_load_lds(kc + blk_base + off + ((pc ^ (row & C::kSwK)) << 3),
-                                     LDS_PTR(void, kv + cbase * 8), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vc + blk_base + off + ((pc ^ ((row << 1) & C::kSwV)) << 3),
-                                     LDS_PTR(void, kv + C::kTile + cbase * 8), 16, 0, 0);
+    dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kl, krs, 0, i, row_bytes, wave, lane);
+    dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vl, vrs, 0, i, row_bytes, wave, lane);
   }
 }
 
@@ -158,7 +157,7 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
   auto step = [&] __device__(const bf16* cur, bf16* pre, int kb) {
     if (kb + C::kStages - 2 < kb1) wait_vmem_keep<C::kStages - 2>(2 * C::kLoads);
     else wait_vmem();
-    __syncthreads();
+    lds_barrier();
     const int nb = kb + C::kStages - 1;
     if (nb < kb1)
       issue_block<C>(pre, kc, vc, block_base(nb), nb * C::kKeys, L, slot_stride, head_off, wave,

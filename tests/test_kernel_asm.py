@@ -1,4 +1,4 @@
-"""Static checks on the compiled gfx950 prefill kernels (CPU only: hipcc
+"""Static checks on the compiled gfx950 kernels (CPU only: hipcc
 cross-compiles to assembly here).
 
 The direct HBM -> LDS tile loads are issued from inline assembly that sets
@@ -33,7 +33,7 @@ def _compile_asm(src, tmp_path):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("name", ["prefill.hip", "prefill_split.hip", "prefill_wide.hip"])
+@pytest.mark.parametrize("name", ["prefill.hip", "prefill_split.hip", "prefill_wide.hip", "decode.hip"])
 def test_m0_only_in_direct_loads(name, tmp_path):
     assert name in ia_build.SOURCES
     text = _compile_asm(os.path.join(CSRC, name), tmp_path)
