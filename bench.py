@@ -117,8 +117,9 @@ def write_traffic(fetch_dir, write_dir):
         if not calib:
             raise SystemExit(f"no calibration kernel found in {d}")
         scale = CALIBRATION_BYTES / (1024.0 * float(np.median(calib)))
-        for key, match, first in (("prefill_kernel<256,2>", "prefill_kernel<invattn::PrefillCfg<256, 2",
-                                   "prefill_kernel"),
+        for key, match, first in (("prefill_split_kernel<256,2>",
+                                   "prefill_split_kernel<invattn::PfSplitCfg<256, 2>",
+                                   "prefill_split_kernel"),
                                   ("decode_chunk_kernel+decode_merge_kernel<512,8>", "decode_",
                                    "decode_chunk_kernel")):
             vals = [v for k, v, g in rows if match in k]
@@ -267,8 +268,8 @@ def main():
 
     pf_roof = {"bound": "mfma", "achieved": pf_tflops, "peak": PEAK_BF16_TFLOPS,
                "unit": "TFLOP/s", "frac": pf_tflops / PEAK_BF16_TFLOPS,
-               "traffic": load_traffic("prefill_kernel<256,2,32>"),
-               "kernel": "prefill_kernel (head_dim 256, group 2)",
+               "traffic": load_traffic("prefill_split_kernel<256,2>"),
+               "kernel": "prefill_split_kernel (head_dim 256, group 2)",
                "work_per_launch": f"{flops:.4g} FLOP = 4*256*32*{pairs} allowed pairs",
                "avg_launch_ms": pf_ms}
     dc_roof = {"bound": "hbm", "achieved": dc_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",

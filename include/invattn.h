@@ -11,17 +11,29 @@
  * no fast-math; casts only at the three declared points; unsupported
  * geometry fails closed with an error and never falls back to another path.
  *
- * Arithmetic, for each query row i with allowed key set A_i:
- *   s_j  = fp32 MFMA dot product of bf16 q_i and bf16 k_j (d ascending in
- *          16-element MFMA steps), then s_j * c with c = fl32(scale*log2(e))
- *   m    = running max over the keys visited so far (fp32, exact)
- *   p_j  = exp2(s_j * c - m)          (hardware exp2, fp32)
- *   l    = l * exp2(m_old - m) + sum_j p_j        (fp32, fixed order)
- *   acc  = acc * exp2(m_old - m) + bf16(p) . v    (bf16 MFMA, fp32 acc)
- *   o    = bf16_rne(acc / l)          (IEEE fp32 division)
- * KV tiles are visited in one ascending order per query row.  Declared casts:
- * inputs are bf16 as given; p -> bf16 (round to nearest even) before the PV
- * product; o -> bf16 (round to nearest even).
+ * Arithmetic, for each query row i with allowed key set A_i, keys visited
+ * in one ascending order of 32-key tiles (prefill) or 16-key cache blocks
+ * (decode), c = fl32(scale * log2(e)):
+ *   s_j  = fp32 MFMA dot product of bf16 q_i and bf16 k_j, head dim in
+ *          ascending MFMA steps (head dim 512: two halves summed as
+ *          half 0 + half 1)
+ *   m    = reference max (scaled units), -inf before the first allowed key;
+ *          it moves to the tile's scaled max only when the row would
+ *          otherwise see p > 2^8 (head dim 256: tested on p itself; other
+ *          head dims and decode: tile max > m + 8), or at the first
+ *          allowed key
+ *   p_j  = exp2(fma(s_j, c, -m))          (hardware exp2, fp32; m -> 0
+ *          while m = -inf)
+ *   l    = l * alpha + (sum of the tile's p in a fixed order); head dim
+ *          256 keeps one such sum per lane and combines a row's four lanes
+ *          once, after the last tile, in a fixed order
+ *   acc  = acc * alpha + bf16(p) . v      (bf16 MFMA, fp32 accumulate)
+ *          with alpha = exp2(m_old - m_new) on a move, else 1 (no multiply)
+ *   o    = bf16_rne(acc / l)              (IEEE fp32 division)
+ * The rules are fixed per (head dim, group size); a row's bytes depend
+ * only on its own sequence.  Declared casts: inputs are bf16 as given;
+ * p -> bf16 (round to nearest even) before the PV product; o -> bf16 (round
+ * to nearest even).
  *
  * Threading: stateless apart from the thread-local error text and
  * provenance record; calls from several host threads are safe.
