@@ -124,6 +124,62 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
                         void* stream);
 
 /*
+ * attn_prefill_paged -- chunked prefill: each sequence's new query tokens
+ * attend to its keys already in a paged KV cache (the cached prefix plus the
+ * chunk itself), read in place through the block table.
+ *
+ * Passages: a row is invariant to chunking ("RFC: Gemma-4-31B-it
+ * train/rollout consistency", section 4, item 6); strict calls consume the
+ * paged KV cache directly ("Vime ROCm Attention operator ablation", section
+ * "Prerequisites"); layer types as attn_prefill_varlen.
+ *
+ * Sequence b has n_b = cu_seqlens[b+1] - cu_seqlens[b] new tokens, at
+ * positions [q_start[b], q_start[b] + n_b); its keys are positions
+ * [0, q_start[b] + n_b), all already written to the cache (the chunk's own
+ * K/V included).  Query i attends to key j when 0 <= i - j (< window).
+ * Every output row is bitwise identical to the row of the same position
+ * from attn_prefill_varlen over the whole sequence with the same K/V
+ * (positions are tiled from 0 in both), whatever the chunk boundaries.
+ *
+ * Arguments (device pointers caller-owned):
+ *   q          bf16 [T, num_q_heads, head_dim], packed new tokens, contiguous
+ *   k_cache, v_cache  bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   o          bf16 [T, num_q_heads, head_dim]; rows beyond cu_seqlens[batch]
+ *              are not written
+ *   lse_opt    fp32 [T, num_q_heads] as attn_prefill_varlen, or NULL
+ *   cu_seqlens int32 [batch+1]: packed ranges of the new tokens, as
+ *              attn_prefill_varlen (an empty range is allowed)
+ *   q_start    int32 [batch], >= 0: position of each sequence's first new
+ *              token (the length of its cached prefix)
+ *   block_table int32 [batch, max_blocks_per_seq]; key j of sequence b is in
+ *              block block_table[b][j / block_size], slot j % block_size.
+ *              Cache blocks are read only for keys in [first attended key of
+ *              the first new token, q_start[b] + n_b); entries of other blocks
+ *              may be read from the table but may hold anything.  An entry
+ *              used outside [0, num_blocks) is clamped into it
+ *              (INVATTN_VALIDATE=1 rejects it)
+ *   batch      >= 0 (0 -> nothing enqueued)
+ *   max_query_len    host bound on every n_b (sizes the grid only)
+ *   max_context_len  host bound on every q_start[b] + n_b; at most
+ *              max_blocks_per_seq * block_size
+ *   num_blocks, block_size (must be 16), num_q_heads, num_kv_heads,
+ *   head_dim, window, softmax_scale: as attn_decode_paged / attn_prefill_varlen
+ *   stream     HIP stream
+ * No bidirectional spans in this layout.
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED, ATTN_E_ALIGN,
+ * ATTN_E_HIP, ATTN_E_VALIDATE; nothing is enqueued on error.
+ */
+int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                       void* o, float* lse_opt, const int32_t* cu_seqlens,
+                       const int32_t* q_start, const int32_t* block_table,
+                       int32_t max_blocks_per_seq, int32_t batch,
+                       int32_t max_query_len, int32_t max_context_len,
+                       int32_t num_blocks, int32_t block_size,
+                       int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t window, float softmax_scale,
+                       void* stream);
+
+/*
  * attn_decode_workspace_size -- bytes of fp32 workspace attn_decode_paged
  * needs for this batch: [batch, num_q_heads, ceil(max_seq_len /
  * ATTN_DECODE_CHUNK), head_dim + 4] fp32 (per chunk record: the unnormalised

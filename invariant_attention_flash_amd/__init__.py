@@ -9,6 +9,8 @@ built, or the GPU is missing, calls raise.
 Entry points (same names as the C ABI):
   attn_prefill_varlen  packed variable-length prefill, sliding or global,
                        GQA, optional bidirectional spans
+  attn_prefill_paged   chunked prefill: new query tokens against the keys of
+                       a paged KV cache (cached prefix plus the chunk)
   attn_decode_paged    one query token per sequence over a paged KV cache
   attn_decode_workspace_size
 """
@@ -18,7 +20,7 @@ import ctypes
 import json
 import os
 
-__all__ = ["attn_prefill_varlen", "attn_decode_paged", "attn_decode_workspace_size",
+__all__ = ["attn_prefill_varlen", "attn_prefill_paged", "attn_decode_paged", "attn_decode_workspace_size",
            "last_provenance", "last_error", "AttnError", "library", "LIB_PATH",
            "ATTN_WINDOW_NONE", "ATTN_DECODE_CHUNK", "ERROR_CODES", "EXPORTS"]
 
@@ -27,7 +29,7 @@ ATTN_WINDOW_NONE = -1
 ATTN_DECODE_CHUNK = 512
 ERROR_CODES = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
                4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP", 7: "ATTN_E_VALIDATE"}
-EXPORTS = ["attn_prefill_varlen", "attn_decode_workspace_size", "attn_decode_paged",
+EXPORTS = ["attn_prefill_varlen", "attn_prefill_paged", "attn_decode_workspace_size", "attn_decode_paged",
            "attn_last_error", "attn_last_provenance", "attn_version"]
 
 
@@ -53,6 +55,9 @@ def library():
         lib.attn_prefill_varlen.restype = ctypes.c_int
         lib.attn_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                             i32, f32, vp, i32, vp]
+        lib.attn_prefill_paged.restype = ctypes.c_int
+        lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                           i32, i32, i32, i32, i32, i32, f32, vp]
         lib.attn_decode_workspace_size.restype = sz
         lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         lib.attn_decode_paged.restype = ctypes.c_int
@@ -148,6 +153,48 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, window=ATTN_WINDOW_NONE
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
         cu_seqlens.shape[0] - 1, int(max_seqlen), hq, hkv, d, int(window),
         float(softmax_scale), _ptr(spans), ns, _stream(stream))
+    _check(rc)
+    return out
+
+
+def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens, q_start, max_query_len,
+                       max_context_len, window=ATTN_WINDOW_NONE, softmax_scale=None, out=None,
+                       lse=None, stream=None):
+    """Chunked prefill over a paged KV cache.
+
+    q [T, Hq, D] bf16 (packed new tokens); k_cache/v_cache [NB, 16, Hkv, D]
+    bf16 holding every key of each sequence up to its last new token;
+    block_table int32 [B, MB]; cu_seqlens int32 [B+1] (packed new-token
+    ranges); q_start int32 [B] (position of each sequence's first new token);
+    out bf16 [T, Hq, D] (allocated if None); lse fp32 [T, Hq] or None.
+    Returns out.
+    """
+    import torch
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, 4)
+    _require(block_table, "block_table", torch.int32, 2)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _require(q_start, "q_start", torch.int32, 1)
+    T, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d:
+        raise ValueError("caches must be [NB, BS, Hkv, D] matching q")
+    B = cu_seqlens.shape[0] - 1
+    if q_start.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("q_start and block_table must have one entry per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 2)
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    rc = library().attn_prefill_paged(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(cu_seqlens),
+        _ptr(q_start), _ptr(block_table), block_table.shape[1], B, int(max_query_len),
+        int(max_context_len), nb, bs, hq, hkv, d, int(window), float(softmax_scale),
+        _stream(stream))
     _check(rc)
     return out
 

@@ -216,6 +216,107 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, fl
   return ATTN_OK;
 }
 
+int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, void* o,
+                       float* lse_opt, const int32_t* cu_seqlens, const int32_t* q_start,
+                       const int32_t* block_table, int32_t max_blocks_per_seq, int32_t batch,
+                       int32_t max_query_len, int32_t max_context_len, int32_t num_blocks,
+                       int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t window, float softmax_scale, void* stream) {
+  g_err.clear();
+  if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
+  if (max_query_len < 0) return fail(ATTN_E_SHAPE, "max_query_len=%d must be >= 0", max_query_len);
+  int rc = check_heads(num_q_heads, num_kv_heads, head_dim, window, softmax_scale);
+  if (rc != ATTN_OK) return rc;
+  if (block_size != 16) return fail(ATTN_E_UNSUPPORTED, "block_size=%d must be 16", block_size);
+  if (batch > 65535) return fail(ATTN_E_UNSUPPORTED, "batch=%d exceeds 65535", batch);
+  const int group = num_q_heads / num_kv_heads;
+  PrefillSchedule sched;
+  if (!prefill_schedule(head_dim, group, &sched))
+    return fail(ATTN_E_UNSUPPORTED, "no kernel for head_dim=%d group=%d", head_dim, group);
+  char sid[160];
+  snprintf(sid, sizeof sid, "prefill_d%d_g%d_rows%d_pos%d_bn%d_t%d_paged16", head_dim, group,
+           sched.rows, sched.positions, sched.bn, sched.threads);
+  if (batch == 0 || max_query_len == 0) {
+    set_provenance("attn_prefill_paged", "none (empty input)", sid, "none", window, head_dim,
+                   num_q_heads, num_kv_heads, batch, 0);
+    return ATTN_OK;
+  }
+  if (max_context_len < max_query_len)
+    return fail(ATTN_E_SHAPE, "max_context_len=%d < max_query_len=%d", max_context_len,
+                max_query_len);
+  if (max_blocks_per_seq <= 0)
+    return fail(ATTN_E_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
+  if (num_blocks <= 0) return fail(ATTN_E_SHAPE, "num_blocks=%d must be >= 1", num_blocks);
+  if ((long long)max_blocks_per_seq * block_size < max_context_len)
+    return fail(ATTN_E_SHAPE, "max_blocks_per_seq*block_size=%lld < max_context_len=%d",
+                (long long)max_blocks_per_seq * block_size, max_context_len);
+  if (!q) return fail(ATTN_E_NULL, "q is NULL");
+  if (!k_cache) return fail(ATTN_E_NULL, "k_cache is NULL");
+  if (!v_cache) return fail(ATTN_E_NULL, "v_cache is NULL");
+  if (!o) return fail(ATTN_E_NULL, "o is NULL");
+  if (!cu_seqlens) return fail(ATTN_E_NULL, "cu_seqlens is NULL");
+  if (!q_start) return fail(ATTN_E_NULL, "q_start is NULL");
+  if (!block_table) return fail(ATTN_E_NULL, "block_table is NULL");
+  if (!aligned16(q)) return fail(ATTN_E_ALIGN, "q is not 16-byte aligned");
+  if (!aligned16(k_cache)) return fail(ATTN_E_ALIGN, "k_cache is not 16-byte aligned");
+  if (!aligned16(v_cache)) return fail(ATTN_E_ALIGN, "v_cache is not 16-byte aligned");
+  if (!aligned16(o)) return fail(ATTN_E_ALIGN, "o is not 16-byte aligned");
+  if (lse_opt && !aligned4(lse_opt)) return fail(ATTN_E_ALIGN, "lse_opt is not 4-byte aligned");
+  if (!aligned4(cu_seqlens)) return fail(ATTN_E_ALIGN, "cu_seqlens is not 4-byte aligned");
+  if (!aligned4(q_start)) return fail(ATTN_E_ALIGN, "q_start is not 4-byte aligned");
+  if (!aligned4(block_table)) return fail(ATTN_E_ALIGN, "block_table is not 4-byte aligned");
+  // The grid covers one more position tile than the query rows need (a chunk
+  // starts anywhere inside a tile).
+  const long long tiles = ((long long)max_query_len + sched.positions - 1) / sched.positions + 1;
+  if (tiles * num_kv_heads * batch > 0x7fffffffLL)
+    return fail(ATTN_E_UNSUPPORTED, "max_query_len=%d too large", max_query_len);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  long long tokens = -1;
+  if (validate_enabled()) {
+    std::vector<int32_t> cu, qs, bt;
+    if ((rc = fetch_ints(cu_seqlens, (size_t)batch + 1, cu, s, "copy cu_seqlens")) != ATTN_OK) return rc;
+    if ((rc = fetch_ints(q_start, (size_t)batch, qs, s, "copy q_start")) != ATTN_OK) return rc;
+    if ((rc = fetch_ints(block_table, (size_t)batch * max_blocks_per_seq, bt, s, "copy block_table")) != ATTN_OK)
+      return rc;
+    if (cu[0] != 0) return fail(ATTN_E_VALIDATE, "cu_seqlens[0]=%d must be 0", cu[0]);
+    for (int b = 0; b < batch; ++b) {
+      const int n = cu[b + 1] - cu[b];
+      if (n < 0) return fail(ATTN_E_VALIDATE, "cu_seqlens decreases at %d", b);
+      if (n > max_query_len)
+        return fail(ATTN_E_VALIDATE, "sequence %d has %d new tokens > max_query_len=%d", b, n,
+                    max_query_len);
+      if (qs[b] < 0 || (long long)qs[b] + n > max_context_len)
+        return fail(ATTN_E_VALIDATE, "q_start[%d]=%d with %d new tokens outside [0, max_context_len=%d]",
+                    b, qs[b], n, max_context_len);
+      if (n == 0) continue;
+      const int L = qs[b] + n;
+      const int lo = window > 0 ? (qs[b] - window + 1 > 0 ? qs[b] - window + 1 : 0) : 0;
+      for (int j = lo / block_size; j <= (L - 1) / block_size; ++j) {
+        const int id = bt[(size_t)b * max_blocks_per_seq + j];
+        if (id < 0 || id >= num_blocks)
+          return fail(ATTN_E_VALIDATE, "block_table[%d][%d]=%d outside [0, num_blocks=%d)", b, j,
+                      id, num_blocks);
+      }
+    }
+    tokens = cu[batch];
+  }
+
+  PrefillArgs a{q, k_cache, v_cache, o, lse_opt, cu_seqlens, nullptr, 0, batch, max_query_len,
+                num_q_heads, num_kv_heads, head_dim, window, fold_scale(softmax_scale)};
+  a.q_start = q_start;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context = max_context_len;
+  hipError_t e = launch_prefill(a, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  set_provenance("attn_prefill_paged", "prefill_kernel (paged keys)", sid,
+                 "none (one ascending KV walk per row)", window, head_dim, num_q_heads,
+                 num_kv_heads, batch, tokens);
+  return ATTN_OK;
+}
+
 size_t attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_q_heads,
                                   int32_t head_dim) {
   if (batch <= 0 || max_seq_len <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;

@@ -24,7 +24,21 @@ struct PrefillArgs {
   int32_t d;
   int32_t window;  // -1 = none
   float c2;        // fl32(scale * log2(e))
+  // Paged layout (attn_prefill_paged): k / v are the caches, max_seqlen
+  // bounds the query rows of one sequence.  q_start == nullptr: contiguous.
+  const int32_t* q_start = nullptr;
+  const int32_t* block_table = nullptr;
+  int32_t max_blocks = 0;
+  int32_t num_blocks = 0;
+  int32_t max_context = 0;
 };
+
+// Position tiles the grid covers per sequence: the query rows of a paged
+// chunk start anywhere inside a tile, so one more tile is needed.
+inline int prefill_grid_tiles(const PrefillArgs& a, int positions) {
+  const int t = (a.max_seqlen + positions - 1) / positions;
+  return a.q_start != nullptr ? t + 1 : t;
+}
 
 struct DecodeArgs {
   const void* q;

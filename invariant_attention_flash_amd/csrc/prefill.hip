@@ -59,6 +59,7 @@ namespace invattn {
 
 template <int D_, int G_, int RB_, int NST_>
 struct Pf16Cfg {
+  static constexpr bool kPaged = false;  // contiguous keys (PagedOf<> sets it)
   static constexpr int D = D_, G = G_, RB = RB_, NST = NST_;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
@@ -82,28 +83,30 @@ struct Pf16Cfg {
 };
 
 
-// Load j of this lane's 2*kLoads direct loads of the tile starting at key
-// k0 into a stage buffer (even j: K rows from kb, odd j: V rows from vb,
-// after the K tile); nbytes = 0 when there is no tile (zeros land).
+// Load j of this lane's 2*kLoads direct loads of one tile into a stage
+// buffer (even j: K rows through krs, odd j: V rows through vrs, after the
+// K tile); k0: the row offset of KvTiles::get.
 template <class C>
-__device__ __forceinline__ void dma_load(bf16* __restrict__ kv, const bf16* kb, const bf16* vb,
-                                         int nbytes, int k0, int j, uint32_t rs_bytes, int wave,
-                                         int lane) {
+__device__ __forceinline__ void dma_load(bf16* __restrict__ kv, const u32x4& krs,
+                                         const u32x4& vrs, int k0, int j, uint32_t rs_bytes,
+                                         int wave, int lane) {
   if ((j & 1) == 0)
-    dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(lds_addr(kv), buffer_rsrc(kb, nbytes), k0, j >> 1,
-                                                 rs_bytes, wave, lane);
+    dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(lds_addr(kv), krs, k0, j >> 1, rs_bytes, wave,
+                                                 lane);
   else
-    dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(lds_addr(kv + C::kTile), buffer_rsrc(vb, nbytes),
-                                                 k0, j >> 1, rs_bytes, wave, lane);
+    dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(lds_addr(kv + C::kTile), vrs, k0, j >> 1,
+                                                 rs_bytes, wave, lane);
 }
 
-template <class C>
-__device__ __forceinline__ void issue16(bf16* __restrict__ kv, const bf16* kb, const bf16* vb,
-                                        int nbytes, int k0, uint32_t rs_bytes, int wave,
-                                        int lane) {
+template <class C, class KT>
+__device__ __forceinline__ void issue16(bf16* __restrict__ kv, const KT& src, int kt,
+                                        bool live, int wave, int lane) {
+  u32x4 krs, vrs;
+  int k0;
+  src.get(kt, live, wave, krs, vrs, k0);
 #pragma unroll
   for (int j = 0; j < 2 * C::kLoads; ++j)
-    dma_load<C>(kv, kb, vb, nbytes, k0, j, rs_bytes, wave, lane);
+    dma_load<C>(kv, krs, vrs, k0, j, src.rs_bytes, wave, lane);
 }
 
 // One pipelined tile step: S^T(t+1) = K Q^T on the K tile `ks` and
@@ -118,7 +121,7 @@ __device__ __forceinline__ void issue16(bf16* __restrict__ kv, const bf16* kb, c
 template <class C, bool PV, bool FIRST, bool DMA>
 __device__ __forceinline__ void mfma_phase(const bf16* __restrict__ ks,
                                            const bf16* __restrict__ vs, bf16* __restrict__ pre,
-                                           const bf16* kseq, const bf16* vseq, int nbytes, int nk0,
+                                           const u32x4& krs, const u32x4& vrs, int nk0,
                                            uint32_t rs_bytes, int wave,
                                            int lane, uint32_t krow, uint32_t kq16, uint32_t vrow,
                                            uint32_t vc16, const bf16x8 (*q)[C::kSt],
@@ -163,7 +166,7 @@ __device__ __forceinline__ void mfma_phase(const bf16* __restrict__ ks,
     if constexpr (DMA) {
       constexpr int kEvery = kN / (2 * C::kLoads);
       if (i % kEvery == 0)
-        dma_load<C>(pre, kseq, vseq, nbytes, nk0, i / kEvery, rs_bytes, wave, lane);
+        dma_load<C>(pre, krs, vrs, nk0, i / kEvery, rs_bytes, wave, lane);
     }
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) s[rb][kb] = mfma16(a, q[rb][st], s[rb][kb]);
@@ -198,7 +201,7 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ v, bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                     const int32_t* __restrict__ spans, int num_spans, int hq, int hkv,
-                    int window, float c2, int tiles, int nseq) {
+                    int window, float c2, int tiles, int nseq, PagedKv pk) {
   constexpr int D = C::D, G = C::G, RB = C::RB, BN = C::BN, NST = C::NST;
   // Stage ring: NST buffers of (K tile, V tile); tile kt lives in buffer
   // (kt - kt0) % NST.  While step kt runs, tiles kt-1 (V read), kt, kt+1 (K
@@ -209,14 +212,16 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // the end of the sequence (longest causal rows first).
   const long long item = xcd_logical_block(blockIdx.x);
   if (item >= (long long)tiles * hkv * nseq) return;
-  const int t = tiles - 1 - (int)(item % tiles);
   const int g = (int)((item / tiles) % hkv);
   const int b = (int)(item / ((long long)tiles * hkv));
-  const int seq0 = cu_seqlens[b];
-  const int L = cu_seqlens[b + 1] - seq0;
+  constexpr bool PAGED = C::kPaged;
+  const SeqGeo sg = seq_geo<PAGED>(cu_seqlens, pk, b);
+  const int L = sg.L;
+  const int t = sg.qlo / C::kPositions + tiles - 1 - (int)(item % tiles);
   const int p0 = t * C::kPositions;
-  if (p0 >= L) return;
-  const int p1 = min(p0 + C::kPositions, L);
+  if (p0 >= sg.qhi) return;
+  const int p1 = min(p0 + C::kPositions, sg.qhi);
+  const int seq0 = sg.qbase;  // packed row of position 0 (q / o / lse, spans)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -234,8 +239,8 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Positions of this wave's rows (a tile needs masks unless it is fully
   // allowed for every one of them).
   const int pw0 = p0 + wave * C::kPosPerWave;
-  const int pw1 = min(pw0 + C::kPosPerWave, L);
-  const bool wave_full = pw0 + C::kPosPerWave <= L;
+  const int pw1 = min(pw0 + C::kPosPerWave, sg.qhi);
+  const bool wave_full = pw0 >= sg.qlo && pw0 + C::kPosPerWave <= sg.qhi;
 
   Lane16 ln;
   ln.x = lane & 15;
@@ -256,7 +261,7 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int row = C::kRowsPerWave * wave + 16 * rb + ln.x;
     const int pos = p0 + row / G;
     qhead[rb] = g * G + row % G;
-    const bool valid = pos < L;
+    const bool valid = pos >= sg.qlo && pos < sg.qhi;
     qpos[rb] = valid ? pos : -1;  // an invalid row admits no key
     my_ss[rb] = 0;
     my_se[rb] = 0;
@@ -267,28 +272,26 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 
   // Q^T operands: lane holds q[row][32*st + 8*gq .. +7] for every st.  Rows
-  // past the sequence end load its first row instead; every key is masked
-  // for them (qpos = -1) and they are never stored.
+  // outside the sequence's query positions load its first query row instead;
+  // every key is masked for them (qpos = -1) and they are never stored.
   bf16x8 qr[RB][C::kSt];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const bf16* qrow =
-        q + ((size_t)(seq0 + max(qpos[rb], 0)) * hq + qhead[rb]) * D + 8 * ln.gq;
+        q + ((size_t)(seq0 + (qpos[rb] >= 0 ? qpos[rb] : sg.qlo)) * hq + qhead[rb]) * D +
+        8 * ln.gq;
 #pragma unroll
     for (int st = 0; st < C::kSt; ++st) qr[rb][st] = ld_global_x8(qrow + 32 * st);
   }
 
   const uint32_t rs_bytes = (uint32_t)hkv * D * 2;
-  // This KV head's rows of the sequence, loaded through buffer resources of
-  // exactly that extent (the host rejects inputs whose rows span 2 GiB or
-  // more).
-  const bf16* kb = k + ((size_t)seq0 * hkv + g) * D;
-  const bf16* vb = v + ((size_t)seq0 * hkv + g) * D;
-  const int nbytes = (int)((uint32_t)L * rs_bytes);
+  // This KV head's keys, loaded through buffer resources of exactly their
+  // extent: the sequence's rows (contiguous layout; the host rejects inputs
+  // whose rows span 2 GiB or more) or one cache block per half tile (paged).
+  static_assert(BN == 32 && C::kWaves == 4, "KvTiles: wave w loads tile rows [8w, 8w+8)");
+  const KvTiles<PAGED> src = kv_tiles<D, PAGED>(k, v, pk, sg, b, g, hkv, window);
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
   constexpr int kPerTile = 2 * C::kLoads;  // direct loads per lane per tile
-  // Extent for tile kt (zero past the last tile).
-  auto extent = [&](int kt) { return kt < kt1 ? nbytes : 0; };
 
   // Accumulators: O starts at the first PV product (zero addend).
   f32x4 oacc[RB][C::kDb];
@@ -300,9 +303,9 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 
   // Prologue: tiles kt0 .. kt0+2 in flight; wait for Q and tile kt0.
-  issue16<C>(kvs[0], kb, vb, extent(kt0), kt0 * BN, rs_bytes, wave, lane);
-  issue16<C>(kvs[1], kb, vb, extent(kt0 + 1), (kt0 + 1) * BN, rs_bytes, wave, lane);
-  issue16<C>(kvs[2], kb, vb, extent(kt0 + 2), (kt0 + 2) * BN, rs_bytes, wave, lane);
+  issue16<C>(kvs[0], src, kt0, true, wave, lane);
+  issue16<C>(kvs[1], src, kt0 + 1, kt0 + 1 < kt1, wave, lane);
+  issue16<C>(kvs[2], src, kt0 + 2, kt0 + 2 < kt1, wave, lane);
   wait_vmcnt<2 * kPerTile>();
   lds_barrier();
 
@@ -310,7 +313,8 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // arrays each (steps are unrolled by two), so nothing is copied.
   f32x4 sa[RB][2], sb[RB][2];
   bf16x8 pa[RB], pbb[RB];
-  mfma_phase<C, false, false, false>(kvs[0], kvs[0], kvs[1], kb, vb, 0, 0, rs_bytes, wave, lane,
+  const u32x4 no_rs{};
+  mfma_phase<C, false, false, false>(kvs[0], kvs[0], kvs[1], no_rs, no_rs, 0, rs_bytes, wave, lane,
                                      ln.krow, ln.kq16, ln.vrow, ln.vc16, qr, sa, pa, oacc);
 
   // Step kt: wait for tile kt+1, then S(kt+1) and PV(kt-1) on the MFMAs,
@@ -334,7 +338,9 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // step issues one tile's loads, real or zero-length).
     wait_vmcnt<kPerTile>();
     lds_barrier();
-    const int next_bytes = extent(kt + 3);
+    u32x4 nkrs, nvrs;
+    int nk0;
+    src.get(kt + 3, kt + 3 < kt1, wave, nkrs, nvrs, nk0);
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
     const uint32_t kq16 = opaque(ln.kq16), vc16 = opaque(ln.vc16);
@@ -353,17 +359,13 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     };
     if (need_mask) {
       const bool moved = softmax_fast<RB, true>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
-      mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, kb, vb, next_bytes, (kt + 3) * BN, rs_bytes,
-                                     wave,
-                                     lane, ln.krow, kq16,
-                                     ln.vrow, vc16, qr, sn, pp, oacc);
+      mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, nkrs, nvrs, nk0, rs_bytes, wave, lane,
+                                     ln.krow, kq16, ln.vrow, vc16, qr, sn, pp, oacc);
       if (moved) rescale(softmax_move<RB, true>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, alpha));
     } else {
       const bool moved = softmax_fast<RB, false>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc);
-      mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, kb, vb, next_bytes, (kt + 3) * BN, rs_bytes,
-                                     wave,
-                                     lane, ln.krow, kq16,
-                                     ln.vrow, vc16, qr, sn, pp, oacc);
+      mfma_phase<C, PV, FIRST, true>(kbuf, vbuf, pre, nkrs, nvrs, nk0, rs_bytes, wave, lane,
+                                     ln.krow, kq16, ln.vrow, vc16, qr, sn, pp, oacc);
       if (moved) rescale(softmax_move<RB, false>(sc, k0, ln, qpos, my_ss, my_se, m, l, pc, alpha));
     }
   };
@@ -406,13 +408,20 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <class C>
 static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-  const int tiles = (a.max_seqlen + C::kPositions - 1) / C::kPositions;
+  const int tiles = prefill_grid_tiles(a, C::kPositions);
   const long long blocks = xcd_padded_blocks((long long)tiles * a.hkv * a.batch);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel<C>, dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
-                     a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2, tiles,
-                     a.batch);
+  const PagedKv pk{a.q_start, a.block_table, a.max_blocks, a.num_blocks, a.max_context};
+  if (a.q_start != nullptr)
+    hipLaunchKernelGGL(prefill_kernel<PagedOf<C>>, dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
+                       a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2, tiles,
+                       a.batch, pk);
+  else
+    hipLaunchKernelGGL(prefill_kernel<C>, dim3((unsigned)blocks), dim3(C::kThreads), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
+                       a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2, tiles,
+                       a.batch, pk);
   return hipGetLastError();
 }
 

@@ -92,6 +92,139 @@ __device__ __forceinline__ void dma_rows(uint32_t tile, const u32x4& rs, int k0,
       : "memory");
 }
 
+// ---------------------------------------------------------------------------
+// Where a sequence's query rows and keys are.
+//
+// Contiguous layout (attn_prefill_varlen): positions [0, L) are the packed
+// rows [cu[b], cu[b+1]) of q / o, and keys [0, L) the K/V rows of the same
+// packed indices.  Paged layout (attn_prefill_paged): positions
+// [q_start[b], q_start[b] + n) are the packed rows [cu[b], cu[b+1]) of q / o
+// (n = cu[b+1] - cu[b]), and keys [0, q_start[b] + n) are read from the paged
+// cache through the sequence's block-table row.  Position tiles stay aligned
+// to position 0 in both layouts, so a row lands in the same wave, lane and
+// MFMA slot and visits the same key tiles either way: its bytes are the same.
+
+struct PagedKv {
+  const int32_t* q_start;      // [batch]; nullptr: contiguous layout
+  const int32_t* block_table;  // [batch, max_blocks]
+  int max_blocks;
+  int num_blocks;
+  int max_context;             // bound on q_start[b] + n (at most 16 * max_blocks)
+};
+
+// Kernel configuration C with keys read from the paged cache (C::kPaged is
+// false for the contiguous layout): a separate kernel instance, so the
+// contiguous kernels carry no paged addressing.
+template <class C>
+struct PagedOf : C {
+  static constexpr bool kPaged = true;
+};
+
+struct SeqGeo {
+  int qlo, qhi;      // query positions [qlo, qhi)
+  int L;             // keys [0, L)
+  int qbase;         // packed row of position p: qbase + p
+};
+
+template <bool PAGED>
+__device__ __forceinline__ SeqGeo seq_geo(const int32_t* cu, const PagedKv& pk, int b) {
+  SeqGeo s;
+  const int r0 = cu[b], n = cu[b + 1] - r0;
+  s.qlo = PAGED ? pk.q_start[b] : 0;
+  // A paged sequence outside the contract (negative start, or ending past
+  // max_context) has no rows: nothing is read or written for it.
+  if (PAGED && (s.qlo < 0 || (long long)s.qlo + n > pk.max_context)) {
+    s.qlo = 0;
+    s.qhi = 0;
+  } else {
+    s.qhi = s.qlo + n;
+  }
+  s.L = s.qhi;
+  s.qbase = r0 - s.qlo;
+  return s;
+}
+
+// Sources of the direct loads of one 32-key tile.  With four waves, wave w
+// loads tile rows [8w, 8w+8), which in the paged layout (16-key cache blocks)
+// lie in block 2*kt + w/2.  `live` = false gives empty resources (the loads
+// write zeros).  k0 is the row offset dma_rows adds to the tile row.
+//
+// Paged layout: only cache blocks holding keys in [klo, L) are read (klo =
+// the first key the sequence's first query row may attend); the other rows of
+// a tile land as zeros and are masked for every row that meets them.  Table
+// reads stay inside the sequence's row, and an entry outside [0, num_blocks)
+// is clamped into it, so a bad table cannot make the loads leave the cache.
+template <bool PAGED>
+struct KvTiles {
+  const bf16* kbase;   // contiguous: this KV head's row 0 of the sequence; paged: cache + g*D
+  const bf16* vbase;
+  const int32_t* bt;   // paged: the sequence's block-table row
+  int num_blocks;
+  int max_blocks;
+  int klo;
+  size_t block_elems;  // paged: elements of one cache block (16 * Hkv * D)
+  int L;
+  uint32_t rs_bytes;   // bytes between consecutive keys of one KV head
+
+  __device__ __forceinline__ void get(int kt, bool live, int wave, u32x4& krs, u32x4& vrs,
+                                      int& k0) const {
+    if constexpr (!PAGED) {
+      const int nb = live ? (int)((uint32_t)L * rs_bytes) : 0;
+      krs = buffer_rsrc(kbase, nb);
+      vrs = buffer_rsrc(vbase, nb);
+      k0 = kt * 32;
+    } else {
+      // Branch-free: the table entry is always read (its index clamped into
+      // the row), then dropped through rows = 0 when the block is not needed.
+      const int j = 2 * kt + (wave >> 1);
+      const int left = L - 16 * j;
+      int rows = left < 16 ? left : 16;
+      const bool need = live && left > 0 && j < max_blocks && 16 * j + 16 > klo;
+      rows = need ? rows : 0;
+      // The table is read through the constant address space: a scalar load
+      // (the index is wave-uniform), waited on with the LDS counter.  A
+      // vector load here would make the compiler wait for every load in
+      // flight, the tile loads it cannot see included.
+      using ConstI32 = const __attribute__((address_space(4))) int32_t;
+      const int jc = j < max_blocks ? j : max_blocks - 1;
+      int id = ((ConstI32*)bt)[jc];
+      id = id < 0 ? 0 : id;
+      id = id < num_blocks ? id : num_blocks - 1;
+      const size_t off = (size_t)(uint32_t)id * block_elems;
+      const int nb = (int)((uint32_t)rows * rs_bytes);
+      krs = buffer_rsrc(kbase + off, nb);
+      vrs = buffer_rsrc(vbase + off, nb);
+      k0 = -16 * (wave >> 1);
+    }
+  }
+};
+
+// Key sources of KV head g of sequence b (head dim D, hkv KV heads).
+template <int D, bool PAGED>
+__device__ __forceinline__ KvTiles<PAGED> kv_tiles(const bf16* k, const bf16* v,
+                                                   const PagedKv& pk, const SeqGeo& sg, int b,
+                                                   int g, int hkv, int window) {
+  KvTiles<PAGED> src;
+  src.L = sg.L;
+  src.rs_bytes = (uint32_t)hkv * D * 2;
+  if constexpr (!PAGED) {
+    src.kbase = k + ((size_t)sg.qbase * hkv + g) * D;
+    src.vbase = v + ((size_t)sg.qbase * hkv + g) * D;
+    src.bt = nullptr;
+    src.num_blocks = src.max_blocks = src.klo = 0;
+    src.block_elems = 0;
+  } else {
+    src.kbase = k + (size_t)g * D;
+    src.vbase = v + (size_t)g * D;
+    src.bt = pk.block_table + (size_t)b * pk.max_blocks;
+    src.num_blocks = pk.num_blocks;
+    src.max_blocks = pk.max_blocks;
+    src.klo = window > 0 ? max(0, sg.qlo - window + 1) : 0;
+    src.block_elems = (size_t)16 * hkv * D;
+  }
+  return src;
+}
+
 // Scores of row block rb as 8 slot values, masked when MASK.  Key j is
 // allowed for a row at position qp when 0 <= qp - j < wlim (causal, window)
 // or j lies in the row's span [ss, se); both tests are one unsigned compare

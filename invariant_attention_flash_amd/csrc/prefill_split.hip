@@ -57,6 +57,7 @@ namespace invattn {
 
 template <int D_, int G_>
 struct PfSplitCfg {
+  static constexpr bool kPaged = false;  // contiguous keys (PagedOf<> sets it)
   static constexpr int D = D_, G = G_;
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 64 * kWaves;
@@ -203,7 +204,7 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
                           const bf16* __restrict__ v, bf16* __restrict__ o,
                           float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                           const int32_t* __restrict__ spans, int num_spans, int hq, int hkv,
-                          int window, float c2, int tiles, int nseq) {
+                          int window, float c2, int tiles, int nseq, PagedKv pk) {
   constexpr int D = C::D, G = C::G, RB = C::RB, BN = C::BN, NR = C::kRing;
   constexpr int kRB = C::kRowBlocks;
   // K ring and V ring (tile kt lives in buffer (kt - kt0) % NR of each);
@@ -218,17 +219,21 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   static_assert(C::kWaves == 4, "one flag word per wave, read as one 16-byte word");
 
   // Logical item = (tile, KV head, sequence), tile fastest; tiles run from
-  // the end of the sequence (longest causal rows first).
+  // the end of the sequence (longest causal rows first).  Tile t covers
+  // positions [t*P, (t+1)*P), counted from the first tile holding a query
+  // row of the sequence.
   const long long item = xcd_logical_block(blockIdx.x);
   if (item >= (long long)tiles * hkv * nseq) return;
-  const int t = tiles - 1 - (int)(item % tiles);
   const int g = (int)((item / tiles) % hkv);
   const int b = (int)(item / ((long long)tiles * hkv));
-  const int seq0 = cu_seqlens[b];
-  const int L = cu_seqlens[b + 1] - seq0;
+  constexpr bool PAGED = C::kPaged;
+  const SeqGeo sg = seq_geo<PAGED>(cu_seqlens, pk, b);
+  const int L = sg.L;
+  const int t = sg.qlo / C::kPositions + tiles - 1 - (int)(item % tiles);
   const int p0 = t * C::kPositions;
-  if (p0 >= L) return;
-  const int p1 = min(p0 + C::kPositions, L);
+  if (p0 >= sg.qhi) return;
+  const int p1 = min(p0 + C::kPositions, sg.qhi);
+  const int seq0 = sg.qbase;  // packed row of position 0 (q / o / lse, spans)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -246,8 +251,8 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   // Positions of this wave's score rows (a tile needs masks unless it is
   // fully allowed for every one of them).
   const int pw0 = p0 + wave * C::kPosPerWave;
-  const int pw1 = min(pw0 + C::kPosPerWave, L);
-  const bool wave_full = pw0 + C::kPosPerWave <= L;
+  const int pw1 = min(pw0 + C::kPosPerWave, sg.qhi);
+  const bool wave_full = pw0 >= sg.qlo && pw0 + C::kPosPerWave <= sg.qhi;
 
   Lane16 ln;
   ln.x = lane & 15;
@@ -270,7 +275,7 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     const int row = C::kRowsPerWave * wave + 16 * rb + ln.x;
     const int pos = p0 + row / G;
     qhead[rb] = g * G + row % G;
-    const bool valid = pos < L;
+    const bool valid = pos >= sg.qlo && pos < sg.qhi;
     qpos[rb] = valid ? pos : -1;  // an invalid row admits no key
     my_ss[rb] = 0;
     my_se[rb] = 0;
@@ -281,13 +286,13 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   }
 
   // Q^T operands: lane holds q[row][32*st + 8*gq .. +7] for every st.  Rows
-  // past the sequence end load its first row instead; every key is masked
-  // for them (qpos = -1) and they are never stored.
+  // outside the sequence's query rows load its first query row instead;
+  // every key is masked for them (qpos = -1) and they are never stored.
   bf16x8 qr[RB][C::kSt];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const bf16* qrow =
-        q + ((size_t)(seq0 + max(qpos[rb], 0)) * hq + qhead[rb]) * D + 8 * ln.gq;
+        q + ((size_t)(seq0 + (qpos[rb] >= 0 ? qpos[rb] : sg.qlo)) * hq + qhead[rb]) * D + 8 * ln.gq;
 #pragma unroll
     for (int st = 0; st < C::kSt; ++st) qr[rb][st] = ld_global_x8(qrow + 32 * st);
   }
@@ -295,28 +300,29 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   const uint32_t rs_bytes = (uint32_t)hkv * D * 2;
   // This KV head's rows of the sequence, loaded through buffer resources of
   // exactly that extent (the host rejects inputs whose rows span 2 GiB or
-  // more).
-  const bf16* kseq = k + ((size_t)seq0 * hkv + g) * D;
-  const bf16* vseq = v + ((size_t)seq0 * hkv + g) * D;
-  const int nbytes = (int)((uint32_t)L * rs_bytes);
+  // more), or its cache blocks.
+  const KvTiles<PAGED> src = kv_tiles<D, PAGED>(k, v, pk, sg, b, g, hkv, window);
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
   constexpr int kPerStep = 2 * C::kLoads;  // direct loads per lane per step
-  auto extent = [&](int kt) { return kt < kt1 ? nbytes : 0; };
   // LDS addresses of the rings (tile kt in buffer (kt - kt0) % NR).
   constexpr uint32_t kTileBytes = C::kTile * 2;
   const uint32_t ks_lds = lds_addr(ks[0]), vs_lds = lds_addr(vs[0]);
   auto load_k = [&](int slot, int kt) {
-    const u32x4 rsc = buffer_rsrc(kseq, extent(kt));
+    u32x4 krsc, vrsc;
+    int k0r;
+    src.get(kt, kt < kt1, wave, krsc, vrsc, k0r);
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i)
-      dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(ks_lds + slot * kTileBytes, rsc, kt * BN, i,
+      dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(ks_lds + slot * kTileBytes, krsc, k0r, i,
                                                   rs_bytes, wave, lane);
   };
   auto load_v = [&](int slot, int kt) {
-    const u32x4 rsc = buffer_rsrc(vseq, extent(kt));
+    u32x4 krsc, vrsc;
+    int k0r;
+    src.get(kt, kt < kt1, wave, krsc, vrsc, k0r);
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i)
-      dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vs_lds + slot * kTileBytes, rsc, kt * BN, i,
+      dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vs_lds + slot * kTileBytes, vrsc, k0r, i,
                                                   rs_bytes, wave, lane);
   };
 
@@ -359,7 +365,7 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   // unrolled by two), so nothing is copied.
   f32x4 sa[RB][2], sb[RB][2];
   {
-    const u32x4 none = buffer_rsrc(kseq, 0);
+    const u32x4 none = buffer_rsrc(k, 0);
     split_phase<C, false, false, false>(ks[0], vs[0], pl[0], 0, 0, none, none, 0, 0, rs_bytes,
                                         wave, lane, ln.krow, ln.kq16, ln.vrow, vc16w, qr, sa,
                                         oacc, [](int) {});
@@ -390,7 +396,10 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
     const uint32_t kq16 = opaque(ln.kq16), vcw = opaque(vc16w);
-    const u32x4 krs = buffer_rsrc(kseq, extent(kt + 3)), vrs = buffer_rsrc(vseq, extent(kt + 1));
+    u32x4 krs, vrs, unused;
+    int kk0, vk0;
+    src.get(kt + 3, kt + 3 < kt1, wave, krs, unused, kk0);
+    src.get(kt + 1, kt + 1 < kt1, wave, unused, vrs, vk0);
     float alpha[RB];
     uint32_t smask = 0;
     bf16x8 pc[RB];
@@ -398,8 +407,8 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
       constexpr bool MASK = decltype(mask_tag)::value;
       TileSoftmax<RB, MASK> ts;
       ts.init(k0, ln, qpos, my_ss, my_se);
-      split_phase<C, PV, FIRST, true>(kcur, vcur, pcur, kpre, vpre, krs, vrs, (kt + 3) * BN,
-                                      (kt + 1) * BN, rs_bytes, wave, lane, ln.krow, kq16,
+      split_phase<C, PV, FIRST, true>(kcur, vcur, pcur, kpre, vpre, krs, vrs, kk0, vk0,
+                                      rs_bytes, wave, lane, ln.krow, kq16,
                                       ln.vrow, vcw, qr, sn, oacc,
                                       [&](int i) { ts.stage(i, sc, ln, rs); });
       if (ts.finish(rs)) smask = ts.move(sc, k0, ln, qpos, my_ss, my_se, rs, alpha);
@@ -460,7 +469,7 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   for (int r = 0; r < kRB; ++r) {
     const int row = 16 * r + ln.x;
     const int pos = p0 + row / G;
-    if (pos >= L) continue;
+    if (pos < sg.qlo || pos >= sg.qhi) continue;
     const float lr = lrow[row];
     bf16* orow = o + ((size_t)(seq0 + pos) * hq + g * G + row % G) * D + 16 * C::kDbW * wave +
                  4 * ln.gq;
@@ -483,13 +492,20 @@ void prefill_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
 
 template <class C>
 static hipError_t launch_split(const PrefillArgs& a, hipStream_t stream) {
-  const int tiles = (a.max_seqlen + C::kPositions - 1) / C::kPositions;
+  const int tiles = prefill_grid_tiles(a, C::kPositions);
   const long long blocks = xcd_padded_blocks((long long)tiles * a.hkv * a.batch);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_split_kernel<C>, dim3((unsigned)blocks), dim3(C::kThreads), 0,
-                     stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o,
-                     a.lse, a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2,
-                     tiles, a.batch);
+  const PagedKv pk{a.q_start, a.block_table, a.max_blocks, a.num_blocks, a.max_context};
+  if (a.q_start != nullptr)
+    hipLaunchKernelGGL(prefill_split_kernel<PagedOf<C>>, dim3((unsigned)blocks), dim3(C::kThreads), 0,
+                       stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o,
+                       a.lse, a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2,
+                       tiles, a.batch, pk);
+  else
+    hipLaunchKernelGGL(prefill_split_kernel<C>, dim3((unsigned)blocks), dim3(C::kThreads), 0,
+                       stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o,
+                       a.lse, a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2,
+                       tiles, a.batch, pk);
   return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ namespace invattn {
 
 template <int D_, int G_, int BN_, int DSPLIT_, int RBW_, int WAVES_, int NST_, int OCC_>
 struct PrefillCfg {
+  static constexpr bool kPaged = false;  // contiguous keys (PagedOf<> sets it)
   static constexpr int D = D_, G = G_, BN = BN_, DSPLIT = DSPLIT_, RBW = RBW_, OCC = OCC_;
   static constexpr int kWaves = WAVES_;
   static constexpr int kStages = NST_;                 // K/V tile buffers in flight
@@ -94,9 +95,13 @@ struct PrefillCfg {
 // the stage buffer `kv` (K tile, then V tile), through buffer resources that
 // span exactly the sequence's rows of this KV head: keys past the sequence
 // end land as zeros (and are masked).
-template <class C>
-__device__ __forceinline__ void issue_tile(bf16* kv, int k0, uint32_t rs_bytes, const u32x4& krs,
-                                           const u32x4& vrs, int wave, int lane) {
+template <class C, class KT>
+__device__ __forceinline__ void issue_tile(bf16* kv, int kt, const KT& src, int wave,
+                                           int lane) {
+  u32x4 krs, vrs;
+  int k0;
+  src.get(kt, true, wave, krs, vrs, k0);
+  const uint32_t rs_bytes = src.rs_bytes;
   const uint32_t kl = lds_addr(kv), vl = lds_addr(kv + C::kTile);
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
@@ -259,7 +264,7 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ v, bf16* __restrict__ o,
                     float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
                     const int32_t* __restrict__ spans, int num_spans, int hq, int hkv,
-                    int window, float c2) {
+                    int window, float c2, PagedKv pk) {
   constexpr int D = C::D, G = C::G, BN = C::BN, DW = C::DW, RBW = C::RBW;
   // One LDS object per pipeline stage (K tile then V tile), so the compiler
   // can tell that direct loads into one stage never alias reads of another.
@@ -268,13 +273,17 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(1024))) bf16 kv2[C::kStages > 2 ? 2 * C::kTile : 8];
   __shared__ __attribute__((aligned(16))) float xchg[C::kXchgFloats > 0 ? C::kXchgFloats : 4];
 
+  // Tile t covers positions [t*P, (t+1)*P), counted from the first tile
+  // holding a query row of the sequence; longest causal tiles first.
   const int b = blockIdx.z, g = blockIdx.y;
-  const int t = gridDim.x - 1 - blockIdx.x;  // longest causal tiles first
-  const int seq0 = cu_seqlens[b];
-  const int L = cu_seqlens[b + 1] - seq0;
+  constexpr bool PAGED = C::kPaged;
+  const SeqGeo sg = seq_geo<PAGED>(cu_seqlens, pk, b);
+  const int L = sg.L;
+  const int seq0 = sg.qbase;  // packed row of position 0 (q / o / lse, spans)
+  const int t = sg.qlo / C::kPositions + (int)(gridDim.x - 1 - blockIdx.x);
   const int p0 = t * C::kPositions;
-  if (p0 >= L) return;
-  const int p1 = min(p0 + C::kPositions, L);
+  if (p0 >= sg.qhi) return;
+  const int p1 = min(p0 + C::kPositions, sg.qhi);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -295,8 +304,8 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Positions of this wave's rows (masks are needed on tiles that are not
   // fully allowed for every one of them).
   const int pw0 = p0 + wg * C::kPosPerWave;
-  const int pw1 = min(pw0 + C::kPosPerWave, L);
-  const bool wave_full = pw0 + C::kPosPerWave <= L;
+  const int pw1 = min(pw0 + C::kPosPerWave, sg.qhi);
+  const bool wave_full = pw0 >= sg.qlo && pw0 + C::kPosPerWave <= sg.qhi;
 
   Lane<C> ln;
   ln.lane = lane;
@@ -321,7 +330,7 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int row = 32 * (wg * RBW + r) + n;
     qpos[r] = p0 + row / G;
     qhead[r] = g * G + row % G;
-    const bool valid = qpos[r] < L;
+    const bool valid = qpos[r] >= sg.qlo && qpos[r] < sg.qhi;
     ln.qpos_m[r] = valid ? qpos[r] : -1;  // an invalid row admits no key
     ln.my_ss[r] = 0;
     ln.my_se[r] = 0;
@@ -333,14 +342,11 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // This KV head's rows of the sequence, loaded through buffer resources of
   // exactly that extent (the host rejects inputs whose rows span 2 GiB or
-  // more).
-  const uint32_t rs_bytes = (uint32_t)hkv * D * 2;
-  const int nbytes = (int)((uint32_t)L * rs_bytes);
-  const u32x4 krs = buffer_rsrc(k + ((size_t)seq0 * hkv + g) * D, nbytes);
-  const u32x4 vrs = buffer_rsrc(v + ((size_t)seq0 * hkv + g) * D, nbytes);
+  // more), or its cache blocks.
+  const KvTiles<PAGED> src = kv_tiles<D, PAGED>(k, v, pk, sg, b, g, hkv, window);
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
-  issue_tile<C>(kv0, kt0 * BN, rs_bytes, krs, vrs, wave, lane);
-  if (C::kStages > 2 && kt0 + 1 < kt1) issue_tile<C>(kv1, (kt0 + 1) * BN, rs_bytes, krs, vrs, wave, lane);
+  issue_tile<C>(kv0, kt0, src, wave, lane);
+  if (C::kStages > 2 && kt0 + 1 < kt1) issue_tile<C>(kv1, kt0 + 1, src, wave, lane);
 
   // Q^T operands: lane holds q[row][dh*DW + 16*s + 8*hh .. +7] for every s.
   bf16x8 qr[RBW][C::kSteps];
@@ -348,7 +354,7 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (int r = 0; r < RBW; ++r) {
     const bool valid = ln.qpos_m[r] >= 0;
     const bf16* qrow =
-        q + ((size_t)(seq0 + (valid ? qpos[r] : 0)) * hq + qhead[r]) * D + dh * DW + 8 * hh;
+        q + ((size_t)(seq0 + (valid ? qpos[r] : sg.qlo)) * hq + qhead[r]) * D + dh * DW + 8 * hh;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
       bf16x8 x = ld_global_x8(qrow + 16 * s);
@@ -377,7 +383,7 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     else wait_vmem();
     lds_barrier();
     if (kt + C::kStages - 1 < kt1)
-      issue_tile<C>(pre, (kt + C::kStages - 1) * BN, rs_bytes, krs, vrs, wave, lane);
+      issue_tile<C>(pre, kt + C::kStages - 1, src, wave, lane);
     const bool need_mask =
         !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
     compute_tile<C>(cur, cur + C::kTile, xchg, k0, need_mask, ln, qr, oacc, m, l);
@@ -416,11 +422,17 @@ void prefill_wide_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <class C>
 static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-  const int tiles = (a.max_seqlen + C::kPositions - 1) / C::kPositions;
+  const int tiles = prefill_grid_tiles(a, C::kPositions);
   dim3 grid(tiles, a.hkv, a.batch);
-  hipLaunchKernelGGL(prefill_wide_kernel<C>, grid, dim3(C::kThreads), 0, stream,
-                     (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
-                     a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2);
+  const PagedKv pk{a.q_start, a.block_table, a.max_blocks, a.num_blocks, a.max_context};
+  if (a.q_start != nullptr)
+    hipLaunchKernelGGL(prefill_wide_kernel<PagedOf<C>>, grid, dim3(C::kThreads), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
+                       a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2, pk);
+  else
+    hipLaunchKernelGGL(prefill_wide_kernel<C>, grid, dim3(C::kThreads), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o, a.lse,
+                       a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2, pk);
   return hipGetLastError();
 }
 

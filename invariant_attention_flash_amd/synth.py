@@ -273,6 +273,82 @@ def decode_case(seed=4, lengths=None, batch=64, hq=32, hkv=4, d=512, block_size=
 
 
 # --------------------------------------------------------------------------
+# chunked prefill over a paged KV cache
+# --------------------------------------------------------------------------
+@dataclass
+class PagedChunks:
+    """Query chunks of the sequences of a PrefillCase, their keys in a paged
+    cache.  Batch entry c is chunk (seq[c], start[c], end[c]): query positions
+    [start, end) of sequence seq[c], whose keys [0, end) are in the cache."""
+    q: np.ndarray            # [T, Hq, D] uint16, the chunks' query rows, packed
+    k_cache: np.ndarray      # [NB, 16, Hkv, D] uint16
+    v_cache: np.ndarray
+    block_table: np.ndarray  # [B, MB] int32 (the row of the chunk's sequence)
+    cu_seqlens: np.ndarray   # [B+1] int32, packed query-row ranges
+    q_start: np.ndarray      # [B] int32
+    seq: list
+    start: list
+    end: list
+    block_size: int = 16
+
+    def max_query_len(self) -> int:
+        return max((e - a for a, e in zip(self.start, self.end)), default=0)
+
+    def max_context_len(self) -> int:
+        return max(self.end, default=0)
+
+
+def chunk_bounds(seed, length, n_cuts):
+    """Sorted chunk boundaries 0 = c0 < ... < L of one sequence: ``n_cuts``
+    random interior cuts from stream [seed, 0, 21, length], plus a cut at
+    L - 1 (the last chunk is one token) when L > 1."""
+    rng = np.random.default_rng([seed, 0, 21, length])
+    cuts = set(int(x) for x in rng.integers(1, max(length, 2), size=n_cuts)) if length > 1 else set()
+    if length > 1:
+        cuts.add(length - 1)
+    return [0] + sorted(c for c in cuts if 0 < c < length) + [length]
+
+
+def paged_chunks(case, chunks, block_size=16, spare_blocks=8, placement_seed=0, poison=True,
+                 max_blocks=None):
+    """Lay every sequence of ``case`` into a paged cache (seeded physical
+    block permutation from stream [0, 11, placement_seed]) and build the batch
+    of ``chunks``, a list of (sequence index, start, end).  Unused slots,
+    spare blocks and table padding are NaN / out-of-range poison when
+    ``poison``."""
+    nseq = len(case.seqs)
+    lens = [s.length for s in case.seqs]
+    nblk = [(L + block_size - 1) // block_size for L in lens]
+    total = sum(nblk) + spare_blocks
+    mb = max(max(nblk), 1) if max_blocks is None else max_blocks
+    fill = BF16_NAN if poison else np.uint16(0)
+    kc = np.full((total, block_size, case.hkv, case.d), fill, np.uint16)
+    vc = np.full((total, block_size, case.hkv, case.d), fill, np.uint16)
+    phys = np.random.default_rng([0, 11, placement_seed]).permutation(total).astype(np.int32)
+    rows = np.full((nseq, mb), total + 7 if poison else 0, np.int32)
+    cursor = 0
+    for i, s in enumerate(case.seqs):
+        ids = phys[cursor:cursor + nblk[i]]
+        cursor += nblk[i]
+        rows[i, :nblk[i]] = ids
+        for j, blk in enumerate(ids):
+            a, b = j * block_size, min(lens[i], (j + 1) * block_size)
+            kc[blk, :b - a] = s.k[a:b]
+            vc[blk, :b - a] = s.v[a:b]
+    seq = [c[0] for c in chunks]
+    start = [int(c[1]) for c in chunks]
+    end = [int(c[2]) for c in chunks]
+    cu = np.zeros(len(chunks) + 1, np.int32)
+    cu[1:] = np.cumsum([e - a for a, e in zip(start, end)])
+    q = np.empty((int(cu[-1]), case.hq, case.d), np.uint16)
+    for c, (i, a, e) in enumerate(zip(seq, start, end)):
+        q[cu[c]:cu[c + 1]] = case.seqs[i].q[a:e]
+    bt = rows[seq] if chunks else np.zeros((0, mb), np.int32)
+    return PagedChunks(q, kc, vc, np.ascontiguousarray(bt), cu, np.array(start, np.int32), seq,
+                       start, end, block_size)
+
+
+# --------------------------------------------------------------------------
 # device-side generation for the full-size paged decode workload
 # --------------------------------------------------------------------------
 def decode_case_device(seed=4, lengths=None, batch=64, hq=32, hkv=4, d=512, block_size=16,

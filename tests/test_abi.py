@@ -137,3 +137,58 @@ def test_error_text_is_per_call():
     assert rc != 0 and "head_dim" in msg
     rc, msg = call_prefill(window=0)
     assert "window" in msg and "head_dim" not in msg
+
+
+def call_prefill_paged(**kw):
+    a = dict(q=1 << 20, kc=1 << 20, vc=1 << 20, o=1 << 20, lse=None, cu=1 << 20, qs=1 << 20,
+             bt=1 << 20, mb=8, batch=2, mql=32, mcl=128, nb=100, bs=16, hq=32, hkv=16, d=256,
+             window=128, scale=0.0625)
+    a.update(kw)
+    ptr = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = ia.library().attn_prefill_paged(
+        ptr(a["q"]), ptr(a["kc"]), ptr(a["vc"]), ptr(a["o"]), ptr(a["lse"]), ptr(a["cu"]),
+        ptr(a["qs"]), ptr(a["bt"]), a["mb"], a["batch"], a["mql"], a["mcl"], a["nb"], a["bs"],
+        a["hq"], a["hkv"], a["d"], a["window"], a["scale"], None)
+    return rc, ia.last_error()
+
+
+PAGED_PREFILL_ERRORS = [
+    (dict(q=None), "ATTN_E_NULL", "q is NULL"),
+    (dict(kc=None), "ATTN_E_NULL", "k_cache"),
+    (dict(vc=None), "ATTN_E_NULL", "v_cache"),
+    (dict(o=None), "ATTN_E_NULL", "o is NULL"),
+    (dict(cu=None), "ATTN_E_NULL", "cu_seqlens"),
+    (dict(qs=None), "ATTN_E_NULL", "q_start"),
+    (dict(bt=None), "ATTN_E_NULL", "block_table"),
+    (dict(batch=-1), "ATTN_E_SHAPE", "batch"),
+    (dict(mql=-1), "ATTN_E_SHAPE", "max_query_len"),
+    (dict(mcl=16), "ATTN_E_SHAPE", "max_context_len"),
+    (dict(mb=7), "ATTN_E_SHAPE", "max_blocks_per_seq"),
+    (dict(mb=0), "ATTN_E_SHAPE", "max_blocks_per_seq"),
+    (dict(nb=0), "ATTN_E_SHAPE", "num_blocks"),
+    (dict(bs=32), "ATTN_E_UNSUPPORTED", "block_size"),
+    (dict(d=128), "ATTN_E_UNSUPPORTED", "head_dim"),
+    (dict(hq=64, hkv=4), "ATTN_E_UNSUPPORTED", "group"),
+    (dict(window=0), "ATTN_E_UNSUPPORTED", "window"),
+    (dict(scale=-1.0), "ATTN_E_UNSUPPORTED", "softmax_scale"),
+    (dict(kc=(1 << 20) + 2), "ATTN_E_ALIGN", "k_cache"),
+    (dict(qs=(1 << 20) + 2), "ATTN_E_ALIGN", "q_start"),
+    (dict(bt=(1 << 20) + 1), "ATTN_E_ALIGN", "block_table"),
+]
+
+
+@pytest.mark.parametrize("kw,code,text", PAGED_PREFILL_ERRORS,
+                         ids=[c[2] + str(i) for i, c in enumerate(PAGED_PREFILL_ERRORS)])
+def test_prefill_paged_rejects(kw, code, text):
+    rc, msg = call_prefill_paged(**kw)
+    assert ia.ERROR_CODES[rc] == code, (rc, msg)
+    assert text in msg
+
+
+def test_prefill_paged_empty_input_needs_no_pointers():
+    rc, msg = call_prefill_paged(q=None, kc=None, vc=None, o=None, cu=None, qs=None, bt=None,
+                                 batch=0)
+    assert rc == 0, msg
+    rc, msg = call_prefill_paged(q=None, kc=None, vc=None, o=None, cu=None, qs=None, bt=None,
+                                 mql=0)
+    assert rc == 0, msg
