@@ -201,7 +201,12 @@ size_t attn_decode_workspace_size(int32_t batch, int32_t max_seq_len,
  *
  * Arguments (device pointers caller-owned):
  *   q            bf16 [batch, num_q_heads, head_dim], contiguous
- *   k_cache, v_cache  bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   k_cache, v_cache  bf16 [num_blocks, block_size, num_kv_heads, head_dim].
+ *                v_cache may be the same pointer as k_cache (V = K, the
+ *                global layers whose K and V share one projection: same
+ *                RFC, section 6, global_k_eq_v_projection); each block is
+ *                then read once, and the output bytes equal those of a
+ *                separate V cache holding the same values.
  *   block_table  int32 [batch, max_blocks_per_seq]; key j of sequence b is in
  *                block block_table[b][j / block_size], slot j % block_size.
  *                Entries for blocks outside the attended key range are never

@@ -35,8 +35,17 @@ namespace invattn {
 // Reference-max hysteresis inside a chunk (log2 units), as in prefill.
 constexpr float kDecodeRescale = 8.0f;
 
+// Two waves per SIMD: registers are capped at 256 per lane, and two
+// workgroups share a CU (two 32 KB stages each at head dim 512), so one
+// workgroup's loads land while the other computes.
+#ifndef DC_OCC
+#define DC_OCC 2
+#endif
+
 template <int D_, int G_, int NST_, int WAVES_>
 struct DecodeCfg {
+  static constexpr bool kAliasKV = false;  // V read from the K cache (KvAliasOf<> sets it)
+  static constexpr int kOcc = DC_OCC;       // waves per SIMD the registers are sized for
   static constexpr int D = D_, G = G_;
   static constexpr int kWaves = WAVES_;
   static constexpr int kThreads = 64 * kWaves;
@@ -59,9 +68,19 @@ struct DecodeCfg {
   static_assert(kDPerWave % 16 == 0, "head-dim slice per wave");
 };
 
+// Configuration C for a V cache that is the K cache (global layers whose K
+// and V share one projection): each block is loaded once, and the V operand
+// is read from the K rows in LDS.  The operand values are the same as with a
+// separate V cache holding the same bytes, so the output bytes are too.
+template <class C>
+struct KvAliasOf : C {
+  static constexpr bool kAliasKV = true;
+};
+
 // Direct loads of cache block `blk` (keys k0 .. k0+15) into stage buffer kv
-// (K rows then V rows), through buffer resources that end at the sequence's
-// last key: slots at or past the sequence end land as zeros (and are masked).
+// (K rows then V rows; K rows only when V aliases K), through buffer
+// resources that end at the sequence's last key: slots at or past the
+// sequence end land as zeros (and are masked).
 template <class C>
 __device__ __forceinline__ void issue_block(bf16* kv, const bf16* kc, const bf16* vc,
                                            size_t blk_base, int k0, int L, uint32_t slot_stride,
@@ -72,26 +91,31 @@ __device__ __forceinline__ void issue_block(bf16* kv, const bf16* kc, const bf16
   const int nbytes = (int)((uint32_t)rows * row_bytes);
   const u32x4 krs = buffer_rsrc(kc + blk_base + head_off, nbytes);
   const u32x4 vrs = buffer_rsrc(vc + blk_base + head_off, nbytes);
-  const uint32_t kl = lds_addr(kv), vl = lds_addr(kv + C::kTile);
+  const uint32_t kl = lds_addr(kv), vl = C::kAliasKV ? kl : lds_addr(kv + C::kTile);
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
     dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kl, krs, 0, i, row_bytes, wave, lane);
-    dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vl, vrs, 0, i, row_bytes, wave, lane);
+    if constexpr (!C::kAliasKV)
+      dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vl, vrs, 0, i, row_bytes, wave, lane);
   }
 }
 
 template <class C>
-__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads)))
+__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads),
+                          amdgpu_waves_per_eu(C::kOcc, C::kOcc)))
 void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc,
                          const bf16* __restrict__ vc, const int32_t* __restrict__ bt,
                          int max_blocks, const int32_t* __restrict__ seq_lens, int max_seq_len,
                          int num_blocks, int hq, int hkv, int window, float c2,
                          float* __restrict__ ws, int n_chunks) {
   constexpr int D = C::D, G = C::G;
-  __shared__ __attribute__((aligned(1024))) bf16 kv0[2 * C::kTile];
-  __shared__ __attribute__((aligned(1024))) bf16 kv1[2 * C::kTile];
-  __shared__ __attribute__((aligned(1024))) bf16 kv2[C::kStages > 2 ? 2 * C::kTile : 8];
-  __shared__ __attribute__((aligned(1024))) bf16 kv3[C::kStages > 3 ? 2 * C::kTile : 8];
+  // Stage buffers: K rows then V rows, or K rows only when V aliases K (the
+  // smaller footprint lets more workgroups share a CU).
+  constexpr int kStage = C::kAliasKV ? C::kTile : 2 * C::kTile;
+  __shared__ __attribute__((aligned(1024))) bf16 kv0[kStage];
+  __shared__ __attribute__((aligned(1024))) bf16 kv1[kStage];
+  __shared__ __attribute__((aligned(1024))) bf16 kv2[C::kStages > 2 ? kStage : 8];
+  __shared__ __attribute__((aligned(1024))) bf16 kv3[C::kStages > 3 ? kStage : 8];
 
   // Grid (KV head, chunk, sequence): the KV heads of one chunk are
   // neighbours in dispatch order, so the rows they read from each cache block
@@ -152,10 +176,12 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
   const int lg = lane & 15;
   const int vrow = 4 * grp + (lg >> 2);
   const int vc1 = wave * C::kDPerWave / 8 + ((lg & 3) >> 1);
-  const int vsw = (vrow << 1) & C::kSwV;
+  // V rows carry the V swizzle, or the K swizzle when they are the K rows.
+  const int vsw = C::kAliasKV ? (vrow & C::kSwK) : ((vrow << 1) & C::kSwV);
+  constexpr int kPerStage = C::kAliasKV ? C::kLoads : 2 * C::kLoads;  // loads per stage
 
   auto step = [&] __device__(const bf16* cur, bf16* pre, int kb) {
-    if (kb + C::kStages - 2 < kb1) wait_vmem_keep<C::kStages - 2>(2 * C::kLoads);
+    if (kb + C::kStages - 2 < kb1) wait_vmem_keep<C::kStages - 2>(kPerStage);
     else wait_vmem();
     lds_barrier();
     const int nb = kb + C::kStages - 1;
@@ -163,7 +189,7 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
       issue_block<C>(pre, kc, vc, block_base(nb), nb * C::kKeys, L, slot_stride, head_off, wave,
                      lane);
     const bf16* ks = cur;
-    const bf16* vs = cur + C::kTile;
+    const bf16* vs = C::kAliasKV ? cur : cur + C::kTile;
     const int k0 = kb * C::kKeys;
     // S^T for keys k0 + [0, 16): lane holds head col, keys 4*grp + i.
     f32x4 sacc = f32x4{};
@@ -284,10 +310,16 @@ void decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict
 template <class C>
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.hkv, a.n_chunks, a.batch);
-  hipLaunchKernelGGL(decode_chunk_kernel<C>, grid, dim3(C::kThreads), 0, stream,
-                     (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
-                     a.block_table, a.max_blocks, a.seq_lens, a.max_seq_len, a.num_blocks, a.hq,
-                     a.hkv, a.window, a.c2, a.workspace, a.n_chunks);
+  if (a.k_cache == a.v_cache)
+    hipLaunchKernelGGL(decode_chunk_kernel<KvAliasOf<C>>, grid, dim3(C::kThreads), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
+                       a.block_table, a.max_blocks, a.seq_lens, a.max_seq_len, a.num_blocks,
+                       a.hq, a.hkv, a.window, a.c2, a.workspace, a.n_chunks);
+  else
+    hipLaunchKernelGGL(decode_chunk_kernel<C>, grid, dim3(C::kThreads), 0, stream,
+                       (const bf16*)a.q, (const bf16*)a.k_cache, (const bf16*)a.v_cache,
+                       a.block_table, a.max_blocks, a.seq_lens, a.max_seq_len, a.num_blocks,
+                       a.hq, a.hkv, a.window, a.c2, a.workspace, a.n_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel<C::D>, dim3(a.hq, a.batch), dim3(64), 0, stream,
@@ -298,7 +330,7 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
 
 // Ring depth and waves per workgroup: fixed constants.
 #ifndef DC_NST
-#define DC_NST 3
+#define DC_NST 2
 #endif
 #ifndef DC_WAVES
 #define DC_WAVES 4

@@ -209,6 +209,7 @@ __device__ __forceinline__ void wait_vmem_keep(int n) {
     // vmcnt(n) with n = loads issued per tile times the tiles allowed in
     // flight; the encodings are immediates, so pick from a small table.
     switch (n * N) {
+      case 1: __asm__ volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
       case 2: __asm__ volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
       case 4: __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
       case 8: __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;

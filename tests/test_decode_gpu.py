@@ -114,3 +114,29 @@ def test_decode_validation(monkeypatch):
         run_decode(dc, max_seq_len=50)
     assert e.value.name == "ATTN_E_VALIDATE"
     gate(f64(run_decode(dc)), oracle_decode(dc), "validated decode")
+
+
+@pytest.mark.parametrize("d,hq,hkv,window", [(512, 32, 4, synth.NO_WINDOW), (256, 16, 4, 100),
+                                             (64, 8, 2, synth.NO_WINDOW)])
+def test_decode_v_aliasing_k(d, hq, hkv, window):
+    """V = K passed as one cache (global_k_eq_v_projection, "RFC: Gemma-4-31B-it
+    train/rollout consistency", section 6): each block is read once, and the
+    bytes equal those of a separate V cache holding the same values."""
+    dc = synth.decode_case(seed=51, lengths=LENGTHS, batch=len(LENGTHS), hq=hq, hkv=hkv, d=d,
+                           window=window)
+    kc = bf16_dev(dc.k_cache)
+    args = (bf16_dev(dc.q), i32_dev(dc.block_table), i32_dev(dc.seq_lens))
+    ms = int(dc.seq_lens.max())
+
+    def run(vc):
+        o = ia.attn_decode_paged(args[0], kc, vc, args[1], args[2], ms, window=dc.window,
+                                 softmax_scale=dc.scale)
+        torch.cuda.synchronize()
+        return o
+
+    alias = bits(run(kc))
+    copy = bits(run(kc.clone()))
+    assert np.array_equal(alias, copy)
+    ref = oracle.decode(dc.q, dc.k_cache, dc.k_cache, dc.block_table, dc.seq_lens,
+                        window=dc.window, scale=dc.scale)
+    gate(synth.bf16_to_f32(alias).astype(np.float64), ref, f"alias d={d}")
