@@ -33,6 +33,14 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+# The prefill kernel the benchmark times (head dim 256, group 2): its name in
+# rocprofv3 output and the key of its HBM traffic in profiles/traffic.json.
+PREFILL_TRAFFIC_KEY = "prefill_ws_kernel<256,2>"
+PREFILL_KERNEL_MATCH = "prefill_ws_kernel<invattn::PfWsCfg<256, 2>"
+PREFILL_KERNEL_FIRST = "prefill_ws_kernel"
+PREFILL_KERNEL_LABEL = "prefill_ws_kernel (head_dim 256, group 2)"
+
+
 def kernel_sources_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "invariant_attention_flash_amd", "csrc")
@@ -117,9 +125,7 @@ def write_traffic(fetch_dir, write_dir):
         if not calib:
             raise SystemExit(f"no calibration kernel found in {d}")
         scale = CALIBRATION_BYTES / (1024.0 * float(np.median(calib)))
-        for key, match, first in (("prefill_split_kernel<256,2>",
-                                   "prefill_split_kernel<invattn::PfSplitCfg<256, 2>",
-                                   "prefill_split_kernel"),
+        for key, match, first in ((PREFILL_TRAFFIC_KEY, PREFILL_KERNEL_MATCH, PREFILL_KERNEL_FIRST),
                                   ("decode_chunk_kernel+decode_merge_kernel<512,8>", "decode_",
                                    "decode_chunk_kernel")):
             vals = [v for k, v, g in rows if match in k]
@@ -268,8 +274,8 @@ def main():
 
     pf_roof = {"bound": "mfma", "achieved": pf_tflops, "peak": PEAK_BF16_TFLOPS,
                "unit": "TFLOP/s", "frac": pf_tflops / PEAK_BF16_TFLOPS,
-               "traffic": load_traffic("prefill_split_kernel<256,2>"),
-               "kernel": "prefill_split_kernel (head_dim 256, group 2)",
+               "traffic": load_traffic(PREFILL_TRAFFIC_KEY),
+               "kernel": PREFILL_KERNEL_LABEL,
                "work_per_launch": f"{flops:.4g} FLOP = 4*256*32*{pairs} allowed pairs",
                "avg_launch_ms": pf_ms}
     dc_roof = {"bound": "hbm", "achieved": dc_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libinvattn.so")
-SOURCES = ["api.hip", "prefill.hip", "prefill_split.hip", "prefill_wide.hip", "decode.hip"]
+SOURCES = ["api.hip", "prefill.hip", "prefill_split.hip", "prefill_ws.hip", "prefill_wide.hip",
+           "decode.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

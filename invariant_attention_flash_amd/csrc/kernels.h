@@ -102,6 +102,9 @@ hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t stream);
 // columns across the waves of a workgroup.
 bool prefill_split_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill_split(const PrefillArgs& a, hipStream_t stream);
+// Head dim 256 (prefill_ws.hip): score waves and PV waves, two per SIMD.
+bool prefill_ws_schedule(int d, int group, PrefillSchedule* s);
+hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream);
 
 constexpr int kDecodeChunk = 512;  // keys per split chunk (fixed; ATTN_DECODE_CHUNK)
 constexpr int kDecodeStage = 16;   // keys per pipeline stage inside a chunk (one cache block)

@@ -441,8 +441,12 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 #ifndef PF_SPLIT256
 #define PF_SPLIT256 1
 #endif
+#ifndef PF_WS256
+#define PF_WS256 1
+#endif
 
 bool prefill_schedule(int d, int group, PrefillSchedule* s) {
+  if (PF_WS256 && prefill_ws_schedule(d, group, s)) return true;
   if (PF_SPLIT256 && prefill_split_schedule(d, group, s)) return true;
 #define X(D, G, ...)                                                          \
   if (d == D && group == G) {                                                 \
@@ -458,6 +462,7 @@ bool prefill_schedule(int d, int group, PrefillSchedule* s) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
   PrefillSchedule sp;
+  if (PF_WS256 && prefill_ws_schedule(a.d, group, &sp)) return launch_prefill_ws(a, stream);
   if (PF_SPLIT256 && prefill_split_schedule(a.d, group, &sp)) return launch_prefill_split(a, stream);
 #define X(D, G, ...) \
   if (a.d == D && group == G) return launch_one<Pf16Cfg<D, G, __VA_ARGS__>>(a, stream);

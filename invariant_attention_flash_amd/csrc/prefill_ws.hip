@@ -1,0 +1,523 @@
+// prefill_ws.hip -- batch-invariant prefill for head dim 256 with the work of
+// a workgroup specialised over two kinds of waves, two waves per SIMD.
+//
+// Sources: sliding and global attention cores are separate layer types with
+// their own head geometry and masks ("RFC: Gemma-4-31B-it train/rollout
+// consistency", section 3 "Architecture map", section 6
+// sliding_attention_core / global_attention_core); the numerical contract of
+// section 4 (fixed fp32 accumulators, an order independent of batch, packing,
+// launch geometry and occupancy, no split-KV, no fast-math, declared casts);
+// bidirectional soft-token spans (section 1, Phase B; contiguous soft-token
+// runs in "Gemma-4-E4B-it multimodal baseline").
+//
+// Why two kinds of waves.  One wave per SIMD that forms scores, runs the
+// softmax and accumulates P V issues all of it from one instruction stream:
+// the softmax's vector instructions and the LDS reads wait behind that
+// wave's own MFMAs.  Here a workgroup has eight waves, two per SIMD: four
+// score waves and four PV waves.  The SIMD interleaves the two streams, so
+// the softmax of one wave runs while the other's MFMAs do, and each wave
+// needs half the registers of a combined one (which is what lets two of them
+// share a SIMD).
+//
+// Work map (the same rows, columns, tiles and order as one wave doing both):
+// a workgroup owns `positions` consecutive positions of ONE sequence, aligned
+// to the sequence start, for the G query heads of one KV head; rows are
+// position-major (row = position*G + head), cut into 8 blocks of 16.
+//   score wave s (0..3): row blocks 2s, 2s+1; Q in registers;
+//     S^T(t+1) = K Q^T  (v_mfma_f32_16x16x32_bf16, K operand from LDS, lane l
+//                        holds keys 4*(l/16)+i of query row l%16, for 16-key
+//                        halves kb = 0, 1),
+//     softmax of tile t (fp32; the online rule of prefill_common.h) staged
+//     between its MFMAs, P(t) (bf16, RNE) to LDS with the accumulator factors
+//     of rows whose reference max moved; loads K(t+3).
+//   PV wave p (0..3): output columns [64p, 64p+64) of all 8 row blocks;
+//     O^T += V^T P^T(t-1) after scaling the blocks whose rows moved in tile
+//     t-1; P^T is the score lane's own 8 probabilities (k-slot 8*(l/16) + s
+//     meaning key 16*(s/4) + 4*(l/16) + s%4), V^T comes through the transpose
+//     read in that key order; loads V(t+1); the epilogue.
+// K and V tiles (32 keys, ascending) stream HBM -> LDS with direct loads into
+// two rings of three buffers; one LDS barrier per step orders the rings, the
+// P exchange and the flags.  Keys past the sequence end load as zeros and are
+// masked.  Every output element sees the same sequence of MFMAs and scalings
+// as in a workgroup whose waves do both jobs, so the bytes are the same.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "prefill_common.h"
+
+namespace invattn {
+
+template <int D_, int G_>
+struct PfWsCfg {
+  static constexpr bool kPaged = false;  // contiguous keys (PagedOf<> sets it)
+  static constexpr int D = D_, G = G_;
+  static constexpr int kRoleWaves = 4;                 // waves of each kind
+  static constexpr int kWaves = 2 * kRoleWaves;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BN = 32;                        // keys per KV tile
+  static constexpr int RB = 2;                         // score row blocks per score wave
+  static constexpr int kRowsPerWave = 16 * RB;
+  static constexpr int kRows = kRoleWaves * kRowsPerWave;  // rows per workgroup
+  static constexpr int kRowBlocks = kRows / 16;
+  static constexpr int kPositions = kRows / G;
+  static constexpr int kPosPerWave = kRowsPerWave / G;
+  static constexpr int kSt = D / 32;                   // QK k-steps (32 head-dim elements)
+  static constexpr int kDbW = D / 16 / kRoleWaves;     // output blocks of 16 columns per PV wave
+  static constexpr int kChunks = D / 8;                // 16-byte chunks per row
+  static constexpr int kTile = BN * D;                 // elements of one K (or V) tile
+  static constexpr int kLoads = BN * kChunks / (64 * kRoleWaves);  // per lane per tile
+  static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
+  static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
+  static constexpr int kRing = 3;                      // buffers per K / V ring
+  static_assert(D % 64 == 0 && kRowsPerWave % G == 0, "row map");
+  static_assert(kLoads >= 1 && BN * kChunks % (64 * kRoleWaves) == 0, "tile load split");
+  static_assert(BN == 32 && kRoleWaves == 4, "KvTiles: loader w reads tile rows [8w, 8w+8)");
+};
+
+// Score wave, one step: S^T(t+1) = K Q^T for its RB row blocks on the K tile
+// `kt`, in 2*kSt groups (one K operand each), with stage i of the previous
+// tile's softmax (sm) after group i's MFMAs and the K(t+3) loads spread over
+// the groups.  The groups are fenced (only SALU instructions may cross), so
+// the vector work stays spread over the MFMAs.
+template <class C, bool DMA, class SM>
+__device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_t kpre,
+                                            const u32x4& krs, int kk0, uint32_t rs_bytes,
+                                            int widx, int lane, uint32_t krow, uint32_t kq16,
+                                            const bf16x8 (*q)[C::kSt], f32x4 (*s)[2], SM&& sm) {
+  constexpr int kN = 2 * C::kSt;              // groups
+  constexpr int kEvery = kN / C::kLoads;      // groups per direct load
+  constexpr int kAhead = 3;
+  static_assert(kN % C::kLoads == 0, "loads spread evenly over the groups");
+  const char* kb0 = reinterpret_cast<const char*>(kt) + krow;
+  auto kread = [&](int i) {
+    return ld_lds_x8(reinterpret_cast<const bf16*>(
+        kb0 + (kq16 ^ (uint32_t)((i >> 1) << 6)) + (i & 1) * 32 * C::D));
+  };
+  bf16x8 kop[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) kop[i] = kread(i);
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    const int st = i >> 1, kb = i & 1;
+    const bf16x8 a = kop[i % kAhead];
+    if (i + kAhead < kN) kop[i % kAhead] = kread(i + kAhead);
+    if constexpr (DMA) {
+      if (i % kEvery == 0)
+        dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kpre, krs, kk0, i / kEvery, rs_bytes, widx,
+                                                    lane);
+    }
+#pragma unroll
+    for (int rb = 0; rb < C::RB; ++rb) {
+      if (st == 0)
+        mfma16_vacc_first(s[rb][kb], a, q[rb][st]);
+      else
+        mfma16_vacc(s[rb][kb], a, q[rb][st]);
+    }
+    sm(i);  // stage i of the previous tile's softmax
+    __builtin_amdgcn_sched_barrier(0x0004);
+  }
+  mfma_drain();  // the scores are read by VALU code next
+}
+
+// PV wave, one step: O^T += V^T P^T for its kDbW output blocks of every row
+// block, V from the tile `vt`, P^T from the exchange buffer `pt`, with the
+// V(t+1) loads spread over the MFMAs.
+//   V operand (output block db): rows 4*gq + x/4 and +16, logical chunk
+//     2*(kDbW*p + db) + (x%4)/2, physical chunk ^ ((2*row) & kSwV),
+//     element 4*(x%2);
+//   P^T operand (row block r): 16 bytes of lane l at pt[64*r + l].
+template <class C, bool DMA>
+__device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
+                                         const bf16x8* __restrict__ pt, uint32_t vpre,
+                                         const u32x4& vrs, int vk0, uint32_t rs_bytes, int widx,
+                                         int lane, uint32_t vrow, uint32_t vc16w,
+                                         f32x4 (*o)[C::kDbW]) {
+  constexpr int kN = C::kRowBlocks;           // one row block per group
+  constexpr int kEvery = kN / C::kLoads;      // groups per direct load
+  static_assert(kN % C::kLoads == 0, "loads spread evenly over the groups");
+  const char* vb0 = reinterpret_cast<const char*>(vt) + vrow;
+  bf16x8 vop[C::kDbW];
+#pragma unroll
+  for (int db = 0; db < C::kDbW; ++db) {
+    const bf16* p = reinterpret_cast<const bf16*>(vb0 + (vc16w ^ (uint32_t)(db << 5)));
+    vop[db] = cat8(ld_lds_tr(p), ld_lds_tr(p + 16 * C::D));
+  }
+  bf16x8 pop[2];
+  pop[0] = pt[lane];
+#pragma unroll
+  for (int r = 0; r < kN; ++r) {
+    if (r + 1 < kN) pop[(r + 1) & 1] = pt[64 * (r + 1) + lane];
+    if constexpr (DMA) {
+      if (r % kEvery == 0)
+        dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, r / kEvery, rs_bytes, widx,
+                                                    lane);
+    }
+#pragma unroll
+    for (int db = 0; db < C::kDbW; ++db)
+      o[r][db] = mfma16(vop[db], pop[r & 1], o[r][db]);
+  }
+}
+
+template <class C>
+__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads),
+                          amdgpu_waves_per_eu(2, 2)))
+void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                       const bf16* __restrict__ v, bf16* __restrict__ o,
+                       float* __restrict__ lse, const int32_t* __restrict__ cu_seqlens,
+                       const int32_t* __restrict__ spans, int num_spans, int hq, int hkv,
+                       int window, float c2, int tiles, int nseq, PagedKv pk) {
+  constexpr int D = C::D, G = C::G, RB = C::RB, BN = C::BN, NR = C::kRing;
+  constexpr int kRB = C::kRowBlocks;
+  // K ring and V ring (tile kt lives in buffer (kt - kt0) % NR of each);
+  // exchange buffers for P, the accumulator factors and the scaling flags of
+  // tile kt (index kt & 1); the final row sums.
+  __shared__ __attribute__((aligned(1024))) bf16 ks[NR][C::kTile];
+  __shared__ __attribute__((aligned(1024))) bf16 vs[NR][C::kTile];
+  __shared__ __attribute__((aligned(1024))) bf16x8 pl[2][kRB * 64];
+  __shared__ __attribute__((aligned(16))) float al[2][C::kRows];
+  __shared__ __attribute__((aligned(16))) uint32_t fl[2][4];
+  __shared__ __attribute__((aligned(16))) float lrow[C::kRows];
+  static_assert(C::kRoleWaves == 4, "one flag word per score wave, read as one 16-byte word");
+
+  // Logical item = (tile, KV head, sequence), tile fastest; tiles run from
+  // the end of the sequence (longest causal rows first).  Tile t covers
+  // positions [t*P, (t+1)*P), counted from the first tile holding a query
+  // row of the sequence.
+  const long long item = xcd_logical_block(blockIdx.x);
+  if (item >= (long long)tiles * hkv * nseq) return;
+  const int g = (int)((item / tiles) % hkv);
+  const int b = (int)(item / ((long long)tiles * hkv));
+  constexpr bool PAGED = C::kPaged;
+  const SeqGeo sg = seq_geo<PAGED>(cu_seqlens, pk, b);
+  const int L = sg.L;
+  const int t = sg.qlo / C::kPositions + tiles - 1 - (int)(item % tiles);
+  const int p0 = t * C::kPositions;
+  if (p0 >= sg.qhi) return;
+  const int p1 = min(p0 + C::kPositions, sg.qhi);
+  const int seq0 = sg.qbase;  // packed row of position 0 (q / o / lse, spans)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const bool pv_wave = wave >= C::kRoleWaves;
+  const int widx = wave & (C::kRoleWaves - 1);  // index among the waves of its kind
+  const bool windowed = window > 0;
+
+  int ss, se;
+  // Key range of the workgroup: the window below its first row, the span
+  // holding its first row, its last row, the span holding its last row.
+  int lo = windowed ? max(0, p0 - window + 1) : 0;
+  int hi = p1;
+  if (num_spans > 0) {
+    if (find_span(spans, num_spans, seq0 + p0, ss, se)) lo = min(lo, max(ss - seq0, 0));
+    if (find_span(spans, num_spans, seq0 + p1 - 1, ss, se)) hi = max(hi, min(se - seq0, L));
+  }
+  const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
+
+  const uint32_t rs_bytes = (uint32_t)hkv * D * 2;
+  // This KV head's rows of the sequence, loaded through buffer resources of
+  // exactly that extent (the host rejects inputs whose rows span 2 GiB or
+  // more), or its cache blocks.  Score waves load K, PV waves load V.
+  const KvTiles<PAGED> src = kv_tiles<D, PAGED>(k, v, pk, sg, b, g, hkv, window);
+  constexpr uint32_t kTileBytes = C::kTile * 2;
+  const uint32_t ks_lds = lds_addr(ks[0]), vs_lds = lds_addr(vs[0]);
+
+  Lane16 ln;
+  ln.x = lane & 15;
+  ln.gq = lane >> 4;
+  ln.krow = (uint32_t)(ln.x * D * 2);
+  ln.kq16 = (uint32_t)((ln.gq ^ (ln.x & C::kSwK)) << 4);
+  {
+    const int y = ln.x, vr = 4 * ln.gq + (y >> 2);
+    ln.vrow = (uint32_t)(vr * D * 2 + 8 * (y & 1));
+    ln.vc16 = (uint32_t)((((y & 3) >> 1) ^ ((2 * vr) & C::kSwV)) << 4);
+  }
+  ln.wlim = windowed ? window : 0x7fffffff;
+  ln.c2 = c2;
+
+  using Mode0 = std::integral_constant<int, 0>;
+  using Mode1 = std::integral_constant<int, 1>;
+  using Mode2 = std::integral_constant<int, 2>;
+
+  if (!pv_wave) {
+    // ------------------------------------------------------------ score wave
+    const int pw0 = p0 + widx * C::kPosPerWave;
+    const int pw1 = min(pw0 + C::kPosPerWave, sg.qhi);
+    const bool wave_full = pw0 >= sg.qlo && pw0 + C::kPosPerWave <= sg.qhi;
+    int qpos[RB], qhead[RB], my_ss[RB], my_se[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = C::kRowsPerWave * widx + 16 * rb + ln.x;
+      const int pos = p0 + row / G;
+      qhead[rb] = g * G + row % G;
+      const bool valid = pos >= sg.qlo && pos < sg.qhi;
+      qpos[rb] = valid ? pos : -1;  // an invalid row admits no key
+      my_ss[rb] = 0;
+      my_se[rb] = 0;
+      if (num_spans > 0 && valid && find_span(spans, num_spans, seq0 + pos, ss, se)) {
+        my_ss[rb] = ss - seq0;
+        my_se[rb] = min(se - seq0, L);
+      }
+    }
+    // Q^T operands: lane holds q[row][32*st + 8*gq .. +7] for every st.
+    // Rows outside the sequence's query rows load its first query row
+    // instead; every key is masked for them and they are never stored.
+    bf16x8 qr[RB][C::kSt];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bf16* qrow = q + ((size_t)(seq0 + (qpos[rb] >= 0 ? qpos[rb] : sg.qlo)) * hq +
+                              qhead[rb]) * D + 8 * ln.gq;
+#pragma unroll
+      for (int st = 0; st < C::kSt; ++st) qr[rb][st] = ld_global_x8(qrow + 32 * st);
+    }
+    auto load_k = [&](int slot, int kt) {
+      u32x4 krsc, vrsc;
+      int k0r;
+      src.get(kt, kt < kt1, widx, krsc, vrsc, k0r);
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i)
+        dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(ks_lds + slot * kTileBytes, krsc, k0r, i,
+                                                    rs_bytes, widx, lane);
+    };
+    RowStats<RB> rs;
+    rs.init();
+
+    // Prologue: K(kt0), K(kt0+1), K(kt0+2); wait for K(kt0) and form S(kt0).
+    load_k(0, kt0);
+    load_k(1, kt0 + 1);
+    load_k(2, kt0 + 2);
+    wait_vmcnt<2 * C::kLoads>();
+    lds_barrier();
+    f32x4 sa[RB][2], sb[RB][2];
+    {
+      const u32x4 none = buffer_rsrc(k, 0);
+      score_phase<C, false>(ks[0], 0, none, 0, rs_bytes, widx, lane, ln.krow, ln.kq16, qr, sa,
+                            [](int) {});
+    }
+    // Step kt: wait for K(kt+1) (loaded two steps ago), then S(kt+1) on the
+    // MFMAs with the K(kt+3) loads among them (into the buffer of K(kt), free
+    // once every wave is past the barrier), while the VALU takes the softmax
+    // of tile kt; the rare reference-max moves are handled after the MFMAs
+    // are issued, and P(kt) goes to the exchange buffer.  After the last tile
+    // the scores formed are never used (the K buffer holds zeros or an older
+    // tile); forming them keeps the step branch-free.
+    auto step = [&] __device__(int kt, f32x4(&sc)[RB][2], f32x4(&sn)[RB][2]) {
+      const int r = (kt - kt0) % NR;
+      const bf16* __restrict__ kcur = ks[(r + 1) % NR];  // K(kt+1)
+      const uint32_t kpre = ks_lds + r * kTileBytes;      // K(kt+3)
+      const int k0 = kt * BN;
+      wait_vmcnt<C::kLoads>();
+      lds_barrier();
+      const bool need_mask =
+          !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
+      const uint32_t kq16 = opaque(ln.kq16);
+      u32x4 krs, unused;
+      int kk0;
+      src.get(kt + 3, kt + 3 < kt1, widx, krs, unused, kk0);
+      float alpha[RB];
+      uint32_t smask = 0;
+      bf16x8 pc[RB];
+      auto run = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        TileSoftmax<RB, MASK> ts;
+        ts.init(k0, ln, qpos, my_ss, my_se);
+        score_phase<C, true>(kcur, kpre, krs, kk0, rs_bytes, widx, lane, ln.krow, kq16, qr, sn,
+                             [&](int i) { ts.stage(i, sc, ln, rs); });
+        if (ts.finish(rs)) smask = ts.move(sc, k0, ln, qpos, my_ss, my_se, rs, alpha);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) pc[rb] = ts.pb[rb];
+      };
+      if (need_mask)
+        run(std::true_type{});
+      else
+        run(std::false_type{});
+      // Exchange: P(kt) of this wave's row blocks, its scaling flags and
+      // (when set) the row factors.
+      bf16x8* pw = pl[kt & 1];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) pw[64 * (RB * widx + rb) + lane] = pc[rb];
+      if (smask != 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if ((smask & (1u << rb)) && ln.gq == 0)
+            al[kt & 1][16 * (RB * widx + rb) + ln.x] = alpha[rb];
+      }
+      if (lane == 0) fl[kt & 1][widx] = smask;
+    };
+    step(kt0, sa, sb);
+    int kt = kt0 + 1;
+    for (; kt + 1 < kt1; kt += 2) {
+      step(kt, sb, sa);
+      step(kt + 1, sa, sb);
+    }
+    if (kt < kt1) step(kt, sb, sa);
+
+    // Final row sums of this wave's rows for the PV waves' epilogue.
+    float lsum[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) lsum[rb] = rs.row_sum(rb);
+    if (ln.gq == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) lrow[C::kRowsPerWave * widx + 16 * rb + ln.x] = lsum[rb];
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (lse != nullptr && ln.gq == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        if (qpos[rb] >= 0)
+          lse[(size_t)(seq0 + qpos[rb]) * hq + qhead[rb]] =
+              (rs.m[rb] + fast_log2(lsum[rb])) * 0.693147180559945309f;
+    }
+    return;
+  }
+
+  // ---------------------------------------------------------------- PV wave
+  // V operand base of this wave's first output block.
+  const uint32_t vc16w = ln.vc16 ^ (uint32_t)((C::kDbW * widx) << 5);
+  auto load_v = [&](int slot, int kt) {
+    u32x4 krsc, vrsc;
+    int k0r;
+    src.get(kt, kt < kt1, widx, krsc, vrsc, k0r);
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i)
+      dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vs_lds + slot * kTileBytes, vrsc, k0r, i,
+                                                  rs_bytes, widx, lane);
+  };
+  // Accumulators start at +0: the first PV product adds to +0, which is the
+  // product itself (as with a zero addend).
+  f32x4 oacc[kRB][C::kDbW];
+#pragma unroll
+  for (int r = 0; r < kRB; ++r)
+#pragma unroll
+    for (int db = 0; db < C::kDbW; ++db) oacc[r][db] = f32x4{};
+
+  // Scale the accumulator blocks whose rows moved their reference max in
+  // tile kt (flags and factors written by the score waves in step kt).
+  auto rescale_from = [&](int kt) {
+    const u32x4 f = *reinterpret_cast<const u32x4*>(fl[kt & 1]);
+    const uint32_t mask = __builtin_amdgcn_readfirstlane(
+        f[0] | (f[1] << RB) | (f[2] << (2 * RB)) | (f[3] << (3 * RB)));
+    if (mask != 0) {
+      // Blocks without a flag take factor 1 (exact).
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) {
+        const float a = (mask & (1u << r)) ? al[kt & 1][16 * r + ln.x] : 1.f;
+#pragma unroll
+        for (int db = 0; db < C::kDbW; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oacc[r][db][i] = oacc[r][db][i] * a;
+      }
+    }
+  };
+
+  // Prologue: V(kt0) (what step kt0-1 would load); the barrier matches the
+  // score waves' prologue barrier.
+  load_v(0, kt0);
+  lds_barrier();
+
+  // Step kt: wait for V(kt-1) (loaded two steps ago), scale for the moves of
+  // tile kt-1, then PV(kt-1) with the V(kt+1) loads among the MFMAs (into
+  // the buffer of V(kt-2), free once every wave is past the barrier).
+  // MODE 0: first tile (no PV yet); 1: first PV (nothing to scale yet);
+  // 2: steady state.
+  auto step = [&] __device__(int kt, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
+    const int r = (kt - kt0) % NR;
+    const bf16* __restrict__ vcur = vs[(r + NR - 1) % NR];       // V(kt-1)
+    const uint32_t vpre = vs_lds + ((r + 1) % NR) * kTileBytes;  // V(kt+1)
+    const bf16x8* __restrict__ pcur = pl[(kt - 1) & 1];         // P(kt-1)
+    wait_vmcnt<C::kLoads>();
+    lds_barrier();
+    u32x4 vrs, unused;
+    int vk0;
+    src.get(kt + 1, kt + 1 < kt1, widx, unused, vrs, vk0);
+    if constexpr (MODE == 0) {
+      // No PV yet: only the V(kt0+1) loads.
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i)
+        dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, i, rs_bytes, widx, lane);
+    } else {
+      if constexpr (MODE == 2) rescale_from(kt - 1);
+      pv_phase<C, true>(vcur, pcur, vpre, vrs, vk0, rs_bytes, widx, lane, ln.vrow,
+                        opaque(vc16w), oacc);
+    }
+  };
+  step(kt0, Mode0{});
+  if (kt0 + 1 < kt1) step(kt0 + 1, Mode1{});
+  for (int kt = kt0 + 2; kt < kt1; ++kt) step(kt, Mode2{});
+
+  // PV of the last tile: every remaining load has landed (the loads after
+  // the last tile are zero-length) and P(kt1-1) is in the exchange buffer.
+  const int kl = kt1 - 1;
+  wait_vmcnt<0>();
+  lds_barrier();
+  if (kl > kt0) rescale_from(kl);
+  pv_phase<C, false>(vs[(kl - kt0) % NR], pl[kl & 1], 0, buffer_rsrc(v, 0), 0, rs_bytes, widx,
+                     lane, ln.vrow, vc16w, oacc);
+
+  // Epilogue: o = acc / l (IEEE fp32 division), bf16 RNE, store this wave's
+  // columns of every row.
+#pragma unroll
+  for (int r = 0; r < kRB; ++r) {
+    const int row = 16 * r + ln.x;
+    const int pos = p0 + row / G;
+    if (pos < sg.qlo || pos >= sg.qhi) continue;
+    const float lr = lrow[row];
+    bf16* orow = o + ((size_t)(seq0 + pos) * hq + g * G + row % G) * D + 16 * C::kDbW * widx +
+                 4 * ln.gq;
+#pragma unroll
+    for (int db = 0; db < C::kDbW; ++db) {
+      bf16x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = to_bf16(oacc[r][db][i] / lr);
+      *reinterpret_cast<bf16x4*>(orow + 16 * db) = w;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one row block's divisions at a time
+  }
+}
+
+template <class C>
+static hipError_t launch_ws(const PrefillArgs& a, hipStream_t stream) {
+  const int tiles = prefill_grid_tiles(a, C::kPositions);
+  const long long blocks = xcd_padded_blocks((long long)tiles * a.hkv * a.batch);
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const PagedKv pk{a.q_start, a.block_table, a.max_blocks, a.num_blocks, a.max_context};
+  if (a.q_start != nullptr)
+    hipLaunchKernelGGL(prefill_ws_kernel<PagedOf<C>>, dim3((unsigned)blocks), dim3(C::kThreads),
+                       0, stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v,
+                       (bf16*)a.o, a.lse, a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv,
+                       a.window, a.c2, tiles, a.batch, pk);
+  else
+    hipLaunchKernelGGL(prefill_ws_kernel<C>, dim3((unsigned)blocks), dim3(C::kThreads), 0,
+                       stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (bf16*)a.o,
+                       a.lse, a.cu_seqlens, a.spans, a.num_spans, a.hq, a.hkv, a.window, a.c2,
+                       tiles, a.batch, pk);
+  return hipGetLastError();
+}
+
+// One kernel instance per (head_dim, group).
+#define INVATTN_WS_TABLE(X) X(256, 1) X(256, 2) X(256, 4) X(256, 8)
+
+bool prefill_ws_schedule(int d, int group, PrefillSchedule* s) {
+#define X(D, G)                                                               \
+  if (d == D && group == G) {                                                 \
+    using C = PfWsCfg<D, G>;                                                  \
+    *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads};        \
+    return true;                                                              \
+  }
+  INVATTN_WS_TABLE(X)
+#undef X
+  return false;
+}
+
+hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream) {
+  const int group = a.hq / a.hkv;
+#define X(D, G) \
+  if (a.d == D && group == G) return launch_ws<PfWsCfg<D, G>>(a, stream);
+  INVATTN_WS_TABLE(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace invattn
