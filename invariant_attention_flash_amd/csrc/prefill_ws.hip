@@ -78,8 +78,9 @@ struct PfWsCfg {
 // Score wave, one step: S^T(t+1) = K Q^T for its RB row blocks on the K tile
 // `kt`, in 2*kSt groups (one K operand each), with stage i of the previous
 // tile's softmax (sm) after group i's MFMAs and the K(t+3) loads spread over
-// the groups.  The groups are fenced (only SALU instructions may cross), so
-// the vector work stays spread over the MFMAs.
+// the groups.  The MFMAs are compiler builtins with VGPR accumulators (the
+// kernel uses no AGPRs), so the compiler tracks their result latency and
+// schedules the softmax's vector work around them freely.
 template <class C, bool DMA, class SM>
 __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_t kpre,
                                             const u32x4& krs, int kk0, uint32_t rs_bytes,
@@ -109,15 +110,10 @@ __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_
     }
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
-      if (st == 0)
-        mfma16_vacc_first(s[rb][kb], a, q[rb][st]);
-      else
-        mfma16_vacc(s[rb][kb], a, q[rb][st]);
+      s[rb][kb] = mfma16(a, q[rb][st], st == 0 ? f32x4{} : s[rb][kb]);
     }
     sm(i);  // stage i of the previous tile's softmax
-    __builtin_amdgcn_sched_barrier(0x0004);
   }
-  mfma_drain();  // the scores are read by VALU code next
 }
 
 // PV wave, one step: O^T += V^T P^T for its kDbW output blocks of every row
