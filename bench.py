@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # The prefill kernel the benchmark times (head dim 256, group 2): its name in
 # rocprofv3 output and the key of its HBM traffic in profiles/traffic.json.
 PREFILL_TRAFFIC_KEY = "prefill_ws_kernel<256,2>"
-PREFILL_KERNEL_MATCH = "prefill_ws_kernel<invattn::PfWsCfg<256, 2>"
+PREFILL_KERNEL_MATCH = "prefill_ws_kernel<invattn::PfWsCfg<256, 2, "
 PREFILL_KERNEL_FIRST = "prefill_ws_kernel"
 PREFILL_KERNEL_LABEL = "prefill_ws_kernel (head_dim 256, group 2)"
 

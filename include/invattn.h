@@ -15,18 +15,17 @@
  * in one ascending order of 32-key tiles (prefill) or 16-key cache blocks
  * (decode), c = fl32(scale * log2(e)):
  *   s_j  = fp32 MFMA dot product of bf16 q_i and bf16 k_j, head dim in
- *          ascending MFMA steps (head dim 512: two halves summed as
- *          half 0 + half 1)
+ *          ascending MFMA steps of 32
  *   m    = reference max (scaled units), -inf before the first allowed key;
  *          it moves to the tile's scaled max only when the row would
- *          otherwise see p > 2^8 (head dim 256: tested on p itself; other
- *          head dims and decode: tile max > m + 8), or at the first
- *          allowed key
+ *          otherwise see p > 2^8 (head dims 256 and 512: tested on p
+ *          itself; head dim 64 and decode: tile max > m + 8), or at the
+ *          first allowed key
  *   p_j  = exp2(fma(s_j, c, -m))          (hardware exp2, fp32; m -> 0
  *          while m = -inf)
- *   l    = l * alpha + (sum of the tile's p in a fixed order); head dim
- *          256 keeps one such sum per lane and combines a row's four lanes
- *          once, after the last tile, in a fixed order
+ *   l    = l * alpha + (sum of the tile's p in a fixed order); head dims
+ *          256 and 512 keep one such sum per lane and combine a row's four
+ *          lanes once, after the last tile, in a fixed order
  *   acc  = acc * alpha + bf16(p) . v      (bf16 MFMA, fp32 accumulate)
  *          with alpha = exp2(m_old - m_new) on a move, else 1 (no multiply)
  *   o    = bf16_rne(acc / l)              (IEEE fp32 division)

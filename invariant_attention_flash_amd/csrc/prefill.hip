@@ -444,9 +444,14 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 #ifndef PF_WS256
 #define PF_WS256 1
 #endif
+#ifndef PF_WS512
+#define PF_WS512 1
+#endif
+
+static bool use_ws(int d) { return (d == 256 && PF_WS256) || (d == 512 && PF_WS512); }
 
 bool prefill_schedule(int d, int group, PrefillSchedule* s) {
-  if (PF_WS256 && prefill_ws_schedule(d, group, s)) return true;
+  if (use_ws(d) && prefill_ws_schedule(d, group, s)) return true;
   if (PF_SPLIT256 && prefill_split_schedule(d, group, s)) return true;
 #define X(D, G, ...)                                                          \
   if (d == D && group == G) {                                                 \
@@ -462,7 +467,7 @@ bool prefill_schedule(int d, int group, PrefillSchedule* s) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
   PrefillSchedule sp;
-  if (PF_WS256 && prefill_ws_schedule(a.d, group, &sp)) return launch_prefill_ws(a, stream);
+  if (use_ws(a.d) && prefill_ws_schedule(a.d, group, &sp)) return launch_prefill_ws(a, stream);
   if (PF_SPLIT256 && prefill_split_schedule(a.d, group, &sp)) return launch_prefill_split(a, stream);
 #define X(D, G, ...) \
   if (a.d == D && group == G) return launch_one<Pf16Cfg<D, G, __VA_ARGS__>>(a, stream);

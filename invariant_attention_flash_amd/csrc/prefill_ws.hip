@@ -1,5 +1,6 @@
-// prefill_ws.hip -- batch-invariant prefill for head dim 256 with the work of
-// a workgroup specialised over two kinds of waves, two waves per SIMD.
+// prefill_ws.hip -- batch-invariant prefill for head dims 256 and 512 with
+// the work of a workgroup specialised over two kinds of waves, two waves per
+// SIMD.
 //
 // Sources: sliding and global attention cores are separate layer types with
 // their own head geometry and masks ("RFC: Gemma-4-31B-it train/rollout
@@ -16,30 +17,32 @@
 // wave's own MFMAs.  Here a workgroup has eight waves, two per SIMD: four
 // score waves and four PV waves.  The SIMD interleaves the two streams, so
 // the softmax of one wave runs while the other's MFMAs do, and each wave
-// needs half the registers of a combined one (which is what lets two of them
-// share a SIMD).
+// needs at most 256 registers (which is what lets two of them share a SIMD).
 //
-// Work map (the same rows, columns, tiles and order as one wave doing both):
-// a workgroup owns `positions` consecutive positions of ONE sequence, aligned
-// to the sequence start, for the G query heads of one KV head; rows are
-// position-major (row = position*G + head), cut into 8 blocks of 16.
-//   score wave s (0..3): row blocks 2s, 2s+1; Q in registers;
+// Work map: a workgroup owns `positions` consecutive positions of ONE
+// sequence, aligned to the sequence start, for the G query heads of one KV
+// head; rows are position-major (row = position*G + head), cut into blocks
+// of 16 (8 blocks at head dim 256, 4 at 512).
+//   score wave s (0..3): row blocks RB*s .. RB*s+RB-1 (RB = 2 at head dim
+//     256, 1 at 512; Q of those rows in 64 VGPRs);
 //     S^T(t+1) = K Q^T  (v_mfma_f32_16x16x32_bf16, K operand from LDS, lane l
 //                        holds keys 4*(l/16)+i of query row l%16, for 16-key
 //                        halves kb = 0, 1),
 //     softmax of tile t (fp32; the online rule of prefill_common.h) staged
 //     between its MFMAs, P(t) (bf16, RNE) to LDS with the accumulator factors
-//     of rows whose reference max moved; loads K(t+3).
-//   PV wave p (0..3): output columns [64p, 64p+64) of all 8 row blocks;
-//     O^T += V^T P^T(t-1) after scaling the blocks whose rows moved in tile
-//     t-1; P^T is the score lane's own 8 probabilities (k-slot 8*(l/16) + s
-//     meaning key 16*(s/4) + 4*(l/16) + s%4), V^T comes through the transpose
-//     read in that key order; loads V(t+1); the epilogue.
+//     of rows whose reference max moved; loads K(t+NR).
+//   PV wave p (0..3): output columns [D/4 * p, D/4 * (p+1)) of every row
+//     block; O^T += V^T P^T(t-1) after scaling the blocks whose rows moved
+//     in tile t-1; P^T is the score lane's own 8 probabilities (k-slot
+//     8*(l/16) + s meaning key 16*(s/4) + 4*(l/16) + s%4), V^T comes through
+//     the transpose read in that key order; loads V(t+NR-2); the epilogue.
 // K and V tiles (32 keys, ascending) stream HBM -> LDS with direct loads into
-// two rings of three buffers; one LDS barrier per step orders the rings, the
-// P exchange and the flags.  Keys past the sequence end load as zeros and are
-// masked.  Every output element sees the same sequence of MFMAs and scalings
-// as in a workgroup whose waves do both jobs, so the bytes are the same.
+// two rings of NR buffers (3 at head dim 256, 2 at 512 where a tile is
+// 32 KB); one LDS barrier per step orders the rings, the P exchange and the
+// flags.  Keys past the sequence end load as zeros and are masked.  At head
+// dim 256 every output element sees the same sequence of MFMAs and scalings
+// as in the one-wave-per-SIMD kernel of prefill_split.hip, so the bytes are
+// the same.
 #include <type_traits>
 
 #include "device_common.h"
@@ -48,7 +51,7 @@
 
 namespace invattn {
 
-template <int D_, int G_>
+template <int D_, int G_, int RB_, int NR_>
 struct PfWsCfg {
   static constexpr bool kPaged = false;  // contiguous keys (PagedOf<> sets it)
   static constexpr int D = D_, G = G_;
@@ -56,7 +59,7 @@ struct PfWsCfg {
   static constexpr int kWaves = 2 * kRoleWaves;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BN = 32;                        // keys per KV tile
-  static constexpr int RB = 2;                         // score row blocks per score wave
+  static constexpr int RB = RB_;                       // score row blocks per score wave
   static constexpr int kRowsPerWave = 16 * RB;
   static constexpr int kRows = kRoleWaves * kRowsPerWave;  // rows per workgroup
   static constexpr int kRowBlocks = kRows / 16;
@@ -69,10 +72,13 @@ struct PfWsCfg {
   static constexpr int kLoads = BN * kChunks / (64 * kRoleWaves);  // per lane per tile
   static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
   static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
-  static constexpr int kRing = 3;                      // buffers per K / V ring
+  static constexpr int kRing = NR_;                    // buffers per K / V ring
   static_assert(D % 64 == 0 && kRowsPerWave % G == 0, "row map");
   static_assert(kLoads >= 1 && BN * kChunks % (64 * kRoleWaves) == 0, "tile load split");
   static_assert(BN == 32 && kRoleWaves == 4, "KvTiles: loader w reads tile rows [8w, 8w+8)");
+  static_assert(kRing == 2 || kRing == 3, "ring of two or three tiles");
+  static_assert(kRing * 2 * kTile * 2 + 2 * kRowBlocks * 64 * 16 + 3 * kRows * 4 + 32 <= 163840,
+                "LDS budget");
 };
 
 // Score wave, one step: S^T(t+1) = K Q^T for its RB row blocks on the K tile
@@ -130,8 +136,10 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
                                          int lane, uint32_t vrow, uint32_t vc16w,
                                          f32x4 (*o)[C::kDbW]) {
   constexpr int kN = C::kRowBlocks;           // one row block per group
-  constexpr int kEvery = kN / C::kLoads;      // groups per direct load
-  static_assert(kN % C::kLoads == 0, "loads spread evenly over the groups");
+  // Direct loads spread evenly: one every kEvery groups, or kPer per group.
+  constexpr int kEvery = kN >= C::kLoads ? kN / C::kLoads : 1;
+  constexpr int kPer = kN >= C::kLoads ? 1 : C::kLoads / kN;
+  static_assert(kN % C::kLoads == 0 || C::kLoads % kN == 0, "loads spread evenly over the groups");
   const char* vb0 = reinterpret_cast<const char*>(vt) + vrow;
   bf16x8 vop[C::kDbW];
 #pragma unroll
@@ -145,9 +153,12 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
   for (int r = 0; r < kN; ++r) {
     if (r + 1 < kN) pop[(r + 1) & 1] = pt[64 * (r + 1) + lane];
     if constexpr (DMA) {
-      if (r % kEvery == 0)
-        dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, r / kEvery, rs_bytes, widx,
-                                                    lane);
+      if (r % kEvery == 0) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+          dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, (r / kEvery) * kPer + u,
+                                                      rs_bytes, widx, lane);
+      }
     }
 #pragma unroll
     for (int db = 0; db < C::kDbW; ++db)
@@ -278,11 +289,10 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     RowStats<RB> rs;
     rs.init();
 
-    // Prologue: K(kt0), K(kt0+1), K(kt0+2); wait for K(kt0) and form S(kt0).
-    load_k(0, kt0);
-    load_k(1, kt0 + 1);
-    load_k(2, kt0 + 2);
-    wait_vmcnt<2 * C::kLoads>();
+    // Prologue: K(kt0) .. K(kt0+NR-1); wait for K(kt0) and form S(kt0).
+#pragma unroll
+    for (int i = 0; i < NR; ++i) load_k(i, kt0 + i);
+    wait_vmcnt<(NR - 1) * C::kLoads>();
     lds_barrier();
     f32x4 sa[RB][2], sb[RB][2];
     {
@@ -290,8 +300,8 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       score_phase<C, false>(ks[0], 0, none, 0, rs_bytes, widx, lane, ln.krow, ln.kq16, qr, sa,
                             [](int) {});
     }
-    // Step kt: wait for K(kt+1) (loaded two steps ago), then S(kt+1) on the
-    // MFMAs with the K(kt+3) loads among them (into the buffer of K(kt), free
+    // Step kt: wait for K(kt+1) (loaded NR-1 steps ago), then S(kt+1) on the
+    // MFMAs with the K(kt+NR) loads among them (into the buffer of K(kt), free
     // once every wave is past the barrier), while the VALU takes the softmax
     // of tile kt; the rare reference-max moves are handled after the MFMAs
     // are issued, and P(kt) goes to the exchange buffer.  After the last tile
@@ -300,16 +310,16 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     auto step = [&] __device__(int kt, f32x4(&sc)[RB][2], f32x4(&sn)[RB][2]) {
       const int r = (kt - kt0) % NR;
       const bf16* __restrict__ kcur = ks[(r + 1) % NR];  // K(kt+1)
-      const uint32_t kpre = ks_lds + r * kTileBytes;      // K(kt+3)
+      const uint32_t kpre = ks_lds + r * kTileBytes;      // K(kt+NR)
       const int k0 = kt * BN;
-      wait_vmcnt<C::kLoads>();
+      wait_vmcnt<(NR - 2) * C::kLoads>();
       lds_barrier();
       const bool need_mask =
           !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
       const uint32_t kq16 = opaque(ln.kq16);
       u32x4 krs, unused;
       int kk0;
-      src.get(kt + 3, kt + 3 < kt1, widx, krs, unused, kk0);
+      src.get(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
       float alpha[RB];
       uint32_t smask = 0;
       bf16x8 pc[RB];
@@ -407,29 +417,30 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   };
 
-  // Prologue: V(kt0) (what step kt0-1 would load); the barrier matches the
-  // score waves' prologue barrier.
-  load_v(0, kt0);
+  // Prologue: V(kt0) .. V(kt0+NR-3) (what the steps before kt0 would load);
+  // the barrier matches the score waves' prologue barrier.
+#pragma unroll
+  for (int i = 0; i + 2 < NR; ++i) load_v(i, kt0 + i);
   lds_barrier();
 
-  // Step kt: wait for V(kt-1) (loaded two steps ago), scale for the moves of
-  // tile kt-1, then PV(kt-1) with the V(kt+1) loads among the MFMAs (into
-  // the buffer of V(kt-2), free once every wave is past the barrier).
+  // Step kt: wait for V(kt-1) (loaded NR-1 steps ago), scale for the moves
+  // of tile kt-1, then PV(kt-1) with the V(kt+NR-2) loads among the MFMAs
+  // (into the buffer of V(kt-2), free once every wave is past the barrier).
   // MODE 0: first tile (no PV yet); 1: first PV (nothing to scale yet);
   // 2: steady state.
   auto step = [&] __device__(int kt, auto mode) {
     constexpr int MODE = decltype(mode)::value;
     const int r = (kt - kt0) % NR;
     const bf16* __restrict__ vcur = vs[(r + NR - 1) % NR];       // V(kt-1)
-    const uint32_t vpre = vs_lds + ((r + 1) % NR) * kTileBytes;  // V(kt+1)
+    const uint32_t vpre = vs_lds + ((r + NR - 2) % NR) * kTileBytes;  // V(kt+NR-2)
     const bf16x8* __restrict__ pcur = pl[(kt - 1) & 1];         // P(kt-1)
-    wait_vmcnt<C::kLoads>();
+    wait_vmcnt<(NR - 2) * C::kLoads>();
     lds_barrier();
     u32x4 vrs, unused;
     int vk0;
-    src.get(kt + 1, kt + 1 < kt1, widx, unused, vrs, vk0);
+    src.get(kt + NR - 2, kt + NR - 2 < kt1, widx, unused, vrs, vk0);
     if constexpr (MODE == 0) {
-      // No PV yet: only the V(kt0+1) loads.
+      // No PV yet: only the V(kt0+NR-2) loads.
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i)
         dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, i, rs_bytes, widx, lane);
@@ -492,13 +503,21 @@ static hipError_t launch_ws(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One kernel instance per (head_dim, group).
-#define INVATTN_WS_TABLE(X) X(256, 1) X(256, 2) X(256, 4) X(256, 8)
+// One kernel instance per (head_dim, group).  Parameters after (D, G): score
+// row blocks per score wave (Q of 16*RB rows in 64 VGPRs: 2 at head dim 256,
+// 1 at 512), buffers per K/V ring (3 at 256; 2 at 512, where a tile of 32
+// keys is 32 KB).
+#define PF_WS_CFG256 2, 3
+#define PF_WS_CFG512 1, 2
+#define INVATTN_WS_TABLE(X)                                                            \
+  X(256, 1, PF_WS_CFG256) X(256, 2, PF_WS_CFG256) X(256, 4, PF_WS_CFG256)              \
+  X(256, 8, PF_WS_CFG256) X(512, 1, PF_WS_CFG512) X(512, 2, PF_WS_CFG512)              \
+  X(512, 4, PF_WS_CFG512) X(512, 8, PF_WS_CFG512)
 
 bool prefill_ws_schedule(int d, int group, PrefillSchedule* s) {
-#define X(D, G)                                                               \
+#define X(D, G, ...)                                                          \
   if (d == D && group == G) {                                                 \
-    using C = PfWsCfg<D, G>;                                                  \
+    using C = PfWsCfg<D, G, __VA_ARGS__>;                                     \
     *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads};        \
     return true;                                                              \
   }
@@ -509,8 +528,8 @@ bool prefill_ws_schedule(int d, int group, PrefillSchedule* s) {
 
 hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
-#define X(D, G) \
-  if (a.d == D && group == G) return launch_ws<PfWsCfg<D, G>>(a, stream);
+#define X(D, G, ...) \
+  if (a.d == D && group == G) return launch_ws<PfWsCfg<D, G, __VA_ARGS__>>(a, stream);
   INVATTN_WS_TABLE(X)
 #undef X
   return hipErrorInvalidValue;
