@@ -56,6 +56,10 @@ def open_library(path: str):
     lib.oracle_decode.restype = ctypes.c_int
     lib.oracle_decode.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, i32,
                                   vp, i32, i32, i32, i32, i32, i32, dbl, vp, vp, i32]
+    lib.oracle_prefill_backward.restype = ctypes.c_int
+    lib.oracle_prefill_backward.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp,
+                                            ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, i32,
+                                            i32, dbl, vp, i32, i32]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = [i32]
     return lib
@@ -154,3 +158,38 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, window=NO_WINDOW, scale=N
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return (o, lse) if want_lse else o
+
+
+def prefill_backward(q, k, v, dout, cu_seqlens, window=NO_WINDOW, scale=None, spans=None,
+                     threads=0, lib=None):
+    """Gradients (dq, dk, dv) of prefill attention for the upstream gradient
+    ``dout`` = dL/dO.  q/dout [T,Hq,D], k/v [T,Hkv,D]; outputs float64 in the
+    same shapes.  Same mask, spans and scale conventions as ``prefill``."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    dout = np.ascontiguousarray(dout)
+    if k.dtype != v.dtype:
+        raise TypeError("k and v must share a dtype")
+    if dout.shape != q.shape:
+        raise ValueError("dout must have the shape of q")
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    sp = None
+    ns = 0
+    if spans is not None and len(spans):
+        sp = np.ascontiguousarray(spans, dtype=np.int32).reshape(-1, 2)
+        ns = sp.shape[0]
+    dq = np.zeros((T, hq, d), np.float64)
+    dk = np.zeros((T, hkv, d), np.float64)
+    dv = np.zeros((T, hkv, d), np.float64)
+    rc = (lib or _load()).oracle_prefill_backward(
+        _ptr(q), _code(q), _ptr(k), _ptr(v), _code(k), _ptr(dout), _code(dout), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(cu), cu.shape[0] - 1, hq, hkv, d, int(window), float(scale),
+        _ptr(sp), ns, int(threads))
+    if rc != 0:
+        raise ValueError("oracle_prefill_backward rejected its arguments")
+    return dq, dk, dv

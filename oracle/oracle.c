@@ -219,6 +219,133 @@ int oracle_decode(const void* q, int qdtype, const void* k_cache,
     return 0;
 }
 
+/*
+ * Gradient of prefill attention with respect to q, k and v for an upstream
+ * gradient dout = dL/dO, by the chain rule applied to the definition above
+ * (the derivative of softmax: dL/ds_j = p_j (dL/dp_j - sum_a p_a dL/dp_a)):
+ *
+ *     p_j    = exp(s_j - lse)                         (the row's softmax)
+ *     o      = sum_j p_j V[j,:]
+ *     delta  = sum_c dout[i,c] o[c]                   (= sum_j p_j dp_j)
+ *     dp_j   = sum_c dout[i,c] V[j,c]
+ *     ds_j   = p_j (dp_j - delta)
+ *     dQ[i,:]  = scale * sum_j ds_j K[j,:]            (j ascending)
+ *     dK[j,:] += scale * ds_j Q[i,:]                  (rows i ascending, then
+ *     dV[j,:] += p_j dout[i,:]                         the group's heads)
+ *
+ * Same mask, GQA map and layouts as oracle_prefill.  dq [T, hq, d],
+ * dk / dv [T, hkv, d] are fp64 outputs.  Two passes: rows (softmax, delta,
+ * dq), then keys (dk, dv summed over every row and query head that admits
+ * the key).  Returns 0, or -1 on bad arguments.
+ */
+int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void* v,
+                            int kvdtype, const void* dout, int dodtype,
+                            double* dq, double* dk, double* dv,
+                            const int32_t* cu_seqlens, int32_t batch, int32_t hq,
+                            int32_t hkv, int32_t d, int32_t window, double scale,
+                            const int32_t* spans, int32_t num_spans, int32_t threads) {
+    if (batch < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
+    const int64_t total = cu_seqlens[batch];
+    const int32_t group = hq / hkv;
+    int64_t max_len = 1;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t len = cu_seqlens[b + 1] - cu_seqlens[b];
+        if (len < 0) return -1;
+        if (len > max_len) max_len = len;
+    }
+    const int64_t nt = total > 0 ? total : 1;
+    int32_t* seq_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)nt);
+    int64_t* span_lo = (int64_t*)malloc(sizeof(int64_t) * (size_t)nt);
+    int64_t* span_hi = (int64_t*)malloc(sizeof(int64_t) * (size_t)nt);
+    double* lse = (double*)malloc(sizeof(double) * (size_t)(nt * hq));
+    double* delta = (double*)malloc(sizeof(double) * (size_t)(nt * hq));
+    for (int32_t b = 0; b < batch; ++b)
+        for (int64_t t = cu_seqlens[b]; t < cu_seqlens[b + 1]; ++t) {
+            seq_of[t] = b;
+            span_lo[t] = span_hi[t] = -1;
+            for (int32_t sp = 0; sp < num_spans; ++sp)
+                if (t >= spans[2 * sp] && t < spans[2 * sp + 1]) {
+                    span_lo[t] = spans[2 * sp] - cu_seqlens[b];
+                    span_hi[t] = spans[2 * sp + 1] - cu_seqlens[b];
+                }
+        }
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#endif
+    /* Pass 1: per (row, query head). */
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)max_len);
+        int64_t* key_off = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_len);
+        double* o = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t w = 0; w < total * hq; ++w) {
+            int64_t t = w / hq;
+            int32_t h = (int32_t)(w % hq), g = h / group, b = seq_of[t];
+            int64_t start = cu_seqlens[b], len = cu_seqlens[b + 1] - start, i = t - start;
+            int64_t n = 0;
+            for (int64_t j = 0; j < len; ++j)
+                if (allowed(i, j, window, span_lo[t], span_hi[t]))
+                    key_off[n++] = ((start + j) * hkv + g) * (int64_t)d;
+            double l;
+            attend_row(q, qdtype, w * (int64_t)d, k, v, kvdtype, key_off, n, d, scale, s, o, &l);
+            lse[w] = l;
+            double del = 0.0;
+            for (int32_t c = 0; c < d; ++c) del += load_elem(dout, dodtype, w * (int64_t)d + c) * o[c];
+            delta[w] = del;
+            double* dqi = dq + w * (int64_t)d;
+            for (int32_t c = 0; c < d; ++c) dqi[c] = 0.0;
+            for (int64_t a = 0; a < n; ++a) {
+                double dot = 0.0, dp = 0.0;
+                for (int32_t c = 0; c < d; ++c) {
+                    dot += load_elem(q, qdtype, w * (int64_t)d + c) * load_elem(k, kvdtype, key_off[a] + c);
+                    dp += load_elem(dout, dodtype, w * (int64_t)d + c) * load_elem(v, kvdtype, key_off[a] + c);
+                }
+                double p = exp(scale * dot - l);
+                double ds = p * (dp - del);
+                for (int32_t c = 0; c < d; ++c) dqi[c] += scale * ds * load_elem(k, kvdtype, key_off[a] + c);
+            }
+        }
+        free(s);
+        free(key_off);
+        free(o);
+    }
+    /* Pass 2: per (key row, KV head). */
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t w = 0; w < total * hkv; ++w) {
+        int64_t tj = w / hkv;
+        int32_t g = (int32_t)(w % hkv), b = seq_of[tj];
+        int64_t start = cu_seqlens[b], len = cu_seqlens[b + 1] - start, j = tj - start;
+        double* dkj = dk + w * (int64_t)d;
+        double* dvj = dv + w * (int64_t)d;
+        for (int32_t c = 0; c < d; ++c) dkj[c] = dvj[c] = 0.0;
+        for (int64_t i = 0; i < len; ++i) {
+            int64_t ti = start + i;
+            if (!allowed(i, j, window, span_lo[ti], span_hi[ti])) continue;
+            for (int32_t h = g * group; h < (g + 1) * group; ++h) {
+                int64_t qo = (ti * hq + h) * (int64_t)d, ko = w * (int64_t)d;
+                double dot = 0.0, dp = 0.0;
+                for (int32_t c = 0; c < d; ++c) {
+                    dot += load_elem(q, qdtype, qo + c) * load_elem(k, kvdtype, ko + c);
+                    dp += load_elem(dout, dodtype, qo + c) * load_elem(v, kvdtype, ko + c);
+                }
+                double p = exp(scale * dot - lse[ti * hq + h]);
+                double ds = p * (dp - delta[ti * hq + h]);
+                for (int32_t c = 0; c < d; ++c) {
+                    dkj[c] += scale * ds * load_elem(q, qdtype, qo + c);
+                    dvj[c] += p * load_elem(dout, dodtype, qo + c);
+                }
+            }
+        }
+    }
+    free(seq_of);
+    free(span_lo);
+    free(span_hi);
+    free(lse);
+    free(delta);
+    return 0;
+}
+
 /* Number of threads an OpenMP region of this library runs with. */
 int oracle_num_threads(int32_t threads) {
 #ifdef _OPENMP

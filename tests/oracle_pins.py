@@ -247,7 +247,75 @@ def pin_decode(lib=None):
         assert np.array_equal(oracle.decode(q, kc2, vc2, bt2, sl, window=w, lib=lib), o)
 
 
+# ------------------------------------------------------------------ backward
+def _loss(q, k, v, dout, cu, window, spans, lib):
+    """L = sum(dout * O) through the forward oracle (fp64 inputs)."""
+    o = oracle.prefill(q, k, v, cu, window=window, scale=0.4, spans=spans, lib=lib)
+    return float((dout * o).sum())
+
+
+def pin_backward_finite_differences(lib=None):
+    """Every entry of dq, dk, dv equals the central difference of
+    L = sum(dout * O) through the forward oracle (step 1e-5, fp64): the
+    gradient is fixed by the forward definition alone."""
+    rng = np.random.default_rng(41)
+    cu = [0, 5, 8]
+    spans = [[1, 4]]
+    q = rng.standard_normal((8, 2, 6))
+    k = rng.standard_normal((8, 1, 6))
+    v = rng.standard_normal((8, 1, 6))
+    dout = rng.standard_normal((8, 2, 6))
+    dq, dk, dv = oracle.prefill_backward(q, k, v, dout, cu, window=3, scale=0.4, spans=spans,
+                                         lib=lib)
+    eps = 1e-5
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + eps
+            up = _loss(q, k, v, dout, cu, 3, spans, lib)
+            x[idx] = old - eps
+            dn = _loss(q, k, v, dout, cu, 3, spans, lib)
+            x[idx] = old
+            num[idx] = (up - dn) / (2 * eps)
+        assert np.abs(num - g).max() <= 1e-7, np.abs(num - g).max()
+
+
+def pin_backward_single_key(lib=None):
+    """Window 1: every row sees only its own key, so p = 1 whatever the
+    scores: dq = dk = 0 exactly and dv of key j = the sum over the group's
+    query heads of dout at row j."""
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((9, 4, 5))
+    k = rng.standard_normal((9, 2, 5))
+    v = rng.standard_normal((9, 2, 5))
+    dout = rng.standard_normal((9, 4, 5))
+    dq, dk, dv = oracle.prefill_backward(q, k, v, dout, [0, 4, 9], window=1, lib=lib)
+    assert not dq.any() and not dk.any()
+    want = dout.reshape(9, 2, 2, 5).sum(axis=2)
+    assert np.abs(dv - want).max() <= 1e-15
+
+
+def pin_backward_gqa_is_mha_summed(lib=None):
+    """GQA with G query heads per KV head equals multi-head attention with
+    each K/V head repeated G times, the repeated heads' dk/dv summed."""
+    rng = np.random.default_rng(43)
+    cu = [0, 6, 11]
+    q = rng.standard_normal((11, 4, 6))
+    k = rng.standard_normal((11, 2, 6))
+    v = rng.standard_normal((11, 2, 6))
+    dout = rng.standard_normal((11, 4, 6))
+    dq, dk, dv = oracle.prefill_backward(q, k, v, dout, cu, window=4, lib=lib)
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    dq2, dk2, dv2 = oracle.prefill_backward(q, kr, vr, dout, cu, window=4, lib=lib)
+    assert np.abs(dq - dq2).max() <= 1e-12
+    assert np.abs(dk - dk2.reshape(11, 2, 2, 6).sum(axis=2)).max() <= 1e-12
+    assert np.abs(dv - dv2.reshape(11, 2, 2, 6).sum(axis=2)).max() <= 1e-12
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_rows_sum_to_one,
             pin_window_covering_sequence_is_global, pin_one_token_returns_v,
             pin_zero_query_is_mean, pin_dominant_key, pin_gqa_reduces_to_mha,
-            pin_packing_invariance, pin_row_subset, pin_decode]
+            pin_packing_invariance, pin_row_subset, pin_decode,
+            pin_backward_finite_differences, pin_backward_single_key,
+            pin_backward_gqa_is_mha_summed]

@@ -34,6 +34,13 @@ MUTANTS = [
      "if (!allowed(i, j, -1, -1, -1)) continue;"),
     ("transposed query/key offset", "load_elem(q, qt, q_off + c) * load_elem(k, kvt, key_off[a] + c)",
      "load_elem(q, qt, q_off + c) * load_elem(k, kvt, key_off[n - 1 - a] + c)"),
+    ("backward: ds sign", "double ds = p * (dp - del);", "double ds = p * (del - dp);"),
+    ("backward: dk misses scale", "dkj[c] += scale * ds *", "dkj[c] += ds *"),
+    ("backward: dv uses ds", "dvj[c] += p * load_elem(dout", "dvj[c] += ds * load_elem(dout"),
+    ("backward: delta from v", "del += load_elem(dout, dodtype, w * (int64_t)d + c) * o[c];",
+     "del += load_elem(dout, dodtype, w * (int64_t)d + c) * load_elem(v, kvdtype, c);"),
+    ("backward: dq uses q", "dqi[c] += scale * ds * load_elem(k, kvdtype, key_off[a] + c);",
+     "dqi[c] += scale * ds * load_elem(q, qdtype, w * (int64_t)d + c);"),
 ]
 
 
