@@ -179,6 +179,52 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                        void* stream);
 
 /*
+ * attn_prefill_varlen_backward -- gradients dq, dk, dv of
+ * attn_prefill_varlen for an upstream gradient dout = dL/do, with every sum
+ * in a fixed order and no atomics.
+ *
+ * Passages: the train/rollout goal includes the training step ("RFC:
+ * Gemma-4-31B-it train/rollout consistency", section 1); fixed fp32
+ * accumulators and orders, no split-K or cross-workgroup atomics (section 4,
+ * items 1 and 3).  Masks, spans and the GQA map are those of the forward.
+ *
+ * Arithmetic (fp32 FMAs; c = fl32(scale * log2 e)):
+ *   delta_i = sum_d dout_i[d] o_i[d]        (o: the forward's bf16 output)
+ *   p_ij    = exp2(fma(q_i.k_j, c, -fl32(lse_i * log2 e)))  (0 off the mask)
+ *   ds_ij   = p_ij (dout_i.v_j - delta_i)
+ *   dq_i    = scale * sum_j ds_ij k_j                 (keys ascending)
+ *   dk_j    = scale * sum_i sum_h ds_ij q_i           (rows ascending, then
+ *   dv_j    =         sum_i sum_h p_ij dout_i          the group's heads)
+ * Dot products run over the head dim in 32-element parts (fma chains,
+ * ascending), the parts added in a fixed butterfly.  Two kernels run on the
+ * stream: dq (and delta into the workspace), then dk and dv.
+ *
+ * Arguments (device pointers caller-owned):
+ *   q, k, v, o  bf16 as for attn_prefill_varlen (o = its output)
+ *   lse         fp32 [T, num_q_heads]: the forward's lse_opt output
+ *   dout        bf16 [T, num_q_heads, head_dim]
+ *   dq          fp32 [T, num_q_heads, head_dim] output
+ *   dk, dv      fp32 [T, num_kv_heads, head_dim] outputs
+ *   workspace   fp32 [total_tokens, num_q_heads] scratch (delta), 16-byte
+ *               aligned, contents need no initialisation
+ *   total_tokens  host value >= cu_seqlens[batch]
+ *   the rest as attn_prefill_varlen.
+ * Rows of tokens outside every sequence are not written.
+ * Errors: as attn_prefill_varlen.
+ */
+int attn_prefill_varlen_backward(const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse,
+                                 const void* dout, float* dq, float* dk,
+                                 float* dv, float* workspace,
+                                 int32_t total_tokens,
+                                 const int32_t* cu_seqlens, int32_t batch,
+                                 int32_t max_seqlen, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t window, float softmax_scale,
+                                 const int32_t* spans_opt, int32_t num_spans,
+                                 void* stream);
+
+/*
  * attn_decode_workspace_size -- bytes of fp32 workspace attn_decode_paged
  * needs for this batch: [batch, num_q_heads, ceil(max_seq_len /
  * ATTN_DECODE_CHUNK), head_dim + 4] fp32 (per chunk record: the unnormalised

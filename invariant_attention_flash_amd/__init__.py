@@ -9,6 +9,8 @@ built, or the GPU is missing, calls raise.
 Entry points (same names as the C ABI):
   attn_prefill_varlen  packed variable-length prefill, sliding or global,
                        GQA, optional bidirectional spans
+  attn_prefill_varlen_backward
+                       its gradients dq, dk, dv in a fixed order
   attn_prefill_paged   chunked prefill: new query tokens against the keys of
                        a paged KV cache (cached prefix plus the chunk)
   attn_decode_paged    one query token per sequence over a paged KV cache
@@ -20,7 +22,8 @@ import ctypes
 import json
 import os
 
-__all__ = ["attn_prefill_varlen", "attn_prefill_paged", "attn_decode_paged", "attn_decode_workspace_size",
+__all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_paged",
+           "attn_decode_paged", "attn_decode_workspace_size",
            "last_provenance", "last_error", "AttnError", "library", "LIB_PATH",
            "ATTN_WINDOW_NONE", "ATTN_DECODE_CHUNK", "ERROR_CODES", "EXPORTS"]
 
@@ -29,7 +32,8 @@ ATTN_WINDOW_NONE = -1
 ATTN_DECODE_CHUNK = 512
 ERROR_CODES = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
                4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP", 7: "ATTN_E_VALIDATE"}
-EXPORTS = ["attn_prefill_varlen", "attn_prefill_paged", "attn_decode_workspace_size", "attn_decode_paged",
+EXPORTS = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_paged",
+           "attn_decode_workspace_size", "attn_decode_paged",
            "attn_last_error", "attn_last_provenance", "attn_version"]
 
 
@@ -58,6 +62,10 @@ def library():
         lib.attn_prefill_paged.restype = ctypes.c_int
         lib.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            i32, i32, i32, i32, i32, i32, f32, vp]
+        lib.attn_prefill_varlen_backward.restype = ctypes.c_int
+        lib.attn_prefill_varlen_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                     vp, i32, i32, i32, i32, i32, i32, f32, vp,
+                                                     i32, vp]
         lib.attn_decode_workspace_size.restype = sz
         lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
         lib.attn_decode_paged.restype = ctypes.c_int
@@ -155,6 +163,63 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, window=ATTN_WINDOW_NONE
         float(softmax_scale), _ptr(spans), ns, _stream(stream))
     _check(rc)
     return out
+
+
+def attn_prefill_varlen_backward(q, k, v, out, lse, dout, cu_seqlens, max_seqlen,
+                                 window=ATTN_WINDOW_NONE, softmax_scale=None, spans=None,
+                                 dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients of attn_prefill_varlen.
+
+    q, k, v, cu_seqlens, max_seqlen, window, softmax_scale, spans as for the
+    forward; out bf16 [T, Hq, D] and lse fp32 [T, Hq] are the forward's
+    outputs; dout bf16 [T, Hq, D] the upstream gradient.  dq fp32 [T, Hq, D],
+    dk/dv fp32 [T, Hkv, D] and workspace fp32 [T, Hq] are allocated if None.
+    Returns (dq, dk, dv).
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _require(t, n, torch.bfloat16, 3)
+    _require(lse, "lse", torch.float32, 2)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != v.shape or k.shape[0] != T or k.shape[2] != d:
+        raise ValueError("k and v must be [T, Hkv, D] matching q")
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must be [T, Hq, D] matching q")
+    if tuple(lse.shape) != (T, hq):
+        raise ValueError("lse must be [T, Hq]")
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty((T, hq), dtype=torch.float32, device=q.device)
+    _require(dq, "dq", torch.float32, 3)
+    _require(dk, "dk", torch.float32, 3)
+    _require(dv, "dv", torch.float32, 3)
+    _require(workspace, "workspace", torch.float32)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape:
+        raise ValueError("dq must match q and dk, dv must match k")
+    if workspace.numel() < T * hq:
+        raise ValueError("workspace must hold T * Hq floats")
+    ns = 0
+    if spans is not None:
+        _require(spans, "spans", torch.int32, 2)
+        ns = spans.shape[0]
+        if ns == 0:
+            spans = None
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    rc = library().attn_prefill_varlen_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(workspace), T, _ptr(cu_seqlens), cu_seqlens.shape[0] - 1,
+        int(max_seqlen), hq, hkv, d, int(window), float(softmax_scale), _ptr(spans), ns,
+        _stream(stream))
+    _check(rc)
+    return dq, dk, dv
 
 
 def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens, q_start, max_query_len,

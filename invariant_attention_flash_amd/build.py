@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libinvattn.so")
 SOURCES = ["api.hip", "prefill.hip", "prefill_split.hip", "prefill_ws.hip", "prefill_wide.hip",
-           "decode.hip"]
+           "decode.hip", "backward.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

@@ -317,6 +317,79 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, 
   return ATTN_OK;
 }
 
+int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, float* dq, float* dk,
+                                 float* dv, float* workspace, int32_t total_tokens,
+                                 const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t window, float softmax_scale, const int32_t* spans_opt,
+                                 int32_t num_spans, void* stream) {
+  g_err.clear();
+  if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
+  if (max_seqlen < 0) return fail(ATTN_E_SHAPE, "max_seqlen=%d must be >= 0", max_seqlen);
+  if (total_tokens < 0) return fail(ATTN_E_SHAPE, "total_tokens=%d must be >= 0", total_tokens);
+  if (num_spans < 0) return fail(ATTN_E_SHAPE, "num_spans=%d must be >= 0", num_spans);
+  int rc = check_heads(num_q_heads, num_kv_heads, head_dim, window, softmax_scale);
+  if (rc != ATTN_OK) return rc;
+  if (batch > 65535) return fail(ATTN_E_UNSUPPORTED, "batch=%d exceeds 65535", batch);
+  const int rows = backward_rows_per_tile(head_dim);
+  char sid[96];
+  snprintf(sid, sizeof sid, "backward_d%d_rows%d_t256_fp32fma", head_dim, rows);
+  if (batch == 0 || max_seqlen == 0) {
+    set_provenance("attn_prefill_varlen_backward", "none (empty input)", sid, "none", window,
+                   head_dim, num_q_heads, num_kv_heads, batch, 0);
+    return ATTN_OK;
+  }
+  if (!q) return fail(ATTN_E_NULL, "q is NULL");
+  if (!k) return fail(ATTN_E_NULL, "k is NULL");
+  if (!v) return fail(ATTN_E_NULL, "v is NULL");
+  if (!o) return fail(ATTN_E_NULL, "o is NULL");
+  if (!lse) return fail(ATTN_E_NULL, "lse is NULL");
+  if (!dout) return fail(ATTN_E_NULL, "dout is NULL");
+  if (!dq) return fail(ATTN_E_NULL, "dq is NULL");
+  if (!dk) return fail(ATTN_E_NULL, "dk is NULL");
+  if (!dv) return fail(ATTN_E_NULL, "dv is NULL");
+  if (!workspace) return fail(ATTN_E_NULL, "workspace is NULL");
+  if (!cu_seqlens) return fail(ATTN_E_NULL, "cu_seqlens is NULL");
+  if (num_spans > 0 && !spans_opt) return fail(ATTN_E_NULL, "spans_opt is NULL with num_spans=%d", num_spans);
+  const void* a16[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+  const char* n16[] = {"q", "k", "v", "o", "dout", "dq", "dk", "dv", "workspace"};
+  for (int i = 0; i < 9; ++i)
+    if (!aligned16(a16[i])) return fail(ATTN_E_ALIGN, "%s is not 16-byte aligned", n16[i]);
+  if (!aligned4(lse)) return fail(ATTN_E_ALIGN, "lse is not 4-byte aligned");
+  if (!aligned4(cu_seqlens)) return fail(ATTN_E_ALIGN, "cu_seqlens is not 4-byte aligned");
+  if (spans_opt && !aligned4(spans_opt)) return fail(ATTN_E_ALIGN, "spans_opt is not 4-byte aligned");
+  const long long tiles = ((long long)max_seqlen + rows - 1) / rows;
+  if (tiles > 0x7fffffffLL) return fail(ATTN_E_UNSUPPORTED, "max_seqlen=%d too large", max_seqlen);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  long long tokens = -1;
+  if (validate_enabled()) {
+    std::vector<int32_t> cu;
+    if ((rc = fetch_ints(cu_seqlens, (size_t)batch + 1, cu, s, "copy cu_seqlens")) != ATTN_OK) return rc;
+    if (cu[0] != 0) return fail(ATTN_E_VALIDATE, "cu_seqlens[0]=%d must be 0", cu[0]);
+    for (int b = 0; b < batch; ++b) {
+      const int len = cu[b + 1] - cu[b];
+      if (len < 0) return fail(ATTN_E_VALIDATE, "cu_seqlens decreases at %d", b);
+      if (len > max_seqlen)
+        return fail(ATTN_E_VALIDATE, "sequence %d has length %d > max_seqlen=%d", b, len, max_seqlen);
+    }
+    if (cu[batch] > total_tokens)
+      return fail(ATTN_E_VALIDATE, "cu_seqlens[batch]=%d > total_tokens=%d", cu[batch], total_tokens);
+    tokens = cu[batch];
+  }
+
+  BackwardArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, spans_opt, num_spans,
+                 batch, max_seqlen, num_q_heads, num_kv_heads, head_dim, window, softmax_scale,
+                 fold_scale(softmax_scale)};
+  hipError_t e = launch_backward(a, s);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  set_provenance("attn_prefill_varlen_backward", "bwd_dq_kernel+bwd_dkv_kernel", sid,
+                 "none (one ascending walk per row and per key)", window, head_dim, num_q_heads,
+                 num_kv_heads, batch, tokens);
+  return ATTN_OK;
+}
+
 size_t attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_q_heads,
                                   int32_t head_dim) {
   if (batch <= 0 || max_seq_len <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;

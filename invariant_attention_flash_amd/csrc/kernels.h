@@ -106,6 +106,34 @@ hipError_t launch_prefill_split(const PrefillArgs& a, hipStream_t stream);
 bool prefill_ws_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream);
 
+// Attention backward (backward.hip): dq and delta (one kernel), then dk and
+// dv (a second kernel reading delta), on the caller's stream.
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;  // [T, hq] scratch
+  const int32_t* cu_seqlens;
+  const int32_t* spans;
+  int32_t num_spans;
+  int32_t batch;
+  int32_t max_seqlen;
+  int32_t hq;
+  int32_t hkv;
+  int32_t d;
+  int32_t window;
+  float scale;
+  float c2;  // fl32(scale * log2(e))
+};
+int backward_rows_per_tile(int d);
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+
 constexpr int kDecodeChunk = 512;  // keys per split chunk (fixed; ATTN_DECODE_CHUNK)
 constexpr int kDecodeStage = 16;   // keys per pipeline stage inside a chunk (one cache block)
 constexpr int decode_record_floats(int d) { return d + 4; }  // acc[d], m, l, pad

@@ -131,6 +131,11 @@ def prefill_case(seed, lengths, hq, hkv, d, window, std=0.5, spans=None, name=""
     return PrefillCase(seqs, hq, hkv, d, window, 1.0 / float(np.sqrt(d)), name)
 
 
+def upstream_grad(seed, shape, std=0.5) -> np.ndarray:
+    """Seeded upstream gradient dL/dO for the backward (bf16 bits, normal)."""
+    return _normal_bf16(np.random.default_rng([seed, 7777]), shape, std)
+
+
 def tiny_case(seed=1, window=32):
     """One sequence of 128 tokens, 4 query / 2 KV heads, head dim 64, fp32
     N(0,1) inputs; the kernel consumes their bf16 rounding."""

@@ -192,3 +192,62 @@ def test_prefill_paged_empty_input_needs_no_pointers():
     rc, msg = call_prefill_paged(q=None, kc=None, vc=None, o=None, cu=None, qs=None, bt=None,
                                  mql=0)
     assert rc == 0, msg
+
+
+def call_backward(**kw):
+    a = dict(q=1 << 20, k=1 << 20, v=1 << 20, o=1 << 20, lse=1 << 20, do=1 << 20, dq=1 << 20,
+             dk=1 << 20, dv=1 << 20, ws=1 << 20, tt=32, cu=1 << 20, batch=2, max_seqlen=16,
+             hq=4, hkv=2, d=64, window=-1, scale=0.125, spans=None, ns=0)
+    a.update(kw)
+    ptr = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = ia.library().attn_prefill_varlen_backward(
+        ptr(a["q"]), ptr(a["k"]), ptr(a["v"]), ptr(a["o"]), ptr(a["lse"]), ptr(a["do"]),
+        ptr(a["dq"]), ptr(a["dk"]), ptr(a["dv"]), ptr(a["ws"]), a["tt"], ptr(a["cu"]),
+        a["batch"], a["max_seqlen"], a["hq"], a["hkv"], a["d"], a["window"], a["scale"],
+        ptr(a["spans"]), a["ns"], None)
+    return rc, ia.last_error()
+
+
+BACKWARD_ERRORS = [
+    (dict(q=None), "ATTN_E_NULL", "q is NULL"),
+    (dict(k=None), "ATTN_E_NULL", "k is NULL"),
+    (dict(v=None), "ATTN_E_NULL", "v is NULL"),
+    (dict(o=None), "ATTN_E_NULL", "o is NULL"),
+    (dict(lse=None), "ATTN_E_NULL", "lse is NULL"),
+    (dict(do=None), "ATTN_E_NULL", "dout is NULL"),
+    (dict(dq=None), "ATTN_E_NULL", "dq is NULL"),
+    (dict(dk=None), "ATTN_E_NULL", "dk is NULL"),
+    (dict(dv=None), "ATTN_E_NULL", "dv is NULL"),
+    (dict(ws=None), "ATTN_E_NULL", "workspace is NULL"),
+    (dict(cu=None), "ATTN_E_NULL", "cu_seqlens"),
+    (dict(ns=1, spans=None), "ATTN_E_NULL", "spans_opt"),
+    (dict(batch=-1), "ATTN_E_SHAPE", "batch"),
+    (dict(max_seqlen=-1), "ATTN_E_SHAPE", "max_seqlen"),
+    (dict(tt=-1), "ATTN_E_SHAPE", "total_tokens"),
+    (dict(ns=-1), "ATTN_E_SHAPE", "num_spans"),
+    (dict(hq=6, hkv=4), "ATTN_E_SHAPE", "multiple"),
+    (dict(d=128), "ATTN_E_UNSUPPORTED", "head_dim"),
+    (dict(window=0), "ATTN_E_UNSUPPORTED", "window"),
+    (dict(scale=float("nan")), "ATTN_E_UNSUPPORTED", "softmax_scale"),
+    (dict(batch=70000), "ATTN_E_UNSUPPORTED", "65535"),
+    (dict(dk=(1 << 20) + 4), "ATTN_E_ALIGN", "dk is not 16-byte"),
+    (dict(ws=(1 << 20) + 4), "ATTN_E_ALIGN", "workspace is not 16-byte"),
+    (dict(lse=(1 << 20) + 2), "ATTN_E_ALIGN", "lse is not 4-byte"),
+]
+
+
+@pytest.mark.parametrize("kw,code,text", BACKWARD_ERRORS,
+                         ids=[c[2] + str(i) for i, c in enumerate(BACKWARD_ERRORS)])
+def test_backward_rejects(kw, code, text):
+    rc, msg = call_backward(**kw)
+    assert ia.ERROR_CODES[rc] == code, (rc, msg)
+    assert text in msg
+
+
+def test_backward_empty_input_needs_no_pointers():
+    none = dict(q=None, k=None, v=None, o=None, lse=None, do=None, dq=None, dk=None, dv=None,
+                ws=None, cu=None)
+    rc, msg = call_backward(batch=0, **none)
+    assert rc == 0, msg
+    rc, msg = call_backward(max_seqlen=0, **none)
+    assert rc == 0, msg
