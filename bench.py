@@ -11,7 +11,8 @@ Printed: one JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
 (4 * head_dim * query_heads * allowed query-key pairs, masked work not
 counted) over its HIP-event-timed launches; the decode's algorithmic HBM GB/s
 (K and V of every attended context token, plus q, o and block-table reads) is
-reported beside it with its own roofline.  The fp64 CPU oracle is timed on a
+reported beside it with its own roofline, and the backward (dq, dk, dv) of
+the same prefill in a timed region of its own.  The fp64 CPU oracle is timed on a
 bounded sample of the same prefill rows on the host cores (reported baseline,
 not a target), and its outputs double as a parity spot-check.
 """
@@ -98,6 +99,12 @@ def load_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
+# The backward's two kernels form their five products (and the recomputed
+# scores and dP) as bf16 MFMAs, so their roofline is the bf16 matrix peak.
+BACKWARD_BOUND = "mfma"
+BACKWARD_PEAK = PEAK_BF16_TFLOPS
+BACKWARD_KERNEL_LABEL = "bwd_dq_kernel<256> + bwd_dkv_kernel<256> (one launch pair)"
+
 CALIBRATION_BYTES = 1 << 30   # plain streaming kernel used to scale the HBM byte counters
 
 
@@ -150,6 +157,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--backward-steps", type=int, default=3,
+                    help="timed calls of the backward on the prefill workload (0 disables)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables)")
     ap.add_argument("--calibrate", action="store_true",
@@ -235,6 +244,47 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     pf_tflops = flops / (pf_ms * 1e-3) / 1e12
+
+    # ---------------- backward of the same prefill (its own timed region,
+    # not part of the step): dq, dk, dv for a seeded upstream gradient
+    bw = None
+    if args.backward_steps > 0:
+        lse = torch.empty(pf["q"].shape[:2], dtype=torch.float32, device=dev)
+        ia.attn_prefill_varlen(pf["q"], pf["k"], pf["v"], pf["cu_seqlens"], pf["max_seqlen"],
+                               window=W, softmax_scale=pf["scale"], out=pf_out, lse=lse)
+        g = torch.from_numpy(synth.upstream_grad(2, tuple(pf["q"].shape)).view(np.int16))
+        dout = g.view(torch.bfloat16).to(dev)
+        dq = torch.empty(pf["q"].shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(pf["k"].shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(pf["k"].shape, dtype=torch.float32, device=dev)
+        bws = torch.empty(pf["q"].shape[:2], dtype=torch.float32, device=dev)
+
+        def backward():
+            ia.attn_prefill_varlen_backward(pf["q"], pf["k"], pf["v"], pf_out, lse, dout,
+                                            pf["cu_seqlens"], pf["max_seqlen"], window=W,
+                                            softmax_scale=pf["scale"], dq=dq, dk=dk, dv=dv,
+                                            workspace=bws)
+
+        backward()
+        torch.cuda.synchronize()
+        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.backward_steps)]
+        for e in bev:
+            e[0].record(stream)
+            backward()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        bw_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in bev]))
+        bw_flops = 2.5 * flops   # five products of D per allowed pair and head
+        bw_tf = bw_flops / (bw_ms * 1e-3) / 1e12
+        bw = {"value": bw_tf, "unit": "TFLOP/s", "calls": args.backward_steps,
+              "roofline": {"bound": BACKWARD_BOUND, "achieved": bw_tf, "peak": BACKWARD_PEAK,
+                           "unit": "TFLOP/s", "frac": bw_tf / BACKWARD_PEAK, "traffic": None,
+                           "kernel": BACKWARD_KERNEL_LABEL,
+                           "work_per_launch": f"{bw_flops:.4g} FLOP = 10*256*32*{pairs} "
+                                              "allowed pairs (dq, dk, dv of the prefill)",
+                           "avg_launch_ms": bw_ms}}
+        del dq, dk, dv, bws, dout, lse
     dc_gbs = dbytes / (dc_ms * 1e-3) / 1e9
 
     # ---------------- CPU oracle baseline + parity spot-check on sampled rows
@@ -309,6 +359,7 @@ def main():
         "roofline": pf_roof,
         "decode": {"value": dc_gbs, "unit": "GB/s", "roofline": dc_roof,
                    "context_tokens": int(sum(dlen))},
+        "backward": bw,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "kernel_sources": kernel_sources_hash(),

@@ -1,28 +1,37 @@
 // backward.hip -- deterministic attention backward (dq, dk, dv) for packed
-// variable-length prefill, with every sum in a fixed order and no atomics.
+// variable-length prefill on the matrix cores, with every sum in a fixed
+// order and no atomics.
 //
 // Sources: the train/rollout consistency goal covers the training step
 // ("RFC: Gemma-4-31B-it train/rollout consistency", section 1 and section 4
 // item 1: every reduction has a declared fp32 accumulator and a fixed order;
 // item 3: no split-K, Stream-K or cross-workgroup atomics); the gradient is
 // the chain rule on the forward's definition (same masks, spans and GQA map
-// as prefill.hip).
+// as the prefill kernels).
 //
-// Arithmetic (fp32 FMAs throughout; c = fl32(scale * log2 e), and the
-// forward's natural-log LSE enters as lse2 = fl32(lse * log2 e)):
-//   delta_i = sum_d dout[i,d] * o[i,d]         (o: the forward's bf16 output)
-//   s_ij    = sum_d q[i,d] * k[j,d]             dp_ij = sum_d dout[i,d] * v[j,d]
-//   p_ij    = exp2(fma(s_ij, c, -lse2_i))       (0 where the mask excludes j)
+// Arithmetic (c = fl32(scale * log2 e); the forward's natural-log LSE enters
+// as lse2 = fl32(lse * log2 e)):
+//   s_ij, dp_ij, delta_i  bf16 MFMA dot products (fp32 accumulation) of
+//           q_i.k_j, v_j.dout_i and o_i.dout_i (o: the forward's bf16 output;
+//           delta by the same MFMA sequence as dp)
+//   p_ij    = exp2(fma(s_ij, c, -lse2_i))   (0 where the mask excludes j)
 //   ds_ij   = p_ij * (dp_ij - delta_i)
-//   dq_i    = scale * sum_j ds_ij k_j           (keys ascending)
-//   dk_j    = scale * sum_i sum_h ds_ij q_i     (rows ascending, then the
-//   dv_j    =         sum_i sum_h p_ij dout_i    group's query heads ascending)
-// Each dot product runs over the head dim in 32-element parts (fma chain,
-// ascending), the parts added by a fixed butterfly.  A thread owns 32
-// head-dim elements of one row (dq kernel) or one key (dk/dv kernel); the
-// D/32 threads of a row or key are adjacent lanes.  Every output element is
-// written once, by one thread, so the result does not depend on the batch,
-// the packing or the launch geometry.
+//   dq_i    = scale * sum_j bf16(ds_ij) k_j          32 keys per MFMA, key
+//                                                    tiles ascending
+//   dk_j    = scale * sum_(i,h) bf16(ds_ij) q_(i,h)  32 (row, head) pairs per
+//   dv_j    =         sum_(i,h) bf16(p_ij) dout_(i,h) MFMA: rows ascending, then
+//                                                    the group's heads
+// A tile's keys (or pairs) start at a position fixed by the row (or key)
+// tile alone, and every output element is written once by one lane, so the
+// result does not depend on the batch, the packing or the grid.
+//
+// MFMA operand layout (v_mfma_f32_16x16x32_bf16): lane l = 16*g + x supplies
+// A[x][8g..8g+7] and B[8g..8g+7][x] and receives D[4g..4g+3][x].  Scores come
+// out as S^T (keys in M, rows in N), so lane (g, x) holds keys 4g+i and
+// 16+4g+i of row x.  Those eight values are the lane's B operand of the
+// gradient products as they stand: k-slot j stands for key 16*(j/4) + 4g +
+// j%4, and the A operand (K, Q or dout transposed) is read from LDS in the
+// same key order with transpose reads.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -30,51 +39,60 @@ namespace invattn {
 
 namespace {
 
-constexpr int kBwdThreads = 256;
-constexpr int kPart = 32;  // head-dim elements per thread
+constexpr int kBwdThreads = 256;   // four waves
+constexpr int kBwdRows = 64;       // rows (dq) or keys (dk, dv) per workgroup: 16 per wave
+constexpr int kBwdTile = 32;       // keys (dq) or (row, head) pairs (dk, dv) per step
 
 template <int D>
 struct BwdCfg {
-  static constexpr int P = D / kPart;               // threads per row / key
-  static constexpr int kRows = kBwdThreads / P;     // rows (keys) per workgroup
-  // LDS staging: 64 KB of fp32 per chunk.
-  static constexpr int kKeyChunk = 65536 / (D * 4 * 2);  // keys per chunk (K and V)
-  static_assert(D % kPart == 0 && P <= 64 && (P & (P - 1)) == 0, "part map");
+  static constexpr int kSt = D / 32;     // k-steps over the head dim
+  static constexpr int kDb = D / 16;     // 16-column blocks of the head dim
+  static constexpr int kLd = D + 8;      // LDS row stride in bf16 (16 bytes of padding)
+  static constexpr int kChunks = kBwdTile * D / 8;   // 16-byte chunks per staged tile
+  static_assert(D % 32 == 0, "head dim in MFMA k-steps");
 };
-
-// Sum over the P adjacent lanes of a row (butterfly: every lane ends with
-// the same value, the additions in the same order).
-template <int P>
-__device__ __forceinline__ float part_sum(float x) {
-#pragma unroll
-  for (int m = P / 2; m >= 1; m >>= 1) x = x + __shfl_xor(x, m);
-  return x;
-}
-
-__device__ __forceinline__ void load_part(const bf16* __restrict__ src, float* dst) {
-#pragma unroll
-  for (int c = 0; c < kPart; c += 8) {
-    const bf16x8 x = ld_global_x8(src + c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dst[c + e] = (float)x[e];
-  }
-}
-
-__device__ __forceinline__ float dot_part(const float* a, const float* b) {
-  float s = a[0] * b[0];
-#pragma unroll
-  for (int c = 1; c < kPart; ++c) s = __builtin_fmaf(a[c], b[c], s);
-  return s;
-}
 
 __device__ __forceinline__ bool admits(int i, int j, int window, int ss, int se) {
   const bool causal = j <= i && (window < 0 || i - j < window);
   return causal || (j >= ss && j < se);
 }
 
-// dq of a tile of rows of one query head, and delta of those rows.
+__device__ __forceinline__ void st_lds_x8(bf16* p, bf16x8 x) {
+  *reinterpret_cast<bf16x8*>(p) = x;
+}
+
+// A operand of the gradient products: X^T for 16 columns [c0, c0 + 16) of
+// a staged [32][kLd] tile, k-slot j <-> tile row 16*(j/4) + 4g + j%4.  Lane
+// 4a + c of a 16-lane group receives element c of the rows addressed by
+// lanes a + 4r; lane m therefore addresses row 4g + m/4 at column c0 +
+// 4*(m%4) (plus 16 rows for k-slots 4..7).
+template <int LD>
+__device__ __forceinline__ bf16x8 lds_t_operand(const bf16* tile, int c0, int g, int x) {
+  const bf16* p = tile + (4 * g + x / 4) * LD + c0 + 4 * (x % 4);
+  return cat8(ld_lds_tr(p), ld_lds_tr(p + 16 * LD));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4& lo, const f32x4& hi) {
+  return bf16x8{to_bf16(lo[0]), to_bf16(lo[1]), to_bf16(lo[2]), to_bf16(lo[3]),
+                to_bf16(hi[0]), to_bf16(hi[1]), to_bf16(hi[2]), to_bf16(hi[3])};
+}
+
+// Stage rows [0, 32) of a tile: row r comes from src(r) (nullptr: zeros).
+template <int D, class Src>
+__device__ __forceinline__ void stage_tile(bf16* tile, Src src, int tid) {
+  using C = BwdCfg<D>;
+#pragma unroll
+  for (int e = tid; e < C::kChunks; e += kBwdThreads) {
+    const int r = e / (D / 8), c = 8 * (e % (D / 8));
+    const bf16* s = src(r);
+    const bf16x8 x = s ? ld_global_x8(s + c) : bf16x8{};
+    st_lds_x8(tile + r * C::kLd + c, x);
+  }
+}
+
+// dq of 64 rows of one query head, and delta of those rows.
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads)))
+__global__ __launch_bounds__(kBwdThreads)
 void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const bf16* __restrict__ v, const bf16* __restrict__ o,
                    const float* __restrict__ lse, const bf16* __restrict__ dout,
@@ -82,32 +100,39 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ spans,
                    int num_spans, int hq, int hkv, int window, float scale, float c2) {
   using C = BwdCfg<D>;
-  constexpr int P = C::P, KC = C::kKeyChunk;
-  __shared__ __attribute__((aligned(16))) float kv[2][KC][D];
-  const int b = blockIdx.z, h = blockIdx.y, g = h / (hq / hkv);
+  __shared__ __attribute__((aligned(16))) bf16 kt[kBwdTile * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 vt[kBwdTile * C::kLd];
+  const int b = blockIdx.z, h = blockIdx.y, kvh = h / (hq / hkv);
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
-  const int r0 = blockIdx.x * C::kRows;
+  const int r0 = blockIdx.x * kBwdRows;
   if (r0 >= L) return;
-  const int r1 = min(r0 + C::kRows, L);
-  const int tid = threadIdx.x, part = tid % P;
-  const int i = r0 + tid / P;
+  const int r1 = min(r0 + kBwdRows, L);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int x = lane & 15, g = lane >> 4;
+  const int i = r0 + 16 * w + x;
   const bool live = i < r1;
-  const int ic = live ? i : r0;  // rows past the tile load row r0 and store nothing
-  const size_t qo = ((size_t)(seq0 + ic) * hq + h) * D + part * kPart;
+  const int ic = live ? i : r0;   // rows past the tile compute on row r0 and store nothing
+  const size_t qo = ((size_t)(seq0 + ic) * hq + h) * D;
 
-  float qv[kPart], dov[kPart], acc[kPart];
-  load_part(q + qo, qv);
-  load_part(dout + qo, dov);
-  float del;
-  {
-    float ov[kPart];
-    load_part(o + qo, ov);
-    del = part_sum<P>(dot_part(dov, ov));
-  }
-  if (live && part == 0) delta[(size_t)(seq0 + i) * hq + h] = del;
-  const float lse2 = lse[(size_t)(seq0 + ic) * hq + h] * 1.4426950408889634f;
+  // Q and dout as B operands (B[d][row]): lane (g, x) holds d = 32st + 8g + 0..7.
+  // delta is the diagonal of O dout^T, formed by the same MFMA sequence as
+  // dP^T = V dout^T (A: the row of O or V, B: dout), so that dp_ij equals
+  // delta_i bit for bit when v_j = o_i.
+  bf16x8 qop[C::kSt], dop[C::kSt];
+  f32x4 dd = f32x4{};
 #pragma unroll
-  for (int c = 0; c < kPart; ++c) acc[c] = 0.f;
+  for (int st = 0; st < C::kSt; ++st) {
+    qop[st] = ld_global_x8(q + qo + 32 * st + 8 * g);
+    dop[st] = ld_global_x8(dout + qo + 32 * st + 8 * g);
+    dd = mfma16(ld_global_x8(o + qo + 32 * st + 8 * g), dop[st], dd);
+  }
+  // D[m][x] sits in lane 16*(m/4) + x, element m%4: the diagonal of row x in
+  // lane 16*(x/4) + x, element x%4.
+  const int dsrc = 16 * (x >> 2) + x;
+  const float dsel = (x & 3) == 0 ? dd[0] : (x & 3) == 1 ? dd[1] : (x & 3) == 2 ? dd[2] : dd[3];
+  const float del = __shfl(dsel, dsrc);
+  if (live && g == 0) delta[(size_t)(seq0 + i) * hq + h] = del;
+  const float lse2 = lse[(size_t)(seq0 + ic) * hq + h] * 1.4426950408889634f;
 
   int ss = 0, se = 0, s0, e0;
   if (num_spans > 0 && find_span(spans, num_spans, seq0 + ic, s0, e0)) {
@@ -115,61 +140,73 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     se = e0 - seq0;
   }
   // Keys of the tile's rows: the window below its first row, the span of its
-  // first row, its last row, the span of its last row.
+  // first row, up to its last row or the span of its last row.
   int lo = window > 0 ? max(0, r0 - window + 1) : 0;
   int hi = r1;
   if (num_spans > 0) {
     if (find_span(spans, num_spans, seq0 + r0, s0, e0)) lo = min(lo, max(s0 - seq0, 0));
     if (find_span(spans, num_spans, seq0 + r1 - 1, s0, e0)) hi = max(hi, min(e0 - seq0, L));
   }
-  for (int j0 = lo; j0 < hi; j0 += KC) {
-    const int n = min(KC, hi - j0);
-    __syncthreads();
-    for (int e = tid * 8; e < n * D; e += kBwdThreads * 8) {
-      const int jj = e / D, c = e % D;
-      const size_t ko = ((size_t)(seq0 + j0 + jj) * hkv + g) * D + c;
-      const bf16x8 xk = ld_global_x8(k + ko), xv = ld_global_x8(v + ko);
+
+  f32x4 acc[C::kDb];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        kv[0][jj][c + u] = (float)xk[u];
-        kv[1][jj][c + u] = (float)xv[u];
+  for (int db = 0; db < C::kDb; ++db) acc[db] = f32x4{};
+
+  for (int k0 = lo; k0 < hi; k0 += kBwdTile) {
+    __syncthreads();
+    stage_tile<D>(kt, [&](int r) -> const bf16* {
+      return k0 + r < hi ? k + ((size_t)(seq0 + k0 + r) * hkv + kvh) * D : nullptr;
+    }, tid);
+    stage_tile<D>(vt, [&](int r) -> const bf16* {
+      return k0 + r < hi ? v + ((size_t)(seq0 + k0 + r) * hkv + kvh) * D : nullptr;
+    }, tid);
+    __syncthreads();
+    // S^T and dP^T: keys 16kb + 4g + e of row x.
+    f32x4 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int st = 0; st < C::kSt; ++st) {
+        const bf16x8 ka = ld_lds_x8(kt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
+        const bf16x8 va = ld_lds_x8(vt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
+        s[kb] = mfma16(ka, qop[st], st == 0 ? f32x4{} : s[kb]);
+        dp[kb] = mfma16(va, dop[st], st == 0 ? f32x4{} : dp[kb]);
       }
     }
-    __syncthreads();
-    for (int jj = 0; jj < n; ++jj) {
-      const float* kr = &kv[0][jj][part * kPart];
-      const float* vr = &kv[1][jj][part * kPart];
-      float kp[kPart], vp[kPart];
+    f32x4 ds[2];
 #pragma unroll
-      for (int c = 0; c < kPart; ++c) {
-        kp[c] = kr[c];
-        vp[c] = vr[c];
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = k0 + 16 * kb + 4 * g + e;
+        const float p = admits(ic, j, window, ss, se) && j < hi
+                            ? fast_exp2(__builtin_fmaf(s[kb][e], c2, -lse2))
+                            : 0.f;
+        ds[kb][e] = p * (dp[kb][e] - del);
       }
-      const float s = part_sum<P>(dot_part(qv, kp));
-      const float dp = part_sum<P>(dot_part(dov, vp));
-      const int j = j0 + jj;
-      const float p = admits(ic, j, window, ss, se) ? fast_exp2(__builtin_fmaf(s, c2, -lse2)) : 0.f;
-      const float ds = p * (dp - del);
-#pragma unroll
-      for (int c = 0; c < kPart; ++c) acc[c] = __builtin_fmaf(ds, kp[c], acc[c]);
     }
+    const bf16x8 dsb = pack8(ds[0], ds[1]);
+    // dQ^T[d][row] += K^T[d][key] dS^T[key][row]
+#pragma unroll
+    for (int db = 0; db < C::kDb; ++db)
+      acc[db] = mfma16(lds_t_operand<C::kLd>(kt, 16 * db, g, x), dsb, acc[db]);
   }
   if (!live) return;
   float* out = dq + qo;
 #pragma unroll
-  for (int c = 0; c < kPart; c += 4) {
-    float4 w;
-    w.x = acc[c] * scale;
-    w.y = acc[c + 1] * scale;
-    w.z = acc[c + 2] * scale;
-    w.w = acc[c + 3] * scale;
-    *reinterpret_cast<float4*>(out + c) = w;
+  for (int db = 0; db < C::kDb; ++db) {
+    float4 wv;
+    wv.x = acc[db][0] * scale;
+    wv.y = acc[db][1] * scale;
+    wv.z = acc[db][2] * scale;
+    wv.w = acc[db][3] * scale;
+    *reinterpret_cast<float4*>(out + 16 * db + 4 * g) = wv;
   }
 }
 
-// dk and dv of a tile of keys of one KV head.
+// dk and dv of 64 keys of one KV head.
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kBwdThreads, kBwdThreads)))
+__global__ __launch_bounds__(kBwdThreads)
 void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ v, const float* __restrict__ lse,
                     const bf16* __restrict__ dout, const float* __restrict__ delta,
@@ -177,28 +214,34 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ spans,
                     int num_spans, int hq, int hkv, int window, float scale, float c2) {
   using C = BwdCfg<D>;
-  constexpr int P = C::P;
-  constexpr int kStage = 65536 / (D * 4 * 2);  // (row, head) pairs staged per chunk
-  __shared__ __attribute__((aligned(16))) float qd[2][kStage][D];
-  __shared__ float rl[kStage][2];     // lse2, delta
-  __shared__ int rs[kStage][3];       // row, span start, span end
-  const int b = blockIdx.z, g = blockIdx.y, G = hq / hkv;
+  __shared__ __attribute__((aligned(16))) bf16 qt[kBwdTile * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 dt[kBwdTile * C::kLd];
+  __shared__ float plse[kBwdTile], pdel[kBwdTile];
+  __shared__ int prow[kBwdTile], pss[kBwdTile], pse[kBwdTile];
+  const int b = blockIdx.z, kvh = blockIdx.y, G = hq / hkv;
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
-  const int j0 = blockIdx.x * C::kRows;
+  const int j0 = blockIdx.x * kBwdRows;
   if (j0 >= L) return;
-  const int j1 = min(j0 + C::kRows, L);
-  const int tid = threadIdx.x, part = tid % P;
-  const int j = j0 + tid / P;
+  const int j1 = min(j0 + kBwdRows, L);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int x = lane & 15, g = lane >> 4;
+  const int j = j0 + 16 * w + x;
   const bool live = j < j1;
   const int jc = live ? j : j0;
-  const size_t ko = ((size_t)(seq0 + jc) * hkv + g) * D + part * kPart;
-  float kp[kPart], vp[kPart], ak[kPart], av[kPart];
-  load_part(k + ko, kp);
-  load_part(v + ko, vp);
+  const size_t ko = ((size_t)(seq0 + jc) * hkv + kvh) * D;
+
+  // K and V as B operands (B[d][key]).
+  bf16x8 kop[C::kSt], vop[C::kSt];
 #pragma unroll
-  for (int c = 0; c < kPart; ++c) {
-    ak[c] = 0.f;
-    av[c] = 0.f;
+  for (int st = 0; st < C::kSt; ++st) {
+    kop[st] = ld_global_x8(k + ko + 32 * st + 8 * g);
+    vop[st] = ld_global_x8(v + ko + 32 * st + 8 * g);
+  }
+  f32x4 ak[C::kDb], av[C::kDb];
+#pragma unroll
+  for (int db = 0; db < C::kDb; ++db) {
+    ak[db] = f32x4{};
+    av[db] = f32x4{};
   }
   // Rows that admit a key of the tile: from its first key (or the span of
   // its first key) to the window above its last key (or the span of its
@@ -211,77 +254,92 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (find_span(spans, num_spans, seq0 + j1 - 1, s0, e0)) hi = max(hi, min(e0 - seq0, L));
   }
   // (row, head) pairs in order: rows ascending, the group's heads ascending.
-  const long long n_pairs = (long long)(hi - lo) * G;
-  for (long long w0 = 0; w0 < n_pairs; w0 += kStage) {
-    const int n = (int)min((long long)kStage, n_pairs - w0);
+  const int n_pairs = (hi - lo) * G;
+  for (int w0 = 0; w0 < n_pairs; w0 += kBwdTile) {
     __syncthreads();
-    for (int e = tid * 8; e < n * D; e += kBwdThreads * 8) {
-      const int ww = e / D, c = e % D;
-      const long long w = w0 + ww;
-      const int i = lo + (int)(w / G), h = g * G + (int)(w % G);
-      const size_t qo = ((size_t)(seq0 + i) * hq + h) * D + c;
-      const bf16x8 xq = ld_global_x8(q + qo), xd = ld_global_x8(dout + qo);
+    auto pair_src = [&](const bf16* base, int r) -> const bf16* {
+      const int pw = w0 + r;
+      if (pw >= n_pairs) return nullptr;
+      return base + ((size_t)(seq0 + lo + pw / G) * hq + kvh * G + pw % G) * D;
+    };
+    stage_tile<D>(qt, [&](int r) { return pair_src(q, r); }, tid);
+    stage_tile<D>(dt, [&](int r) { return pair_src(dout, r); }, tid);
+    if (tid < kBwdTile) {
+      const int pw = w0 + tid;
+      int row = -1, ps = 0, pe = 0;
+      float l2 = 0.f, dl = 0.f;
+      if (pw < n_pairs) {
+        row = lo + pw / G;
+        const size_t ro = (size_t)(seq0 + row) * hq + kvh * G + pw % G;
+        l2 = lse[ro] * 1.4426950408889634f;
+        dl = delta[ro];
+        if (num_spans > 0 && find_span(spans, num_spans, seq0 + row, s0, e0)) {
+          ps = s0 - seq0;
+          pe = e0 - seq0;
+        }
+      }
+      prow[tid] = row;
+      pss[tid] = ps;
+      pse[tid] = pe;
+      plse[tid] = l2;
+      pdel[tid] = dl;
+    }
+    __syncthreads();
+    // S and dP: pairs 16pb + 4g + e of key x.
+    f32x4 s[2], dp[2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        qd[0][ww][c + u] = (float)xq[u];
-        qd[1][ww][c + u] = (float)xd[u];
+    for (int pb = 0; pb < 2; ++pb) {
+#pragma unroll
+      for (int st = 0; st < C::kSt; ++st) {
+        const bf16x8 qa = ld_lds_x8(qt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
+        const bf16x8 da = ld_lds_x8(dt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
+        s[pb] = mfma16(qa, kop[st], st == 0 ? f32x4{} : s[pb]);
+        dp[pb] = mfma16(da, vop[st], st == 0 ? f32x4{} : dp[pb]);
       }
     }
-    for (int ww = tid; ww < n; ww += kBwdThreads) {
-      const long long w = w0 + ww;
-      const int i = lo + (int)(w / G), h = g * G + (int)(w % G);
-      const size_t ro = (size_t)(seq0 + i) * hq + h;
-      rl[ww][0] = lse[ro] * 1.4426950408889634f;
-      rl[ww][1] = delta[ro];
-      int ss = 0, se = 0;
-      if (num_spans > 0 && find_span(spans, num_spans, seq0 + i, s0, e0)) {
-        ss = s0 - seq0;
-        se = e0 - seq0;
+    f32x4 p[2], ds[2];
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * pb + 4 * g + e;
+        const int row = prow[t];
+        const float pv = row >= 0 && admits(row, jc, window, pss[t], pse[t])
+                             ? fast_exp2(__builtin_fmaf(s[pb][e], c2, -plse[t]))
+                             : 0.f;
+        p[pb][e] = pv;
+        ds[pb][e] = pv * (dp[pb][e] - pdel[t]);
       }
-      rs[ww][0] = i;
-      rs[ww][1] = ss;
-      rs[ww][2] = se;
     }
-    __syncthreads();
-    for (int ww = 0; ww < n; ++ww) {
-      const float* qr = &qd[0][ww][part * kPart];
-      const float* dr = &qd[1][ww][part * kPart];
-      float qv[kPart], dov[kPart];
+    const bf16x8 pbf = pack8(p[0], p[1]);
+    const bf16x8 dsb = pack8(ds[0], ds[1]);
+    // dV^T[d][key] += dout^T[d][pair] P[pair][key];  dK^T += Q^T dS
 #pragma unroll
-      for (int c = 0; c < kPart; ++c) {
-        qv[c] = qr[c];
-        dov[c] = dr[c];
-      }
-      const float s = part_sum<P>(dot_part(qv, kp));
-      const float dp = part_sum<P>(dot_part(dov, vp));
-      const float p = admits(rs[ww][0], jc, window, rs[ww][1], rs[ww][2])
-                          ? fast_exp2(__builtin_fmaf(s, c2, -rl[ww][0]))
-                          : 0.f;
-      const float ds = p * (dp - rl[ww][1]);
-#pragma unroll
-      for (int c = 0; c < kPart; ++c) {
-        ak[c] = __builtin_fmaf(ds, qv[c], ak[c]);
-        av[c] = __builtin_fmaf(p, dov[c], av[c]);
-      }
+    for (int db = 0; db < C::kDb; ++db) {
+      av[db] = mfma16(lds_t_operand<C::kLd>(dt, 16 * db, g, x), pbf, av[db]);
+      ak[db] = mfma16(lds_t_operand<C::kLd>(qt, 16 * db, g, x), dsb, ak[db]);
     }
   }
   if (!live) return;
 #pragma unroll
-  for (int c = 0; c < kPart; c += 4) {
-    float4 w;
-    w.x = ak[c] * scale;
-    w.y = ak[c + 1] * scale;
-    w.z = ak[c + 2] * scale;
-    w.w = ak[c + 3] * scale;
-    *reinterpret_cast<float4*>(dk + ko + c) = w;
-    *reinterpret_cast<float4*>(dv + ko + c) = make_float4(av[c], av[c + 1], av[c + 2], av[c + 3]);
+  for (int db = 0; db < C::kDb; ++db) {
+    float4 wk, wv;
+    wk.x = ak[db][0] * scale;
+    wk.y = ak[db][1] * scale;
+    wk.z = ak[db][2] * scale;
+    wk.w = ak[db][3] * scale;
+    wv.x = av[db][0];
+    wv.y = av[db][1];
+    wv.z = av[db][2];
+    wv.w = av[db][3];
+    *reinterpret_cast<float4*>(dk + ko + 16 * db + 4 * g) = wk;
+    *reinterpret_cast<float4*>(dv + ko + 16 * db + 4 * g) = wv;
   }
 }
 
 template <int D>
 hipError_t launch_bwd_d(const BackwardArgs& a, hipStream_t stream) {
-  using C = BwdCfg<D>;
-  const unsigned tiles = (unsigned)((a.max_seqlen + C::kRows - 1) / C::kRows);
+  const unsigned tiles = (unsigned)((a.max_seqlen + kBwdRows - 1) / kBwdRows);
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(tiles, a.hq, a.batch), dim3(kBwdThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,
                      a.lse, (const bf16*)a.dout, a.dq, a.delta, a.cu_seqlens, a.spans,
@@ -298,12 +356,7 @@ hipError_t launch_bwd_d(const BackwardArgs& a, hipStream_t stream) {
 }  // namespace
 
 int backward_rows_per_tile(int d) {
-  switch (d) {
-    case 64: return BwdCfg<64>::kRows;
-    case 256: return BwdCfg<256>::kRows;
-    case 512: return BwdCfg<512>::kRows;
-    default: return 0;
-  }
+  return (d == 64 || d == 256 || d == 512) ? kBwdRows : 0;
 }
 
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
