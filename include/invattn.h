@@ -188,16 +188,20 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
  * accumulators and orders, no split-K or cross-workgroup atomics (section 4,
  * items 1 and 3).  Masks, spans and the GQA map are those of the forward.
  *
- * Arithmetic (fp32 FMAs; c = fl32(scale * log2 e)):
- *   delta_i = sum_d dout_i[d] o_i[d]        (o: the forward's bf16 output)
- *   p_ij    = exp2(fma(q_i.k_j, c, -fl32(lse_i * log2 e)))  (0 off the mask)
- *   ds_ij   = p_ij (dout_i.v_j - delta_i)
- *   dq_i    = scale * sum_j ds_ij k_j                 (keys ascending)
- *   dk_j    = scale * sum_i sum_h ds_ij q_i           (rows ascending, then
- *   dv_j    =         sum_i sum_h p_ij dout_i          the group's heads)
- * Dot products run over the head dim in 32-element parts (fma chains,
- * ascending), the parts added in a fixed butterfly.  Two kernels run on the
- * stream: dq (and delta into the workspace), then dk and dv.
+ * Arithmetic (c = fl32(scale * log2 e); lse2 = fl32(lse * log2 e)):
+ *   s_ij, dp_ij, delta_i: bf16 MFMA dot products with fp32 accumulation of
+ *           q_i.k_j, v_j.dout_i and o_i.dout_i (delta by the same MFMA
+ *           sequence as dp, so dp_ij = delta_i exactly when v_j = o_i)
+ *   p_ij    = exp2(fma(s_ij, c, -lse2_i))         (0 off the mask)
+ *   ds_ij   = p_ij (dp_ij - delta_i)
+ *   dq_i    = scale * sum_j bf16(ds_ij) k_j       MFMAs over 32 keys, key
+ *                                                  tiles ascending from a
+ *                                                  start fixed by the row tile
+ *   dk_j    = scale * sum_(i,h) bf16(ds_ij) q_ih  MFMAs over 32 (row, head)
+ *   dv_j    =         sum_(i,h) bf16(p_ij) dout_ih pairs: rows ascending, then
+ *                                                  the group's heads
+ * Two kernels run on the stream: dq (and delta into the workspace), then dk
+ * and dv.  Each output element is written once; no atomics.
  *
  * Arguments (device pointers caller-owned):
  *   q, k, v, o  bf16 as for attn_prefill_varlen (o = its output)

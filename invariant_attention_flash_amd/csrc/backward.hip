@@ -77,18 +77,33 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4& lo, const f32x4& hi) {
                 to_bf16(hi[0]), to_bf16(hi[1]), to_bf16(hi[2]), to_bf16(hi[3])};
 }
 
-// Stage rows [0, 32) of a tile: row r comes from src(r) (nullptr: zeros).
-template <int D, class Src>
-__device__ __forceinline__ void stage_tile(bf16* tile, Src src, int tid) {
-  using C = BwdCfg<D>;
+// A staged tile moves in two halves so that the next tile's global loads
+// are in flight while the current one is used: fetch() loads this thread's
+// 16-byte chunks into registers (row r from src(r); nullptr: zeros), put()
+// stores them into an LDS tile of row stride kLd.
+template <int D>
+struct TileRegs {
+  static constexpr int kPer = BwdCfg<D>::kChunks / kBwdThreads;
+  static_assert(BwdCfg<D>::kChunks % kBwdThreads == 0, "whole chunks per thread");
+  bf16x8 r[kPer];
+
+  template <class Src>
+  __device__ __forceinline__ void fetch(Src src, int tid) {
 #pragma unroll
-  for (int e = tid; e < C::kChunks; e += kBwdThreads) {
-    const int r = e / (D / 8), c = 8 * (e % (D / 8));
-    const bf16* s = src(r);
-    const bf16x8 x = s ? ld_global_x8(s + c) : bf16x8{};
-    st_lds_x8(tile + r * C::kLd + c, x);
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kBwdThreads;
+      const bf16* s = src(e / (D / 8));
+      r[u] = s ? ld_global_x8(s + 8 * (e % (D / 8))) : bf16x8{};
+    }
   }
-}
+  __device__ __forceinline__ void put(bf16* tile, int tid) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kBwdThreads;
+      st_lds_x8(tile + (e / (D / 8)) * BwdCfg<D>::kLd + 8 * (e % (D / 8)), r[u]);
+    }
+  }
+};
 
 // dq of 64 rows of one query head, and delta of those rows.
 template <int D>
@@ -100,8 +115,8 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ spans,
                    int num_spans, int hq, int hkv, int window, float scale, float c2) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 kt[kBwdTile * C::kLd];
-  __shared__ __attribute__((aligned(16))) bf16 vt[kBwdTile * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 kts[2][kBwdTile * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 vts[2][kBwdTile * C::kLd];
   const int b = blockIdx.z, h = blockIdx.y, kvh = h / (hq / hkv);
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
   const int r0 = blockIdx.x * kBwdRows;
@@ -152,15 +167,26 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
   for (int db = 0; db < C::kDb; ++db) acc[db] = f32x4{};
 
-  for (int k0 = lo; k0 < hi; k0 += kBwdTile) {
-    __syncthreads();
-    stage_tile<D>(kt, [&](int r) -> const bf16* {
+  TileRegs<D> kr, vr;
+  auto fetch = [&](int k0) {
+    kr.fetch([&](int r) -> const bf16* {
       return k0 + r < hi ? k + ((size_t)(seq0 + k0 + r) * hkv + kvh) * D : nullptr;
     }, tid);
-    stage_tile<D>(vt, [&](int r) -> const bf16* {
+    vr.fetch([&](int r) -> const bf16* {
       return k0 + r < hi ? v + ((size_t)(seq0 + k0 + r) * hkv + kvh) * D : nullptr;
     }, tid);
-    __syncthreads();
+  };
+  // Tile t sits in buffer t & 1; tile t+1's loads fly while tile t is used,
+  // one barrier per tile.
+  fetch(lo);
+  kr.put(kts[0], tid);
+  vr.put(vts[0], tid);
+  __syncthreads();
+  for (int k0 = lo, t = 0; k0 < hi; k0 += kBwdTile, ++t) {
+    const bool more = k0 + kBwdTile < hi;
+    if (more) fetch(k0 + kBwdTile);
+    const bf16* kt = kts[t & 1];
+    const bf16* vt = vts[t & 1];
     // S^T and dP^T: keys 16kb + 4g + e of row x.
     f32x4 s[2], dp[2];
 #pragma unroll
@@ -190,6 +216,11 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int db = 0; db < C::kDb; ++db)
       acc[db] = mfma16(lds_t_operand<C::kLd>(kt, 16 * db, g, x), dsb, acc[db]);
+    if (more) {
+      kr.put(kts[(t + 1) & 1], tid);
+      vr.put(vts[(t + 1) & 1], tid);
+    }
+    __syncthreads();
   }
   if (!live) return;
   float* out = dq + qo;
@@ -214,10 +245,10 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ spans,
                     int num_spans, int hq, int hkv, int window, float scale, float c2) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 qt[kBwdTile * C::kLd];
-  __shared__ __attribute__((aligned(16))) bf16 dt[kBwdTile * C::kLd];
-  __shared__ float plse[kBwdTile], pdel[kBwdTile];
-  __shared__ int prow[kBwdTile], pss[kBwdTile], pse[kBwdTile];
+  __shared__ __attribute__((aligned(16))) bf16 qts[2][kBwdTile * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 dts[2][kBwdTile * C::kLd];
+  __shared__ float plses[2][kBwdTile], pdels[2][kBwdTile];
+  __shared__ int prows[2][kBwdTile], psss[2][kBwdTile], pses[2][kBwdTile];
   const int b = blockIdx.z, kvh = blockIdx.y, G = hq / hkv;
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
   const int j0 = blockIdx.x * kBwdRows;
@@ -255,36 +286,63 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   // (row, head) pairs in order: rows ascending, the group's heads ascending.
   const int n_pairs = (hi - lo) * G;
-  for (int w0 = 0; w0 < n_pairs; w0 += kBwdTile) {
-    __syncthreads();
+  TileRegs<D> qr, dr;
+  int mrow = -1, mss = 0, mse = 0;
+  float ml2 = 0.f, mdl = 0.f;
+  auto fetch = [&](int w0) {
     auto pair_src = [&](const bf16* base, int r) -> const bf16* {
       const int pw = w0 + r;
       if (pw >= n_pairs) return nullptr;
       return base + ((size_t)(seq0 + lo + pw / G) * hq + kvh * G + pw % G) * D;
     };
-    stage_tile<D>(qt, [&](int r) { return pair_src(q, r); }, tid);
-    stage_tile<D>(dt, [&](int r) { return pair_src(dout, r); }, tid);
+    qr.fetch([&](int r) { return pair_src(q, r); }, tid);
+    dr.fetch([&](int r) { return pair_src(dout, r); }, tid);
     if (tid < kBwdTile) {
       const int pw = w0 + tid;
-      int row = -1, ps = 0, pe = 0;
-      float l2 = 0.f, dl = 0.f;
+      mrow = -1;
+      mss = mse = 0;
+      ml2 = mdl = 0.f;
       if (pw < n_pairs) {
-        row = lo + pw / G;
-        const size_t ro = (size_t)(seq0 + row) * hq + kvh * G + pw % G;
-        l2 = lse[ro] * 1.4426950408889634f;
-        dl = delta[ro];
-        if (num_spans > 0 && find_span(spans, num_spans, seq0 + row, s0, e0)) {
-          ps = s0 - seq0;
-          pe = e0 - seq0;
+        mrow = lo + pw / G;
+        const size_t ro = (size_t)(seq0 + mrow) * hq + kvh * G + pw % G;
+        ml2 = lse[ro] * 1.4426950408889634f;
+        mdl = delta[ro];
+        if (num_spans > 0 && find_span(spans, num_spans, seq0 + mrow, s0, e0)) {
+          mss = s0 - seq0;
+          mse = e0 - seq0;
         }
       }
-      prow[tid] = row;
-      pss[tid] = ps;
-      pse[tid] = pe;
-      plse[tid] = l2;
-      pdel[tid] = dl;
     }
-    __syncthreads();
+  };
+  auto put = [&](int buf) {
+    qr.put(qts[buf], tid);
+    dr.put(dts[buf], tid);
+    if (tid < kBwdTile) {
+      prows[buf][tid] = mrow;
+      psss[buf][tid] = mss;
+      pses[buf][tid] = mse;
+      plses[buf][tid] = ml2;
+      pdels[buf][tid] = mdl;
+    }
+  };
+  // Pair tile t sits in buffer t & 1; tile t+1's loads fly while tile t is
+  // used, one barrier per tile.
+  if (n_pairs > 0) {
+    fetch(0);
+    put(0);
+  }
+  __syncthreads();
+  for (int w0 = 0, t = 0; w0 < n_pairs; w0 += kBwdTile, ++t) {
+    const bool more = w0 + kBwdTile < n_pairs;
+    if (more) fetch(w0 + kBwdTile);
+    const int cb = t & 1;
+    const bf16* qt = qts[cb];
+    const bf16* dt = dts[cb];
+    const int* prow = prows[cb];
+    const int* pss = psss[cb];
+    const int* pse = pses[cb];
+    const float* plse = plses[cb];
+    const float* pdel = pdels[cb];
     // S and dP: pairs 16pb + 4g + e of key x.
     f32x4 s[2], dp[2];
 #pragma unroll
@@ -319,6 +377,8 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       av[db] = mfma16(lds_t_operand<C::kLd>(dt, 16 * db, g, x), pbf, av[db]);
       ak[db] = mfma16(lds_t_operand<C::kLd>(qt, 16 * db, g, x), dsb, ak[db]);
     }
+    if (more) put(cb ^ 1);
+    __syncthreads();
   }
   if (!live) return;
 #pragma unroll
