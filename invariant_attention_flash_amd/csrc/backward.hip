@@ -48,7 +48,13 @@ struct BwdCfg {
   static constexpr int kSt = D / 32;     // k-steps over the head dim
   static constexpr int kDb = D / 16;     // 16-column blocks of the head dim
   static constexpr int kLd = D + 8;      // LDS row stride in bf16 (16 bytes of padding)
-  static constexpr int kChunks = kBwdTile * D / 8;   // 16-byte chunks per staged tile
+  // dk/dv: 32-pair halves per step (two independent halves where the LDS
+  // budget allows); each half is one MFMA group of the fixed pair order.
+  static constexpr int kHalves = D <= 256 ? 2 : 1;
+  // dk/dv: next pair tile's loads held in registers during the current one
+  // (at head dim 512 the accumulators leave no room: staged after the step).
+  static constexpr bool kPrefetch = D <= 256;
+  static constexpr int kPairs = kBwdTile * kHalves;
   static_assert(D % 32 == 0, "head dim in MFMA k-steps");
 };
 
@@ -81,10 +87,10 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4& lo, const f32x4& hi) {
 // are in flight while the current one is used: fetch() loads this thread's
 // 16-byte chunks into registers (row r from src(r); nullptr: zeros), put()
 // stores them into an LDS tile of row stride kLd.
-template <int D>
+template <int D, int ROWS = kBwdTile>
 struct TileRegs {
-  static constexpr int kPer = BwdCfg<D>::kChunks / kBwdThreads;
-  static_assert(BwdCfg<D>::kChunks % kBwdThreads == 0, "whole chunks per thread");
+  static constexpr int kPer = ROWS * D / 8 / kBwdThreads;
+  static_assert((ROWS * D / 8) % kBwdThreads == 0, "whole chunks per thread");
   bf16x8 r[kPer];
 
   template <class Src>
@@ -117,6 +123,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   using C = BwdCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 kts[2][kBwdTile * C::kLd];
   __shared__ __attribute__((aligned(16))) bf16 vts[2][kBwdTile * C::kLd];
+  __shared__ bf16x8 xch[4][64];   // dS of every wave's row block as B operands
   const int b = blockIdx.z, h = blockIdx.y, kvh = h / (hq / hkv);
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
   const int r0 = blockIdx.x * kBwdRows;
@@ -126,7 +133,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int x = lane & 15, g = lane >> 4;
   const int i = r0 + 16 * w + x;
   const bool live = i < r1;
-  const int ic = live ? i : r0;   // rows past the tile compute on row r0 and store nothing
+  const int ic = live ? i : r0;   // rows past the tile compute on row r0; nothing stored
   const size_t qo = ((size_t)(seq0 + ic) * hq + h) * D;
 
   // Q and dout as B operands (B[d][row]): lane (g, x) holds d = 32st + 8g + 0..7.
@@ -163,9 +170,15 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (find_span(spans, num_spans, seq0 + r1 - 1, s0, e0)) hi = max(hi, min(e0 - seq0, L));
   }
 
-  f32x4 acc[C::kDb];
+  // The wave accumulates dQ^T for its quarter of the head dim (columns
+  // w*D/4 + 16*db + ...) and all four row blocks of the workgroup.
+  constexpr int kDq = C::kDb / 4;
+  f32x4 acc[kDq][4];
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db) acc[db] = f32x4{};
+  for (int db = 0; db < kDq; ++db) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) acc[db][rb] = f32x4{};
+  }
 
   TileRegs<D> kr, vr;
   auto fetch = [&](int k0) {
@@ -211,27 +224,36 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         ds[kb][e] = p * (dp[kb][e] - del);
       }
     }
-    const bf16x8 dsb = pack8(ds[0], ds[1]);
-    // dQ^T[d][row] += K^T[d][key] dS^T[key][row]
+    xch[w][lane] = pack8(ds[0], ds[1]);
+    __syncthreads();
+    // dQ^T[d][row] += K^T[d][key] dS^T[key][row]; each transpose read serves
+    // the four row blocks.
 #pragma unroll
-    for (int db = 0; db < C::kDb; ++db)
-      acc[db] = mfma16(lds_t_operand<C::kLd>(kt, 16 * db, g, x), dsb, acc[db]);
+    for (int db = 0; db < kDq; ++db) {
+      const bf16x8 ak = lds_t_operand<C::kLd>(kt, w * (D / 4) + 16 * db, g, x);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) acc[db][rb] = mfma16(ak, xch[rb][lane], acc[db][rb]);
+    }
     if (more) {
       kr.put(kts[(t + 1) & 1], tid);
       vr.put(vts[(t + 1) & 1], tid);
     }
     __syncthreads();
   }
-  if (!live) return;
-  float* out = dq + qo;
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db) {
-    float4 wv;
-    wv.x = acc[db][0] * scale;
-    wv.y = acc[db][1] * scale;
-    wv.z = acc[db][2] * scale;
-    wv.w = acc[db][3] * scale;
-    *reinterpret_cast<float4*>(out + 16 * db + 4 * g) = wv;
+  for (int rb = 0; rb < 4; ++rb) {
+    const int ir = r0 + 16 * rb + x;
+    if (ir >= r1) continue;
+    float* out = dq + ((size_t)(seq0 + ir) * hq + h) * D + w * (D / 4) + 4 * g;
+#pragma unroll
+    for (int db = 0; db < kDq; ++db) {
+      float4 wv;
+      wv.x = acc[db][rb][0] * scale;
+      wv.y = acc[db][rb][1] * scale;
+      wv.z = acc[db][rb][2] * scale;
+      wv.w = acc[db][rb][3] * scale;
+      *reinterpret_cast<float4*>(out + 16 * db) = wv;
+    }
   }
 }
 
@@ -245,10 +267,13 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ spans,
                     int num_spans, int hq, int hkv, int window, float scale, float c2) {
   using C = BwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) bf16 qts[2][kBwdTile * C::kLd];
-  __shared__ __attribute__((aligned(16))) bf16 dts[2][kBwdTile * C::kLd];
-  __shared__ float plses[2][kBwdTile], pdels[2][kBwdTile];
-  __shared__ int prows[2][kBwdTile], psss[2][kBwdTile], pses[2][kBwdTile];
+  constexpr int NP = C::kPairs;
+  __shared__ __attribute__((aligned(16))) bf16 qts[2][NP * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 dts[2][NP * C::kLd];
+  __shared__ __attribute__((aligned(16))) float plses[2][NP], pdels[2][NP];
+  __shared__ __attribute__((aligned(16))) int prows[2][NP], psss[2][NP], pses[2][NP];
+  // P and dS of every wave's key block as B operands (bf16x8 per lane).
+  __shared__ bf16x8 xch[2][C::kHalves][4][64];
   const int b = blockIdx.z, kvh = blockIdx.y, G = hq / hkv;
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
   const int j0 = blockIdx.x * kBwdRows;
@@ -268,11 +293,17 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     kop[st] = ld_global_x8(k + ko + 32 * st + 8 * g);
     vop[st] = ld_global_x8(v + ko + 32 * st + 8 * g);
   }
-  f32x4 ak[C::kDb], av[C::kDb];
+  // The wave accumulates dK^T and dV^T for its quarter of the head dim
+  // (columns w*D/4 + 16*db + ...) and all four key blocks of the workgroup.
+  constexpr int kDq = C::kDb / 4;
+  f32x4 ak[kDq][4], av[kDq][4];
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db) {
-    ak[db] = f32x4{};
-    av[db] = f32x4{};
+  for (int db = 0; db < kDq; ++db) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      ak[db][kb] = f32x4{};
+      av[db][kb] = f32x4{};
+    }
   }
   // Rows that admit a key of the tile: from its first key (or the span of
   // its first key) to the window above its last key (or the span of its
@@ -286,7 +317,7 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   // (row, head) pairs in order: rows ascending, the group's heads ascending.
   const int n_pairs = (hi - lo) * G;
-  TileRegs<D> qr, dr;
+  TileRegs<D, NP> qr, dr;
   int mrow = -1, mss = 0, mse = 0;
   float ml2 = 0.f, mdl = 0.f;
   auto fetch = [&](int w0) {
@@ -297,7 +328,7 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     };
     qr.fetch([&](int r) { return pair_src(q, r); }, tid);
     dr.fetch([&](int r) { return pair_src(dout, r); }, tid);
-    if (tid < kBwdTile) {
+    if (tid < NP) {
       const int pw = w0 + tid;
       mrow = -1;
       mss = mse = 0;
@@ -317,7 +348,7 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   auto put = [&](int buf) {
     qr.put(qts[buf], tid);
     dr.put(dts[buf], tid);
-    if (tid < kBwdTile) {
+    if (tid < NP) {
       prows[buf][tid] = mrow;
       psss[buf][tid] = mss;
       pses[buf][tid] = mse;
@@ -325,16 +356,22 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       pdels[buf][tid] = mdl;
     }
   };
-  // Pair tile t sits in buffer t & 1; tile t+1's loads fly while tile t is
-  // used, one barrier per tile.
-  if (n_pairs > 0) {
+  // Pair tile t sits in buffer t & 1; with prefetch, tile t+1's loads fly
+  // while tile t is used.
+  if (C::kPrefetch && n_pairs > 0) {
     fetch(0);
     put(0);
   }
   __syncthreads();
-  for (int w0 = 0, t = 0; w0 < n_pairs; w0 += kBwdTile, ++t) {
-    const bool more = w0 + kBwdTile < n_pairs;
-    if (more) fetch(w0 + kBwdTile);
+  for (int w0 = 0, t = 0; w0 < n_pairs; w0 += NP, ++t) {
+    const bool more = w0 + NP < n_pairs;
+    if constexpr (C::kPrefetch) {
+      if (more) fetch(w0 + NP);
+    } else {
+      fetch(w0);
+      put(t & 1);
+      __syncthreads();
+    }
     const int cb = t & 1;
     const bf16* qt = qts[cb];
     const bf16* dt = dts[cb];
@@ -343,57 +380,89 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int* pse = pses[cb];
     const float* plse = plses[cb];
     const float* pdel = pdels[cb];
-    // S and dP: pairs 16pb + 4g + e of key x.
-    f32x4 s[2], dp[2];
+    // Per half hf: S and dP of pairs 32hf + 16pb + 4g + e for key x of the
+    // wave's key block, posted for every wave.
 #pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
+    for (int hf = 0; hf < C::kHalves; ++hf) {
+      const bf16* qh = qt + 32 * hf * C::kLd;
+      const bf16* dh = dt + 32 * hf * C::kLd;
+      f32x4 s[2], dp[2];
 #pragma unroll
-      for (int st = 0; st < C::kSt; ++st) {
-        const bf16x8 qa = ld_lds_x8(qt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
-        const bf16x8 da = ld_lds_x8(dt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
-        s[pb] = mfma16(qa, kop[st], st == 0 ? f32x4{} : s[pb]);
-        dp[pb] = mfma16(da, vop[st], st == 0 ? f32x4{} : dp[pb]);
+      for (int pb = 0; pb < 2; ++pb) {
+#pragma unroll
+        for (int st = 0; st < C::kSt; ++st) {
+          const bf16x8 qa = ld_lds_x8(qh + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
+          const bf16x8 da = ld_lds_x8(dh + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
+          s[pb] = mfma16(qa, kop[st], st == 0 ? f32x4{} : s[pb]);
+          dp[pb] = mfma16(da, vop[st], st == 0 ? f32x4{} : dp[pb]);
+        }
+      }
+      f32x4 p[2], ds[2];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        // The lane's four consecutive pairs: one 16-byte read per array.
+        const int t0 = 32 * hf + 16 * pb + 4 * g;
+        const int4 rw = *reinterpret_cast<const int4*>(prow + t0);
+        const int4 sa = *reinterpret_cast<const int4*>(pss + t0);
+        const int4 sb = *reinterpret_cast<const int4*>(pse + t0);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(plse + t0);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(pdel + t0);
+        const int rv[4] = {rw.x, rw.y, rw.z, rw.w};
+        const int av0[4] = {sa.x, sa.y, sa.z, sa.w};
+        const int av1[4] = {sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = rv[e] >= 0 && admits(rv[e], jc, window, av0[e], av1[e])
+                               ? fast_exp2(__builtin_fmaf(s[pb][e], c2, -l2[e]))
+                               : 0.f;
+          p[pb][e] = pv;
+          ds[pb][e] = pv * (dp[pb][e] - dl[e]);
+        }
+      }
+      xch[0][hf][w][lane] = pack8(p[0], p[1]);
+      xch[1][hf][w][lane] = pack8(ds[0], ds[1]);
+    }
+    __syncthreads();
+    // dV^T[d][key] += dout^T[d][pair] P[pair][key];  dK^T += Q^T dS.  Each
+    // transpose read serves the four key blocks; halves in pair order.
+#pragma unroll
+    for (int db = 0; db < kDq; ++db) {
+      const int c0 = w * (D / 4) + 16 * db;
+#pragma unroll
+      for (int hf = 0; hf < C::kHalves; ++hf) {
+        const bf16x8 ad = lds_t_operand<C::kLd>(dt + 32 * hf * C::kLd, c0, g, x);
+        const bf16x8 aq = lds_t_operand<C::kLd>(qt + 32 * hf * C::kLd, c0, g, x);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          av[db][kb] = mfma16(ad, xch[0][hf][kb][lane], av[db][kb]);
+          ak[db][kb] = mfma16(aq, xch[1][hf][kb][lane], ak[db][kb]);
+        }
       }
     }
-    f32x4 p[2], ds[2];
-#pragma unroll
-    for (int pb = 0; pb < 2; ++pb) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * pb + 4 * g + e;
-        const int row = prow[t];
-        const float pv = row >= 0 && admits(row, jc, window, pss[t], pse[t])
-                             ? fast_exp2(__builtin_fmaf(s[pb][e], c2, -plse[t]))
-                             : 0.f;
-        p[pb][e] = pv;
-        ds[pb][e] = pv * (dp[pb][e] - pdel[t]);
-      }
+    if constexpr (C::kPrefetch) {
+      if (more) put(cb ^ 1);
     }
-    const bf16x8 pbf = pack8(p[0], p[1]);
-    const bf16x8 dsb = pack8(ds[0], ds[1]);
-    // dV^T[d][key] += dout^T[d][pair] P[pair][key];  dK^T += Q^T dS
-#pragma unroll
-    for (int db = 0; db < C::kDb; ++db) {
-      av[db] = mfma16(lds_t_operand<C::kLd>(dt, 16 * db, g, x), pbf, av[db]);
-      ak[db] = mfma16(lds_t_operand<C::kLd>(qt, 16 * db, g, x), dsb, ak[db]);
-    }
-    if (more) put(cb ^ 1);
     __syncthreads();
   }
-  if (!live) return;
 #pragma unroll
-  for (int db = 0; db < C::kDb; ++db) {
-    float4 wk, wv;
-    wk.x = ak[db][0] * scale;
-    wk.y = ak[db][1] * scale;
-    wk.z = ak[db][2] * scale;
-    wk.w = ak[db][3] * scale;
-    wv.x = av[db][0];
-    wv.y = av[db][1];
-    wv.z = av[db][2];
-    wv.w = av[db][3];
-    *reinterpret_cast<float4*>(dk + ko + 16 * db + 4 * g) = wk;
-    *reinterpret_cast<float4*>(dv + ko + 16 * db + 4 * g) = wv;
+  for (int kb = 0; kb < 4; ++kb) {
+    const int jk = j0 + 16 * kb + x;
+    if (jk >= j1) continue;
+    const size_t kko = ((size_t)(seq0 + jk) * hkv + kvh) * D + w * (D / 4) + 4 * g;
+#pragma unroll
+    for (int db = 0; db < kDq; ++db) {
+      float4 wk, wv;
+      wk.x = ak[db][kb][0] * scale;
+      wk.y = ak[db][kb][1] * scale;
+      wk.z = ak[db][kb][2] * scale;
+      wk.w = ak[db][kb][3] * scale;
+      wv.x = av[db][kb][0];
+      wv.y = av[db][kb][1];
+      wv.z = av[db][kb][2];
+      wv.w = av[db][kb][3];
+      *reinterpret_cast<float4*>(dk + kko + 16 * db) = wk;
+      *reinterpret_cast<float4*>(dv + kko + 16 * db) = wv;
+    }
   }
 }
 
