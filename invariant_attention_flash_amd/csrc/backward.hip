@@ -111,6 +111,8 @@ struct TileRegs {
   }
 };
 
+}  // namespace
+
 // dq of 64 rows of one query head, and delta of those rows.
 template <int D>
 __global__ __launch_bounds__(kBwdThreads)
@@ -465,6 +467,8 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   }
 }
+
+namespace {
 
 template <int D>
 hipError_t launch_bwd_d(const BackwardArgs& a, hipStream_t stream) {
