@@ -43,6 +43,11 @@ constexpr int kBwdThreads = 256;   // four waves
 constexpr int kBwdRows = 64;       // rows (dq) or keys (dk, dv) per workgroup: 16 per wave
 constexpr int kBwdTile = 32;       // keys (dq) or (row, head) pairs (dk, dv) per step
 
+// dk/dv at head dim 256 on the two-kind kernel (0: bwd_dkv_kernel).
+#ifndef BWD_WS
+#define BWD_WS 1
+#endif
+
 template <int D>
 struct BwdCfg {
   static constexpr int kSt = D / 32;     // k-steps over the head dim
@@ -468,6 +473,225 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
+// dk and dv of 64 keys of one KV head, two kinds of waves (head dim 256).
+// Waves 0-3 (score waves) form S, dP, P and dS of 32 pairs for key
+// block w and post P and dS; waves 4-7 (gradient waves) accumulate dV^T and
+// dK^T for column quarter w-4 of all four key blocks from the previous
+// step's posts.  Pair tiles sit in a ring of three LDS buffers: during step
+// t the score waves read tile t, the gradient waves tile t-1, and tile t+1
+// lands.  Every accumulator sees the same MFMAs in the same order as in
+// bwd_dkv_kernel, so the bytes are the same.
+template <int D>
+__global__ __launch_bounds__(2 * kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                       const bf16* __restrict__ v, const float* __restrict__ lse,
+                       const bf16* __restrict__ dout, const float* __restrict__ delta,
+                       float* __restrict__ dk, float* __restrict__ dv,
+                       const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ spans,
+                       int num_spans, int hq, int hkv, int window, float scale, float c2) {
+  using C = BwdCfg<D>;
+  constexpr int NP = kBwdTile;
+  constexpr int kRing = 3;
+  constexpr int kThreads = 2 * kBwdThreads;
+  constexpr int kPer = NP * D / 8 / kThreads;   // 16-byte chunks per thread per tensor
+  static_assert((NP * D / 8) % kThreads == 0, "whole chunks per thread");
+  __shared__ __attribute__((aligned(16))) bf16 qts[kRing][NP * C::kLd];
+  __shared__ __attribute__((aligned(16))) bf16 dts[kRing][NP * C::kLd];
+  __shared__ __attribute__((aligned(16))) float plses[kRing][NP], pdels[kRing][NP];
+  __shared__ __attribute__((aligned(16))) int prows[kRing][NP], psss[kRing][NP], pses[kRing][NP];
+  __shared__ bf16x8 xch[2][2][4][64];   // [step parity][P, dS][key block][lane]
+  const int b = blockIdx.z, kvh = blockIdx.y, G = hq / hkv;
+  const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
+  const int j0 = blockIdx.x * kBwdRows;
+  if (j0 >= L) return;
+  const int j1 = min(j0 + kBwdRows, L);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool scorer = wv < 4;
+  const int w = wv & 3;
+  const int x = lane & 15, g = lane >> 4;
+
+  int s0, e0;
+  int lo = j0;
+  int hi = window > 0 ? min(L, j1 - 1 + window) : L;
+  if (num_spans > 0) {
+    if (find_span(spans, num_spans, seq0 + j0, s0, e0)) lo = min(lo, max(s0 - seq0, 0));
+    if (find_span(spans, num_spans, seq0 + j1 - 1, s0, e0)) hi = max(hi, min(e0 - seq0, L));
+  }
+  const int n_pairs = (hi - lo) * G;
+  const int n_tiles = (n_pairs + NP - 1) / NP;
+
+  bf16x8 qr[kPer], dr[kPer];
+  int mrow = -1, mss = 0, mse = 0;
+  float ml2 = 0.f, mdl = 0.f;
+  auto fetch = [&](int t) {
+    const int w0 = t * NP;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      const int pw = w0 + e / (D / 8), c = 8 * (e % (D / 8));
+      if (pw < n_pairs) {
+        const size_t ro = ((size_t)(seq0 + lo + pw / G) * hq + kvh * G + pw % G) * D + c;
+        qr[u] = ld_global_x8(q + ro);
+        dr[u] = ld_global_x8(dout + ro);
+      } else {
+        qr[u] = bf16x8{};
+        dr[u] = bf16x8{};
+      }
+    }
+    if (tid < NP) {
+      const int pw = w0 + tid;
+      mrow = -1;
+      mss = mse = 0;
+      ml2 = mdl = 0.f;
+      if (pw < n_pairs) {
+        mrow = lo + pw / G;
+        const size_t ro = (size_t)(seq0 + mrow) * hq + kvh * G + pw % G;
+        ml2 = lse[ro] * 1.4426950408889634f;
+        mdl = delta[ro];
+        if (num_spans > 0 && find_span(spans, num_spans, seq0 + mrow, s0, e0)) {
+          mss = s0 - seq0;
+          mse = e0 - seq0;
+        }
+      }
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = tid + u * kThreads;
+      const int r = e / (D / 8), c = 8 * (e % (D / 8));
+      st_lds_x8(qts[buf] + r * C::kLd + c, qr[u]);
+      st_lds_x8(dts[buf] + r * C::kLd + c, dr[u]);
+    }
+    if (tid < NP) {
+      prows[buf][tid] = mrow;
+      psss[buf][tid] = mss;
+      pses[buf][tid] = mse;
+      plses[buf][tid] = ml2;
+      pdels[buf][tid] = mdl;
+    }
+  };
+
+  if (n_tiles > 0) {
+    fetch(0);
+    put(0);
+  }
+  __syncthreads();
+  // Each kind runs its own loop (so that its registers do not overlap the
+  // other kind's); both pass n_tiles + 1 barriers.
+  if (scorer) {
+    // K and V of key j as B operands.
+    const int j = j0 + 16 * w + x;
+    const int jc = j < j1 ? j : j0;
+    bf16x8 kop[C::kSt], vop[C::kSt];
+    const size_t ko = ((size_t)(seq0 + jc) * hkv + kvh) * D;
+#pragma unroll
+    for (int st = 0; st < C::kSt; ++st) {
+      kop[st] = ld_global_x8(k + ko + 32 * st + 8 * g);
+      vop[st] = ld_global_x8(v + ko + 32 * st + 8 * g);
+    }
+    for (int t = 0; t <= n_tiles; ++t) {
+      const bool more = t + 1 < n_tiles;
+      if (more) fetch(t + 1);
+      if (t < n_tiles) {
+        const int cb = t % kRing;
+        const bf16* qt = qts[cb];
+        const bf16* dt = dts[cb];
+        f32x4 sc[2], dp[2];
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+#pragma unroll
+          for (int st = 0; st < C::kSt; ++st) {
+            const bf16x8 qa = ld_lds_x8(qt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
+            const bf16x8 da = ld_lds_x8(dt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
+            sc[pb] = mfma16(qa, kop[st], st == 0 ? f32x4{} : sc[pb]);
+            dp[pb] = mfma16(da, vop[st], st == 0 ? f32x4{} : dp[pb]);
+          }
+        }
+        f32x4 p[2], ds[2];
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+          const int t0 = 16 * pb + 4 * g;
+          const int4 rw = *reinterpret_cast<const int4*>(prows[cb] + t0);
+          const int4 sa = *reinterpret_cast<const int4*>(psss[cb] + t0);
+          const int4 sb = *reinterpret_cast<const int4*>(pses[cb] + t0);
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(plses[cb] + t0);
+          const f32x4 dl = *reinterpret_cast<const f32x4*>(pdels[cb] + t0);
+          const int rv[4] = {rw.x, rw.y, rw.z, rw.w};
+          const int av0[4] = {sa.x, sa.y, sa.z, sa.w};
+          const int av1[4] = {sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = rv[e] >= 0 && admits(rv[e], jc, window, av0[e], av1[e])
+                                 ? fast_exp2(__builtin_fmaf(sc[pb][e], c2, -l2[e]))
+                                 : 0.f;
+            p[pb][e] = pv;
+            ds[pb][e] = pv * (dp[pb][e] - dl[e]);
+          }
+        }
+        xch[t & 1][0][w][lane] = pack8(p[0], p[1]);
+        xch[t & 1][1][w][lane] = pack8(ds[0], ds[1]);
+      }
+      if (more) put((t + 1) % kRing);
+      __syncthreads();
+    }
+    return;
+  }
+  // Gradient waves: dK^T, dV^T for columns w*D/4 + 16*db + 4g + i, key blocks kb.
+  constexpr int kDq = C::kDb / 4;
+  f32x4 ak[kDq][4], av[kDq][4];
+#pragma unroll
+  for (int db = 0; db < kDq; ++db) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      ak[db][kb] = f32x4{};
+      av[db][kb] = f32x4{};
+    }
+  }
+  for (int t = 0; t <= n_tiles; ++t) {
+    const bool more = t + 1 < n_tiles;
+    if (more) fetch(t + 1);
+    if (t >= 1) {
+      const int pbuf = (t - 1) % kRing;
+      const bf16* qt = qts[pbuf];
+      const bf16* dt = dts[pbuf];
+#pragma unroll
+      for (int db = 0; db < kDq; ++db) {
+        const int c0 = w * (D / 4) + 16 * db;
+        const bf16x8 ad = lds_t_operand<C::kLd>(dt, c0, g, x);
+        const bf16x8 aq = lds_t_operand<C::kLd>(qt, c0, g, x);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          av[db][kb] = mfma16(ad, xch[(t - 1) & 1][0][kb][lane], av[db][kb]);
+          ak[db][kb] = mfma16(aq, xch[(t - 1) & 1][1][kb][lane], ak[db][kb]);
+        }
+      }
+    }
+    if (more) put((t + 1) % kRing);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int jk = j0 + 16 * kb + x;
+    if (jk >= j1) continue;
+    const size_t kko = ((size_t)(seq0 + jk) * hkv + kvh) * D + w * (D / 4) + 4 * g;
+#pragma unroll
+    for (int db = 0; db < kDq; ++db) {
+      float4 wk, wvv;
+      wk.x = ak[db][kb][0] * scale;
+      wk.y = ak[db][kb][1] * scale;
+      wk.z = ak[db][kb][2] * scale;
+      wk.w = ak[db][kb][3] * scale;
+      wvv.x = av[db][kb][0];
+      wvv.y = av[db][kb][1];
+      wvv.z = av[db][kb][2];
+      wvv.w = av[db][kb][3];
+      *reinterpret_cast<float4*>(dk + kko + 16 * db) = wk;
+      *reinterpret_cast<float4*>(dv + kko + 16 * db) = wvv;
+    }
+  }
+}
+
 namespace {
 
 template <int D>
@@ -479,10 +703,16 @@ hipError_t launch_bwd_d(const BackwardArgs& a, hipStream_t stream) {
                      a.num_spans, a.hq, a.hkv, a.window, a.scale, a.c2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3(tiles, a.hkv, a.batch), dim3(kBwdThreads), 0,
-                     stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
-                     (const bf16*)a.dout, (const float*)a.delta, a.dk, a.dv, a.cu_seqlens,
-                     a.spans, a.num_spans, a.hq, a.hkv, a.window, a.scale, a.c2);
+  if constexpr (D == 256 && BWD_WS)
+    hipLaunchKernelGGL(bwd_dkv_ws_kernel<D>, dim3(tiles, a.hkv, a.batch), dim3(2 * kBwdThreads),
+                       0, stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
+                       (const bf16*)a.dout, (const float*)a.delta, a.dk, a.dv, a.cu_seqlens,
+                       a.spans, a.num_spans, a.hq, a.hkv, a.window, a.scale, a.c2);
+  else
+    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3(tiles, a.hkv, a.batch), dim3(kBwdThreads), 0,
+                       stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
+                       (const bf16*)a.dout, (const float*)a.delta, a.dk, a.dv, a.cu_seqlens,
+                       a.spans, a.num_spans, a.hq, a.hkv, a.window, a.scale, a.c2);
   return hipGetLastError();
 }
 
