@@ -655,6 +655,12 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int pbuf = (t - 1) % kRing;
       const bf16* qt = qts[pbuf];
       const bf16* dt = dts[pbuf];
+      bf16x8 px[4], dx[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        px[kb] = xch[(t - 1) & 1][0][kb][lane];
+        dx[kb] = xch[(t - 1) & 1][1][kb][lane];
+      }
 #pragma unroll
       for (int db = 0; db < kDq; ++db) {
         const int c0 = w * (D / 4) + 16 * db;
@@ -662,8 +668,8 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const bf16x8 aq = lds_t_operand<C::kLd>(qt, c0, g, x);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          av[db][kb] = mfma16(ad, xch[(t - 1) & 1][0][kb][lane], av[db][kb]);
-          ak[db][kb] = mfma16(aq, xch[(t - 1) & 1][1][kb][lane], ak[db][kb]);
+          av[db][kb] = mfma16(ad, px[kb], av[db][kb]);
+          ak[db][kb] = mfma16(aq, dx[kb], ak[db][kb]);
         }
       }
     }
