@@ -21,7 +21,13 @@ CSRC = os.path.join(ROOT, "invariant_attention_flash_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc"
 
 
+_ASM = {}
+
+
 def _compile_asm(src, tmp_path):
+    """gfx950 assembly of one source (compiled once per test session)."""
+    if src in _ASM:
+        return _ASM[src]
     out = os.path.join(str(tmp_path), os.path.basename(src) + ".s")
     cmd = [HIPCC, "--offload-arch=gfx950", "--cuda-device-only", "-S", "-O3", "-std=c++17",
            "-fno-fast-math", "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
@@ -29,7 +35,8 @@ def _compile_asm(src, tmp_path):
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, src, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    return open(out).read()
+    _ASM[src] = open(out).read()
+    return _ASM[src]
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
@@ -56,3 +63,17 @@ def test_m0_only_in_direct_loads(name, tmp_path):
         if inside and "buffer_load_dwordx4" in code and code.rstrip().endswith("lds"):
             loads += 1
     assert loads > 0, "no direct loads found"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("name", [s for s in ia_build.SOURCES if s != "api.hip"])
+def test_kernels_use_no_scratch(name, tmp_path):
+    """Every kernel fits its registers: no spills to scratch memory (the
+    two-kind kernels rely on each kind's registers fitting two waves per
+    SIMD)."""
+    text = _compile_asm(os.path.join(CSRC, name), tmp_path)
+    kernels = re.findall(r"^\s*\.amdhsa_kernel\s+(\S+)", text, re.M)
+    sizes = re.findall(r"^\s*\.amdhsa_private_segment_fixed_size\s+(\d+)", text, re.M)
+    assert kernels and len(kernels) == len(sizes), name
+    spilled = [k for k, s in zip(kernels, sizes) if int(s) != 0]
+    assert not spilled, f"kernels with scratch in {name}: {spilled}"
