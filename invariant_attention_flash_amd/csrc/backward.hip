@@ -52,7 +52,10 @@ template <int D>
 struct BwdCfg {
   static constexpr int kSt = D / 32;     // k-steps over the head dim
   static constexpr int kDb = D / 16;     // 16-column blocks of the head dim
-  static constexpr int kLd = D + 8;      // LDS row stride in bf16 (16 bytes of padding)
+  // LDS row stride in bf16: 32 bytes of padding put the rows 8 banks apart,
+  // so neither the 16-byte row reads (8 rows) nor the transpose reads (4
+  // rows x 4 column groups) of a pass share a bank.
+  static constexpr int kLd = D + 16;
   // dk/dv: 32-pair halves per step (two independent halves where the LDS
   // budget allows); each half is one MFMA group of the fixed pair order.
   static constexpr int kHalves = D <= 256 ? 2 : 1;
@@ -63,9 +66,31 @@ struct BwdCfg {
   static_assert(D % 32 == 0, "head dim in MFMA k-steps");
 };
 
+// Key j is in row i's allowed set.  BITWISE: without short-circuits, so
+// that callers select rather than branch (the one-kind dk/dv kernel at head
+// dim 512 keeps the short-circuit form, which needs fewer live registers).
+template <bool BITWISE = true>
 __device__ __forceinline__ bool admits(int i, int j, int window, int ss, int se) {
-  const bool causal = j <= i && (window < 0 || i - j < window);
-  return causal || (j >= ss && j < se);
+  if constexpr (BITWISE) {
+    const bool causal = (j <= i) & ((window < 0) | (i - j < window));
+    return causal | ((j >= ss) & (j < se));
+  } else {
+    const bool causal = j <= i && (window < 0 || i - j < window);
+    return causal || (j >= ss && j < se);
+  }
+}
+
+// p = ok ? exp2(arg) : 0.  SELECT: exp2 always, then a select (no branch);
+// otherwise the compiler may branch around the exp2 (fewer live registers:
+// the one-kind dk/dv kernel at head dim 512 needs that).
+template <bool SELECT>
+__device__ __forceinline__ float masked_exp2(bool ok, float arg) {
+  if constexpr (SELECT) {
+    const float ex = fast_exp2(arg);
+    return ok ? ex : 0.f;
+  } else {
+    return ok ? fast_exp2(arg) : 0.f;
+  }
 }
 
 __device__ __forceinline__ void st_lds_x8(bf16* p, bf16x8 x) {
@@ -208,11 +233,13 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bf16* kt = kts[t & 1];
     const bf16* vt = vts[t & 1];
     // S^T and dP^T: keys 16kb + 4g + e of row x.
+    // Four independent MFMA chains (S and dP of both key blocks), k-steps
+    // outermost.
     f32x4 s[2], dp[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int st = 0; st < C::kSt; ++st) {
 #pragma unroll
-      for (int st = 0; st < C::kSt; ++st) {
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 ka = ld_lds_x8(kt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
         const bf16x8 va = ld_lds_x8(vt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
         s[kb] = mfma16(ka, qop[st], st == 0 ? f32x4{} : s[kb]);
@@ -225,9 +252,8 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = k0 + 16 * kb + 4 * g + e;
-        const float p = admits(ic, j, window, ss, se) && j < hi
-                            ? fast_exp2(__builtin_fmaf(s[kb][e], c2, -lse2))
-                            : 0.f;
+        const float p = masked_exp2<true>(admits(ic, j, window, ss, se) & (j < hi),
+                                          __builtin_fmaf(s[kb][e], c2, -lse2));
         ds[kb][e] = p * (dp[kb][e] - del);
       }
     }
@@ -393,6 +419,7 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int hf = 0; hf < C::kHalves; ++hf) {
       const bf16* qh = qt + 32 * hf * C::kLd;
       const bf16* dh = dt + 32 * hf * C::kLd;
+      // (Pair blocks outermost: at head dim 512 the other order spills.)
       f32x4 s[2], dp[2];
 #pragma unroll
       for (int pb = 0; pb < 2; ++pb) {
@@ -419,9 +446,9 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int av1[4] = {sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pv = rv[e] >= 0 && admits(rv[e], jc, window, av0[e], av1[e])
-                               ? fast_exp2(__builtin_fmaf(s[pb][e], c2, -l2[e]))
-                               : 0.f;
+          const float pv = masked_exp2<(D <= 256)>(
+              (rv[e] >= 0) && admits<(D <= 256)>(rv[e], jc, window, av0[e], av1[e]),
+              __builtin_fmaf(s[pb][e], c2, -l2[e]));
           p[pb][e] = pv;
           ds[pb][e] = pv * (dp[pb][e] - dl[e]);
         }
@@ -599,9 +626,9 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const bf16* dt = dts[cb];
         f32x4 sc[2], dp[2];
 #pragma unroll
-        for (int pb = 0; pb < 2; ++pb) {
+        for (int st = 0; st < C::kSt; ++st) {
 #pragma unroll
-          for (int st = 0; st < C::kSt; ++st) {
+          for (int pb = 0; pb < 2; ++pb) {
             const bf16x8 qa = ld_lds_x8(qt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
             const bf16x8 da = ld_lds_x8(dt + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
             sc[pb] = mfma16(qa, kop[st], st == 0 ? f32x4{} : sc[pb]);
@@ -622,9 +649,9 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           const int av1[4] = {sb.x, sb.y, sb.z, sb.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float pv = rv[e] >= 0 && admits(rv[e], jc, window, av0[e], av1[e])
-                                 ? fast_exp2(__builtin_fmaf(sc[pb][e], c2, -l2[e]))
-                                 : 0.f;
+            const float pv = masked_exp2<true>(
+                (rv[e] >= 0) & admits(rv[e], jc, window, av0[e], av1[e]),
+                __builtin_fmaf(sc[pb][e], c2, -l2[e]));
             p[pb][e] = pv;
             ds[pb][e] = pv * (dp[pb][e] - dl[e]);
           }
