@@ -119,6 +119,37 @@ int fetch_ints(const int32_t* dev, size_t n, std::vector<int32_t>& out, hipStrea
   return ATTN_OK;
 }
 
+// INVATTN_VALIDATE content checks of a packed varlen batch: cu_seqlens
+// starts at 0, never decreases and no sequence exceeds max_seqlen; spans are
+// non-empty, ascending, disjoint and each inside one sequence.  *tokens gets
+// cu_seqlens[batch].
+int validate_varlen(const int32_t* cu_seqlens, int batch, int max_seqlen, const int32_t* spans,
+                    int num_spans, hipStream_t s, long long* tokens) {
+  std::vector<int32_t> cu, sp;
+  int rc;
+  if ((rc = fetch_ints(cu_seqlens, (size_t)batch + 1, cu, s, "copy cu_seqlens")) != ATTN_OK) return rc;
+  if (cu[0] != 0) return fail(ATTN_E_VALIDATE, "cu_seqlens[0]=%d must be 0", cu[0]);
+  for (int b = 0; b < batch; ++b) {
+    const int len = cu[b + 1] - cu[b];
+    if (len < 0) return fail(ATTN_E_VALIDATE, "cu_seqlens decreases at %d", b);
+    if (len > max_seqlen)
+      return fail(ATTN_E_VALIDATE, "sequence %d has length %d > max_seqlen=%d", b, len, max_seqlen);
+  }
+  *tokens = cu[batch];
+  if ((rc = fetch_ints(spans, (size_t)num_spans * 2, sp, s, "copy spans")) != ATTN_OK) return rc;
+  int seq = 0;
+  for (int i = 0; i < num_spans; ++i) {
+    const int a = sp[2 * i], e = sp[2 * i + 1];
+    if (a >= e) return fail(ATTN_E_VALIDATE, "span %d is empty or reversed [%d,%d)", i, a, e);
+    if (i > 0 && a < sp[2 * i - 1])
+      return fail(ATTN_E_VALIDATE, "span %d overlaps or is out of order", i);
+    while (seq < batch && cu[seq + 1] <= a) ++seq;
+    if (seq >= batch || a < cu[seq] || e > cu[seq + 1])
+      return fail(ATTN_E_VALIDATE, "span %d [%d,%d) is not inside one sequence", i, a, e);
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,29 +214,10 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, fl
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   long long tokens = -1;
-  if (validate_enabled()) {
-    std::vector<int32_t> cu, sp;
-    if ((rc = fetch_ints(cu_seqlens, (size_t)batch + 1, cu, s, "copy cu_seqlens")) != ATTN_OK) return rc;
-    if (cu[0] != 0) return fail(ATTN_E_VALIDATE, "cu_seqlens[0]=%d must be 0", cu[0]);
-    for (int b = 0; b < batch; ++b) {
-      const int len = cu[b + 1] - cu[b];
-      if (len < 0) return fail(ATTN_E_VALIDATE, "cu_seqlens decreases at %d", b);
-      if (len > max_seqlen)
-        return fail(ATTN_E_VALIDATE, "sequence %d has length %d > max_seqlen=%d", b, len, max_seqlen);
-    }
-    tokens = cu[batch];
-    if ((rc = fetch_ints(spans_opt, (size_t)num_spans * 2, sp, s, "copy spans")) != ATTN_OK) return rc;
-    int seq = 0;
-    for (int i = 0; i < num_spans; ++i) {
-      const int a = sp[2 * i], e = sp[2 * i + 1];
-      if (a >= e) return fail(ATTN_E_VALIDATE, "span %d is empty or reversed [%d,%d)", i, a, e);
-      if (i > 0 && a < sp[2 * i - 1])
-        return fail(ATTN_E_VALIDATE, "span %d overlaps or is out of order", i);
-      while (seq < batch && cu[seq + 1] <= a) ++seq;
-      if (seq >= batch || a < cu[seq] || e > cu[seq + 1])
-        return fail(ATTN_E_VALIDATE, "span %d [%d,%d) is not inside one sequence", i, a, e);
-    }
-  }
+  if (validate_enabled() &&
+      (rc = validate_varlen(cu_seqlens, batch, max_seqlen, spans_opt, num_spans, s, &tokens)) !=
+          ATTN_OK)
+    return rc;
 
   PrefillArgs a{q, k, v, o, lse_opt, cu_seqlens, spans_opt, num_spans, batch, max_seqlen,
                 num_q_heads, num_kv_heads, head_dim, window, fold_scale(softmax_scale)};
@@ -365,18 +377,11 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, co
 
   long long tokens = -1;
   if (validate_enabled()) {
-    std::vector<int32_t> cu;
-    if ((rc = fetch_ints(cu_seqlens, (size_t)batch + 1, cu, s, "copy cu_seqlens")) != ATTN_OK) return rc;
-    if (cu[0] != 0) return fail(ATTN_E_VALIDATE, "cu_seqlens[0]=%d must be 0", cu[0]);
-    for (int b = 0; b < batch; ++b) {
-      const int len = cu[b + 1] - cu[b];
-      if (len < 0) return fail(ATTN_E_VALIDATE, "cu_seqlens decreases at %d", b);
-      if (len > max_seqlen)
-        return fail(ATTN_E_VALIDATE, "sequence %d has length %d > max_seqlen=%d", b, len, max_seqlen);
-    }
-    if (cu[batch] > total_tokens)
-      return fail(ATTN_E_VALIDATE, "cu_seqlens[batch]=%d > total_tokens=%d", cu[batch], total_tokens);
-    tokens = cu[batch];
+    if ((rc = validate_varlen(cu_seqlens, batch, max_seqlen, spans_opt, num_spans, s, &tokens)) !=
+        ATTN_OK)
+      return rc;
+    if (tokens > total_tokens)
+      return fail(ATTN_E_VALIDATE, "cu_seqlens[batch]=%lld > total_tokens=%d", tokens, total_tokens);
   }
 
   BackwardArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, spans_opt, num_spans,

@@ -217,3 +217,31 @@ def test_full_size_sliding_workload():
     grad_gate(full[0][sl], rq, "full dq")
     grad_gate(full[1][sl], rk, "full dk")
     grad_gate(full[2][sl], rv, "full dv")
+
+
+def test_validation_rejects_bad_indices(monkeypatch):
+    """INVATTN_VALIDATE=1: the backward applies the forward's index checks
+    (cu_seqlens, spans) and checks cu_seqlens[batch] against total_tokens."""
+    case = make_case("validate", [40, 30], 8, 4, 64, 16)
+    q, k, v, cu, _ = case.pack()
+    qt, kt, vt = bf16_dev(q), bf16_dev(k), bf16_dev(v)
+    o, lse = run_prefill(qt, kt, vt, cu, 64, 16, want_lse=True)
+    do = bf16_dev(case.dout)
+    monkeypatch.setenv("INVATTN_VALIDATE", "1")
+
+    def call(cu_, ms, spans=None, T=None):
+        spt = i32_dev(np.asarray(spans, np.int32).reshape(-1, 2)) if spans else None
+        n = q.shape[0] if T is None else T
+        return ia.attn_prefill_varlen_backward(qt[:n], kt[:n], vt[:n], o[:n], lse[:n], do[:n],
+                                               i32_dev(cu_), ms, window=16, spans=spt)
+
+    for bad in ((np.array([0, 50, 30], np.int32), 64, None, None),   # decreasing
+                (cu, 35, None, None),                                 # longer than max_seqlen
+                (cu, 64, [(30, 45)], None),                           # span crosses sequences
+                (cu, 64, None, 60)):                                  # past total_tokens
+        with pytest.raises(ia.AttnError) as e:
+            call(*bad)
+        assert e.value.name == "ATTN_E_VALIDATE", bad
+    dq, dk, dv = call(cu, 64, [(5, 20), (41, 60)])
+    torch.cuda.synchronize()
+    assert np.isfinite(dq.cpu().numpy()).all()
