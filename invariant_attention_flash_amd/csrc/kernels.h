@@ -78,7 +78,7 @@ struct PrefillSchedule {
 // to a multiple of 8*kXcdChunk; items past the end exit at once.  Only the
 // placement changes: a row's arithmetic never depends on its block.
 constexpr int kXcds = 8;
-constexpr int kXcdChunk = 32;
+constexpr int kXcdChunk = 8;
 
 __host__ __device__ inline long long xcd_padded_blocks(long long n) {
   const long long q = (long long)kXcds * kXcdChunk;
