@@ -372,7 +372,9 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, co
   if (!aligned4(cu_seqlens)) return fail(ATTN_E_ALIGN, "cu_seqlens is not 4-byte aligned");
   if (spans_opt && !aligned4(spans_opt)) return fail(ATTN_E_ALIGN, "spans_opt is not 4-byte aligned");
   const long long tiles = ((long long)max_seqlen + rows - 1) / rows;
-  if (tiles > 0x7fffffffLL) return fail(ATTN_E_UNSUPPORTED, "max_seqlen=%d too large", max_seqlen);
+  if (tiles * num_q_heads * batch > 0x7fffffffLL)
+    return fail(ATTN_E_UNSUPPORTED, "max_seqlen=%d x num_q_heads=%d x batch=%d needs more than 2^31 "
+                "workgroups", max_seqlen, num_q_heads, batch);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   long long tokens = -1;

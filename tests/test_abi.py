@@ -230,6 +230,7 @@ BACKWARD_ERRORS = [
     (dict(window=0), "ATTN_E_UNSUPPORTED", "window"),
     (dict(scale=float("nan")), "ATTN_E_UNSUPPORTED", "softmax_scale"),
     (dict(batch=70000), "ATTN_E_UNSUPPORTED", "65535"),
+    (dict(max_seqlen=1 << 30, hq=32, hkv=16, batch=65535), "ATTN_E_UNSUPPORTED", "2^31"),
     (dict(dk=(1 << 20) + 4), "ATTN_E_ALIGN", "dk is not 16-byte"),
     (dict(ws=(1 << 20) + 4), "ATTN_E_ALIGN", "workspace is not 16-byte"),
     (dict(lse=(1 << 20) + 2), "ATTN_E_ALIGN", "lse is not 4-byte"),
