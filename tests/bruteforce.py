@@ -10,13 +10,28 @@ from __future__ import annotations
 
 import numpy as np
 
-from invariant_attention_flash_amd.synth import bf16_to_f32
+
+def bf16_value(bits):
+    """Value of bf16 bit patterns (uint16) in fp64, from the format's fields:
+    sign bit 15, 8-bit biased exponent (bias 127), 7-bit fraction; exponent 0
+    is subnormal (fraction/128 * 2^-126), exponent 255 is inf/NaN.  Written
+    from the field definition, not by reinterpreting the upper half of an
+    fp32 word, so it is an independent rendering of the widening."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    f = (b & 0x7F).astype(np.float64)
+    normal = np.ldexp(1.0 + f / 128.0, (e - 127).astype(np.int32))
+    sub = np.ldexp(f / 128.0, -126)
+    special = np.where(f == 0, np.inf, np.nan)
+    val = np.where(e == 0, sub, np.where(e == 255, special, normal))
+    return sign * val
 
 
 def _f64(a):
     a = np.asarray(a)
     if a.dtype == np.uint16:
-        return bf16_to_f32(a).astype(np.float64)
+        return bf16_value(a)
     return a.astype(np.float64)
 
 

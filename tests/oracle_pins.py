@@ -313,9 +313,95 @@ def pin_backward_gqa_is_mha_summed(lib=None):
     assert np.abs(dv - dv2.reshape(11, 2, 2, 6).sum(axis=2)).max() <= 1e-12
 
 
+# ------------------------------------------------------ stored input formats
+# The GPU reads bf16 as given and every parity comparison feeds the oracle
+# the same bf16 bit patterns ("RFC: Gemma-4-31B-it train/rollout
+# consistency", section 4 item 5: inputs in their declared dtype; "Gated
+# RMSNorm CUDA kernel for the GDN block", accuracy against FP64 on the exact
+# stored inputs).  These pins fix the oracle's widening of those patterns.
+
+def _bf16_exact(bits):
+    """Exact value of one bf16 pattern from its fields, in Fractions."""
+    sign = -1 if bits >> 15 else 1
+    e, f = (bits >> 7) & 0xFF, bits & 0x7F
+    assert e != 255
+    if e == 0:
+        return sign * Fraction(f, 128) * Fraction(1, 2 ** 126)
+    return sign * (1 + Fraction(f, 128)) * (Fraction(2) ** (e - 127))
+
+
+_BF16_PATTERNS = [0x3F80, 0xBF80, 0x4040, 0x3FC0, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F,
+                  0xFF7F, 0x0000, 0x8000, 0x3E2A, 0xC2F7, 0x4B00, 0x3380, 0x1234, 0x5555]
+
+
+def pin_bf16_widening(lib=None):
+    """One-key rows return V exactly, so bf16 V patterns (normal, subnormal,
+    largest finite, signed zero) must come out as their exact values, and
+    likewise through the paged decode read."""
+    pats = np.array(_BF16_PATTERNS, np.uint16)
+    n = len(pats)
+    d = 4
+    v = np.zeros((n, 1, d), np.uint16)
+    for t in range(n):
+        for c in range(d):
+            v[t, 0, c] = pats[(t + c) % n]
+    rng = np.random.default_rng(29)
+    q = rng.integers(0x3C00, 0x4000, size=(n, 2, d)).astype(np.uint16)
+    k = rng.integers(0x3C00, 0x4000, size=(n, 1, d)).astype(np.uint16)
+    want = np.array([[float(_bf16_exact(int(v[t, 0, c]))) for c in range(d)] for t in range(n)])
+    o = oracle.prefill(q, k, v, np.arange(n + 1), lib=lib)      # every sequence one token
+    for h in range(2):
+        assert np.array_equal(o[:, h, :], want)
+    o = oracle.prefill(q, k, v, [0, n], window=1, lib=lib)      # window 1: own key only
+    assert np.array_equal(o[:, 0, :], want)
+    # decode: one-token contexts, cache block t holds token t
+    kc = np.zeros((n, 16, 1, d), np.uint16)
+    vc = np.zeros((n, 16, 1, d), np.uint16)
+    kc[:, 0] = k
+    vc[:, 0] = v
+    bt = np.arange(n, dtype=np.int32)[:, None]
+    o = oracle.decode(q, kc, vc, bt, np.ones(n, np.int32), lib=lib)
+    assert np.array_equal(o[:, 1, :], want)
+
+
+def _random_bf16(rng, shape):
+    """bf16 patterns with random sign and fraction and exponents 2^-5 .. 2^2."""
+    sign = rng.integers(0, 2, size=shape) << 15
+    exp = rng.integers(122, 130, size=shape) << 7
+    frac = rng.integers(0, 128, size=shape)
+    return (sign | exp | frac).astype(np.uint16)
+
+
+def pin_bruteforce_stored_formats(lib=None):
+    """The oracle on bf16 patterns and on fp32 values equals the brute force,
+    which decodes bf16 from its fields (prefill with windows, spans, GQA, and
+    paged decode)."""
+    rng = np.random.default_rng(31)
+    for lengths, hq, hkv, d, w, nsp in (([9, 26, 3], 4, 2, 16, 5, 1), ([40], 8, 1, 8, -1, 2)):
+        T = sum(lengths)
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        _, _, _, _, spans = _random_case(rng, lengths, hq, hkv, d, nsp)
+        for make in (lambda s: _random_bf16(rng, s),
+                     lambda s: rng.standard_normal(s).astype(np.float32)):
+            q, k, v = make((T, hq, d)), make((T, hkv, d)), make((T, hkv, d))
+            o, lse = oracle.prefill(q, k, v, cu, window=w, spans=spans or None, want_lse=True,
+                                    lib=lib)
+            bo, bl = bruteforce.attention(q, k, v, cu, window=w, spans=spans)
+            assert np.abs(o - bo).max() <= 1e-12, (q.dtype, lengths)
+            assert np.abs(lse - bl).max() <= 1e-12, (q.dtype, lengths)
+    lengths = [1, 16, 33]
+    for make in (lambda s: _random_bf16(rng, s), lambda s: rng.standard_normal(s).astype(np.float32)):
+        q, kc, vc, bt, sl = _decode_inputs(rng, lengths, 4, 2, 8, 16)
+        q, kc, vc = make(q.shape), make(kc.shape), make(vc.shape)
+        for w in (-1, 7):
+            o = oracle.decode(q, kc, vc, bt, sl, window=w, lib=lib)
+            assert np.abs(o - bruteforce.decode(q, kc, vc, bt, sl, window=w)).max() <= 1e-12
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_rows_sum_to_one,
             pin_window_covering_sequence_is_global, pin_one_token_returns_v,
             pin_zero_query_is_mean, pin_dominant_key, pin_gqa_reduces_to_mha,
             pin_packing_invariance, pin_row_subset, pin_decode,
             pin_backward_finite_differences, pin_backward_single_key,
-            pin_backward_gqa_is_mha_summed]
+            pin_backward_gqa_is_mha_summed, pin_bf16_widening,
+            pin_bruteforce_stored_formats]

@@ -34,6 +34,11 @@ MUTANTS = [
      "if (!allowed(i, j, -1, -1, -1)) continue;"),
     ("transposed query/key offset", "load_elem(q, qt, q_off + c) * load_elem(k, kvt, key_off[a] + c)",
      "load_elem(q, qt, q_off + c) * load_elem(k, kvt, key_off[n - 1 - a] + c)"),
+    ("bf16 widening without the shift", "[idx]) << 16;", "[idx]);"),
+    ("bf16 widening shifted by 15", "[idx]) << 16;", "[idx]) << 15;"),
+    ("bf16 element index off", "((const uint16_t*)base)[idx])", "((const uint16_t*)base)[idx ^ 1])"),
+    ("fp32 element index off", "((const float*)base)[idx];", "((const float*)base)[idx ^ 1];"),
+    ("fp32 read as bf16", "if (dtype == ORACLE_F32)", "if (dtype == -5)"),
     ("backward: ds sign", "double ds = p * (dp - del);", "double ds = p * (del - dp);"),
     ("backward: dk misses scale", "dkj[c] += scale * ds *", "dkj[c] += ds *"),
     ("backward: dv uses ds", "dvj[c] += p * load_elem(dout", "dvj[c] += ds * load_elem(dout"),
