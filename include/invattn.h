@@ -50,6 +50,10 @@
 extern "C" {
 #endif
 
+/* The HIP stream handle, declared as HIP's runtime header declares it, so
+ * this header needs no HIP include (the same typedef may appear twice). */
+typedef struct ihipStream_t* hipStream_t;
+
 /* Window value meaning "no window": a global (full causal) layer. */
 #define ATTN_WINDOW_NONE (-1)
 
@@ -107,7 +111,7 @@ enum {
  *              the kernel read out of bounds (ranges are clamped to the
  *              sequence) but give unspecified masks; INVATTN_VALIDATE=1
  *              rejects them.
- *   stream     HIP stream (hipStream_t) the work is enqueued on; 0 = default
+ *   stream     HIP stream the work is enqueued on; NULL = the default stream
  *
  * Supported: group size num_q_heads/num_kv_heads in {1, 2, 4, 8}.
  * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED, ATTN_E_ALIGN,
@@ -120,7 +124,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o,
                         int32_t num_q_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t window, float softmax_scale,
                         const int32_t* spans_opt, int32_t num_spans,
-                        void* stream);
+                        hipStream_t stream);
 
 /*
  * attn_prefill_paged -- chunked prefill: each sequence's new query tokens
@@ -176,7 +180,7 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                        int32_t num_blocks, int32_t block_size,
                        int32_t num_q_heads, int32_t num_kv_heads,
                        int32_t head_dim, int32_t window, float softmax_scale,
-                       void* stream);
+                       hipStream_t stream);
 
 /*
  * attn_prefill_varlen_backward -- gradients dq, dk, dv of
@@ -226,7 +230,7 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t window, float softmax_scale,
                                  const int32_t* spans_opt, int32_t num_spans,
-                                 void* stream);
+                                 hipStream_t stream);
 
 /*
  * attn_decode_workspace_size -- bytes of fp32 workspace attn_decode_paged
@@ -234,6 +238,11 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v,
  * ATTN_DECODE_CHUNK), head_dim + 4] fp32 (per chunk record: the unnormalised
  * accumulator, the running max, the running sum, one pad word keeping records
  * 16-byte aligned).  Pure function; returns 0 for non-positive arguments.
+ *
+ * Passage: a split-KV is allowed when its split and merge tree are fixed
+ * ("RFC: Gemma-4-31B-it train/rollout consistency", section 4, item 3); the
+ * chunk records are that split's partial results, and the caller owns their
+ * memory (the library allocates nothing).
  */
 size_t attn_decode_workspace_size(int32_t batch, int32_t max_seq_len,
                                   int32_t num_q_heads, int32_t head_dim);
@@ -286,19 +295,26 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int32_t block_size, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t window,
                       float softmax_scale, void* workspace,
-                      size_t workspace_bytes, void* o, void* stream);
+                      size_t workspace_bytes, void* o, hipStream_t stream);
 
 /* Text of the last failure on this thread ("" if none).  The pointer stays
- * valid until the next call on this thread. */
+ * valid until the next call on this thread.  Unsupported input fails closed
+ * with a named reason instead of falling back ("RFC: Gemma-4-31B-it
+ * train/rollout consistency", section 4, item 7). */
 const char* attn_last_error(void);
 
 /*
  * Provenance record of the last successful call on this thread
- * ("RFC: Gemma-4-31B-it train/rollout consistency", section 4, item 8):
- * JSON with requested/actual backend, kernel id, schedule id (tile sizes),
- * split policy, accumulator dtype, layer type, device, dtype, shape
- * fingerprint and fallback state.  Writes at most n bytes including the
- * terminating NUL; returns the full length, or -1 if no call succeeded yet.
+ * ("RFC: Gemma-4-31B-it train/rollout consistency", section 4, item 8), as
+ * one JSON object with the keys op, requested_backend, actual_backend,
+ * kernel_id (the kernel instances launched, with their template parameters),
+ * schedule_id (tile geometry), split_policy, accumulator_dtype, layer_type
+ * ("sliding" or "global"), device, arch, dtype, shape {batch, max_len,
+ * tokens (null unless INVATTN_VALIDATE=1 read it), num_q_heads,
+ * num_kv_heads, head_dim, window}, casts, exp, fallback ("none") and
+ * version.  With INVATTN_TRACE=1 every successful call also prints its
+ * record to stderr.  Writes at most n bytes including the terminating NUL;
+ * returns the full length, or -1 if no call succeeded yet.
  */
 int attn_last_provenance(char* buf, size_t n);
 

@@ -113,17 +113,37 @@ def _stream(stream):
 
 
 def _require(t, name, dtype, dim=None):
+    """Type, layout and rank of one tensor argument (the device is checked
+    by _on_one_gpu once every shape has been checked)."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on a GPU device")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dim is not None and t.dim() != dim:
         raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+
+
+def _shape(t, name, want):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} must have shape {tuple(want)}, got {tuple(t.shape)}")
+
+
+def _on_one_gpu(**tensors):
+    """Every tensor argument lives on the same GPU (the kernels read and
+    write them there)."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU device")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
 
 
 def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, window=ATTN_WINDOW_NONE,
@@ -147,14 +167,19 @@ def attn_prefill_varlen(q, k, v, cu_seqlens, max_seqlen, window=ATTN_WINDOW_NONE
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", torch.bfloat16, 3)
+    _shape(out, "out", q.shape)
     if lse is not None:
         _require(lse, "lse", torch.float32, 2)
+        _shape(lse, "lse", (T, hq))
     ns = 0
     if spans is not None:
         _require(spans, "spans", torch.int32, 2)
+        if spans.shape[1] != 2:
+            raise ValueError(f"spans must be [S, 2], got {tuple(spans.shape)}")
         ns = spans.shape[0]
         if ns == 0:
             spans = None
+    _on_one_gpu(q=q, k=k, v=v, cu_seqlens=cu_seqlens, out=out, lse=lse, spans=spans)
     if softmax_scale is None:
         softmax_scale = d ** -0.5
     rc = library().attn_prefill_varlen(
@@ -208,9 +233,13 @@ def attn_prefill_varlen_backward(q, k, v, out, lse, dout, cu_seqlens, max_seqlen
     ns = 0
     if spans is not None:
         _require(spans, "spans", torch.int32, 2)
+        if spans.shape[1] != 2:
+            raise ValueError(f"spans must be [S, 2], got {tuple(spans.shape)}")
         ns = spans.shape[0]
         if ns == 0:
             spans = None
+    _on_one_gpu(q=q, k=k, v=v, out=out, lse=lse, dout=dout, cu_seqlens=cu_seqlens, dq=dq, dk=dk,
+                dv=dv, workspace=workspace, spans=spans)
     if softmax_scale is None:
         softmax_scale = d ** -0.5
     rc = library().attn_prefill_varlen_backward(
@@ -251,8 +280,12 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens, q_start, ma
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", torch.bfloat16, 3)
+    _shape(out, "out", q.shape)
     if lse is not None:
         _require(lse, "lse", torch.float32, 2)
+        _shape(lse, "lse", (T, hq))
+    _on_one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                cu_seqlens=cu_seqlens, q_start=q_start, out=out, lse=lse)
     if softmax_scale is None:
         softmax_scale = d ** -0.5
     rc = library().attn_prefill_paged(
@@ -288,17 +321,24 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
     nb, bs, hkv, d2 = k_cache.shape
     if v_cache.shape != k_cache.shape or d2 != d:
         raise ValueError("caches must be [NB, BS, Hkv, D] matching q")
-    if softmax_scale is None:
-        softmax_scale = d ** -0.5
-    need = attn_decode_workspace_size(B, int(max_seq_len), hq, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous GPU tensor")
-    wbytes = workspace.numel() * workspace.element_size()
+    _shape(seq_lens, "seq_lens", (B,))
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table must have {B} rows (one per sequence), got "
+                         f"{block_table.shape[0]}")
     if out is None:
         out = torch.empty_like(q)
     _require(out, "out", torch.bfloat16, 3)
+    _shape(out, "out", q.shape)
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _on_one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                seq_lens=seq_lens, out=out, workspace=workspace)
+    need = attn_decode_workspace_size(B, int(max_seq_len), hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
     rc = library().attn_decode_paged(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(seq_lens), B, int(max_seq_len), nb, bs, hq, hkv, d, int(window),

@@ -9,13 +9,13 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libinvattn.so")
-SOURCES = ["api.hip", "prefill.hip", "prefill_split.hip", "prefill_ws.hip", "prefill_wide.hip",
-           "decode.hip", "backward.hip"]
+SOURCES = ["api.hip", "prefill.hip", "prefill_ws.hip", "decode.hip", "backward.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -44,19 +44,23 @@ def _run(cmd):
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source and link the shared library (always rebuilds)."""
+    """Compile every source (in parallel) and link the shared library
+    (always rebuilds)."""
     out_dir = os.path.join(ROOT, "_build")
     os.makedirs(out_dir, exist_ok=True)
-    objs = []
     flags = HIP_FLAGS + list(extra_flags or [])
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(out_dir, src.replace(".hip", ".o"))
-        cmd = [hipcc()] + flags + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                                   "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        _run(cmd)
+        cmds.append([hipcc()] + flags + ["-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                                         "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    for cmd in cmds if verbose else ():
+        print(" ".join(cmd), flush=True)
+    jobs = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as pool:
+        for f in [pool.submit(_run, c) for c in cmds]:
+            f.result()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

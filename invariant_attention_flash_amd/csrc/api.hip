@@ -64,24 +64,38 @@ std::string device_name(int dev) {
   return cached;
 }
 
+bool trace_enabled() {
+  const char* e = getenv("INVATTN_TRACE");
+  return e != nullptr && e[0] == '1';
+}
+
+// The record of a successful call; with INVATTN_TRACE=1 it is also printed
+// to stderr, one line per call.  `tokens` < 0: not known on the host (the
+// packed token count lives in device memory unless INVATTN_VALIDATE=1 copied
+// it).
 void set_provenance(const char* op, const char* kernel, const std::string& schedule,
                     const char* split, int window, int d, int hq, int hkv, int batch,
-                    long long tokens) {
+                    int max_len, long long tokens) {
   int dev = -1;
   (void)hipGetDevice(&dev);
-  char buf[1024];
+  char tok[32];
+  if (tokens >= 0) snprintf(tok, sizeof tok, "%lld", tokens);
+  else snprintf(tok, sizeof tok, "null");
+  char buf[1280];
   snprintf(buf, sizeof buf,
            "{\"op\":\"%s\",\"requested_backend\":\"invattn-hip\",\"actual_backend\":"
            "\"invattn-hip\",\"kernel_id\":\"%s\",\"schedule_id\":\"%s\",\"split_policy\":\"%s\","
            "\"accumulator_dtype\":\"fp32\",\"layer_type\":\"%s\",\"device\":%d,\"arch\":\"%s\","
-           "\"dtype\":\"bf16\",\"shape\":{\"batch\":%d,\"tokens\":%lld,\"num_q_heads\":%d,"
-           "\"num_kv_heads\":%d,\"head_dim\":%d,\"window\":%d},\"casts\":[\"p->bf16 rne\","
-           "\"o->bf16 rne\"],\"exp\":\"v_exp_f32\",\"fallback\":\"none\",\"version\":\"%s\"}",
+           "\"dtype\":\"bf16\",\"shape\":{\"batch\":%d,\"max_len\":%d,\"tokens\":%s,"
+           "\"num_q_heads\":%d,\"num_kv_heads\":%d,\"head_dim\":%d,\"window\":%d},"
+           "\"casts\":[\"p->bf16 rne\",\"o->bf16 rne\"],\"exp\":\"v_exp_f32\",\"fallback\":\"none\","
+           "\"version\":\"%s\"}",
            op, kernel, schedule.c_str(), split, layer_type(window), dev,
-           device_name(dev < 0 ? 0 : dev).c_str(), batch, tokens, hq, hkv, d, window,
+           device_name(dev < 0 ? 0 : dev).c_str(), batch, max_len, tok, hq, hkv, d, window,
            attn_version());
   g_prov = buf;
   g_have_prov = true;
+  if (trace_enabled()) fprintf(stderr, "invattn: %s\n", buf);
 }
 
 int check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t window, float scale) {
@@ -172,7 +186,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, fl
                         const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t window, float softmax_scale, const int32_t* spans_opt,
-                        int32_t num_spans, void* stream) {
+                        int32_t num_spans, hipStream_t stream) {
   g_err.clear();
   if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
   if (max_seqlen < 0) return fail(ATTN_E_SHAPE, "max_seqlen=%d must be >= 0", max_seqlen);
@@ -189,7 +203,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, fl
            sched.positions, sched.bn, sched.threads);
   if (batch == 0 || max_seqlen == 0) {
     set_provenance("attn_prefill_varlen", "none (empty input)", sid, "none", window, head_dim,
-                   num_q_heads, num_kv_heads, batch, 0);
+                   num_q_heads, num_kv_heads, batch, max_seqlen, 0);
     return ATTN_OK;
   }
   if (!q) return fail(ATTN_E_NULL, "q is NULL");
@@ -211,7 +225,7 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, fl
   if ((long long)max_seqlen * num_kv_heads * head_dim * 2 > 0x7fffffffLL)
     return fail(ATTN_E_UNSUPPORTED, "max_seqlen=%d x num_kv_heads=%d x head_dim=%d spans 2 GiB or more",
                 max_seqlen, num_kv_heads, head_dim);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
 
   long long tokens = -1;
   if (validate_enabled() &&
@@ -223,8 +237,8 @@ int attn_prefill_varlen(const void* q, const void* k, const void* v, void* o, fl
                 num_q_heads, num_kv_heads, head_dim, window, fold_scale(softmax_scale)};
   hipError_t e = launch_prefill(a, s);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  set_provenance("attn_prefill_varlen", "prefill_kernel", sid, "none (one ascending KV walk per row)",
-                 window, head_dim, num_q_heads, num_kv_heads, batch, tokens);
+  set_provenance("attn_prefill_varlen", sched.kernel, sid, "none (one ascending KV walk per row)",
+                 window, head_dim, num_q_heads, num_kv_heads, batch, max_seqlen, tokens);
   return ATTN_OK;
 }
 
@@ -233,7 +247,7 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, 
                        const int32_t* block_table, int32_t max_blocks_per_seq, int32_t batch,
                        int32_t max_query_len, int32_t max_context_len, int32_t num_blocks,
                        int32_t block_size, int32_t num_q_heads, int32_t num_kv_heads,
-                       int32_t head_dim, int32_t window, float softmax_scale, void* stream) {
+                       int32_t head_dim, int32_t window, float softmax_scale, hipStream_t stream) {
   g_err.clear();
   if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
   if (max_query_len < 0) return fail(ATTN_E_SHAPE, "max_query_len=%d must be >= 0", max_query_len);
@@ -250,7 +264,7 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, 
            sched.rows, sched.positions, sched.bn, sched.threads);
   if (batch == 0 || max_query_len == 0) {
     set_provenance("attn_prefill_paged", "none (empty input)", sid, "none", window, head_dim,
-                   num_q_heads, num_kv_heads, batch, 0);
+                   num_q_heads, num_kv_heads, batch, max_query_len, 0);
     return ATTN_OK;
   }
   if (max_context_len < max_query_len)
@@ -282,7 +296,7 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, 
   const long long tiles = ((long long)max_query_len + sched.positions - 1) / sched.positions + 1;
   if (tiles * num_kv_heads * batch > 0x7fffffffLL)
     return fail(ATTN_E_UNSUPPORTED, "max_query_len=%d too large", max_query_len);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
 
   long long tokens = -1;
   if (validate_enabled()) {
@@ -323,9 +337,9 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, 
   a.max_context = max_context_len;
   hipError_t e = launch_prefill(a, s);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
-  set_provenance("attn_prefill_paged", "prefill_kernel (paged keys)", sid,
-                 "none (one ascending KV walk per row)", window, head_dim, num_q_heads,
-                 num_kv_heads, batch, tokens);
+  const std::string kid = std::string("PagedOf ") + sched.kernel;
+  set_provenance("attn_prefill_paged", kid.c_str(), sid, "none (one ascending KV walk per row)",
+                 window, head_dim, num_q_heads, num_kv_heads, batch, max_query_len, tokens);
   return ATTN_OK;
 }
 
@@ -335,7 +349,7 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, co
                                  const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t window, float softmax_scale, const int32_t* spans_opt,
-                                 int32_t num_spans, void* stream) {
+                                 int32_t num_spans, hipStream_t stream) {
   g_err.clear();
   if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
   if (max_seqlen < 0) return fail(ATTN_E_SHAPE, "max_seqlen=%d must be >= 0", max_seqlen);
@@ -349,7 +363,7 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, co
   snprintf(sid, sizeof sid, "backward_d%d_rows%d_t256_fp32fma", head_dim, rows);
   if (batch == 0 || max_seqlen == 0) {
     set_provenance("attn_prefill_varlen_backward", "none (empty input)", sid, "none", window,
-                   head_dim, num_q_heads, num_kv_heads, batch, 0);
+                   head_dim, num_q_heads, num_kv_heads, batch, max_seqlen, 0);
     return ATTN_OK;
   }
   if (!q) return fail(ATTN_E_NULL, "q is NULL");
@@ -375,7 +389,7 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, co
   if (tiles * num_q_heads * batch > 0x7fffffffLL)
     return fail(ATTN_E_UNSUPPORTED, "max_seqlen=%d x num_q_heads=%d x batch=%d needs more than 2^31 "
                 "workgroups", max_seqlen, num_q_heads, batch);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
 
   long long tokens = -1;
   if (validate_enabled()) {
@@ -389,11 +403,12 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, co
   BackwardArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, cu_seqlens, spans_opt, num_spans,
                  batch, max_seqlen, num_q_heads, num_kv_heads, head_dim, window, softmax_scale,
                  fold_scale(softmax_scale)};
-  hipError_t e = launch_backward(a, s);
+  const char* kernel = "";
+  hipError_t e = launch_backward(a, s, &kernel);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
-  set_provenance("attn_prefill_varlen_backward", "bwd_dq_kernel+bwd_dkv_kernel", sid,
+  set_provenance("attn_prefill_varlen_backward", kernel, sid,
                  "none (one ascending walk per row and per key)", window, head_dim, num_q_heads,
-                 num_kv_heads, batch, tokens);
+                 num_kv_heads, batch, max_seqlen, tokens);
   return ATTN_OK;
 }
 
@@ -410,7 +425,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t window,
                       float softmax_scale, void* workspace, size_t workspace_bytes, void* o,
-                      void* stream) {
+                      hipStream_t stream) {
   g_err.clear();
   if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
   int rc = check_heads(num_q_heads, num_kv_heads, head_dim, window, softmax_scale);
@@ -426,7 +441,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
            kDecodeChunk);
   if (batch == 0) {
     set_provenance("attn_decode_paged", "none (empty input)", sid, split, window, head_dim,
-                   num_q_heads, num_kv_heads, batch, 0);
+                   num_q_heads, num_kv_heads, batch, max_seq_len, 0);
     return ATTN_OK;
   }
   if (max_seq_len <= 0) return fail(ATTN_E_SHAPE, "max_seq_len=%d must be >= 1", max_seq_len);
@@ -452,7 +467,7 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
   const size_t need = attn_decode_workspace_size(batch, max_seq_len, num_q_heads, head_dim);
   if (workspace_bytes < need)
     return fail(ATTN_E_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStream_t s = stream;
 
   long long tokens = -1;
   if (validate_enabled()) {
@@ -480,10 +495,11 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                max_seq_len, num_blocks, num_q_heads, num_kv_heads, head_dim, window,
                fold_scale(softmax_scale), reinterpret_cast<float*>(workspace),
                (max_seq_len + kDecodeChunk - 1) / kDecodeChunk, o};
-  hipError_t e = launch_decode(a, s);
+  const char* kernel = "";
+  hipError_t e = launch_decode(a, s, &kernel);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  set_provenance("attn_decode_paged", "decode_chunk_kernel+decode_merge_kernel", sid, split,
-                 window, head_dim, num_q_heads, num_kv_heads, batch, tokens);
+  set_provenance("attn_decode_paged", kernel, sid, split, window, head_dim, num_q_heads,
+                 num_kv_heads, batch, max_seq_len, tokens);
   return ATTN_OK;
 }
 

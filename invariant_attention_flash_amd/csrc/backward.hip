@@ -43,11 +43,6 @@ constexpr int kBwdThreads = 256;   // four waves
 constexpr int kBwdRows = 64;       // rows (dq) or keys (dk, dv) per workgroup: 16 per wave
 constexpr int kBwdTile = 32;       // keys (dq) or (row, head) pairs (dk, dv) per step
 
-// dk/dv at head dim 256 on the two-kind kernel (0: bwd_dkv_kernel).
-#ifndef BWD_WS
-#define BWD_WS 1
-#endif
-
 template <int D>
 struct BwdCfg {
   static constexpr int kSt = D / 32;     // k-steps over the head dim
@@ -773,7 +768,8 @@ hipError_t launch_bwd_d(const BackwardArgs& a, hipStream_t stream) {
                      a.num_spans, a.hq, a.hkv, a.window, a.scale, a.c2, tiles, a.batch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (D == 256 && BWD_WS)
+  // Head dim 256: dk/dv on the two-kind workgroup; 64 and 512: one kind.
+  if constexpr (D == 256)
     hipLaunchKernelGGL(bwd_dkv_ws_kernel<D>, dim3((unsigned)kv_blocks), dim3(2 * kBwdThreads), 0,
                        stream, (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.lse,
                        (const bf16*)a.dout, (const float*)a.delta, a.dk, a.dv, a.cu_seqlens,
@@ -794,11 +790,17 @@ int backward_rows_per_tile(int d) {
   return (d == 64 || d == 256 || d == 512) ? kBwdRows : 0;
 }
 
-hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, const char** kernel) {
   switch (a.d) {
-    case 64: return launch_bwd_d<64>(a, stream);
-    case 256: return launch_bwd_d<256>(a, stream);
-    case 512: return launch_bwd_d<512>(a, stream);
+    case 64:
+      *kernel = "bwd_dq_kernel<64>+bwd_dkv_kernel<64>";
+      return launch_bwd_d<64>(a, stream);
+    case 256:
+      *kernel = "bwd_dq_kernel<256>+bwd_dkv_ws_kernel<256>";
+      return launch_bwd_d<256>(a, stream);
+    case 512:
+      *kernel = "bwd_dq_kernel<512>+bwd_dkv_kernel<512>";
+      return launch_bwd_d<512>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

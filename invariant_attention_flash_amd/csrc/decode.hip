@@ -38,14 +38,12 @@ constexpr float kDecodeRescale = 8.0f;
 // Two waves per SIMD: registers are capped at 256 per lane, and two
 // workgroups share a CU (two 32 KB stages each at head dim 512), so one
 // workgroup's loads land while the other computes.
-#ifndef DC_OCC
-#define DC_OCC 2
-#endif
+constexpr int kDecodeOcc = 2;
 
 template <int D_, int G_, int NST_, int WAVES_>
 struct DecodeCfg {
   static constexpr bool kAliasKV = false;  // V read from the K cache (KvAliasOf<> sets it)
-  static constexpr int kOcc = DC_OCC;       // waves per SIMD the registers are sized for
+  static constexpr int kOcc = kDecodeOcc;     // waves per SIMD the registers are sized for
   static constexpr int D = D_, G = G_;
   static constexpr int kWaves = WAVES_;
   static constexpr int kThreads = 64 * kWaves;
@@ -328,22 +326,24 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Ring depth and waves per workgroup: fixed constants.
-#ifndef DC_NST
-#define DC_NST 2
-#endif
-#ifndef DC_WAVES
-#define DC_WAVES 4
-#endif
+// Ring depth (kDecodeRing stages of one cache block) and waves per
+// workgroup (four, or one per 16 head-dim columns at head dim 64): fixed
+// constants.
+constexpr int kDecodeRing = 2;
 #define INVATTN_DECODE_TABLE(X) \
   X(64, 1) X(64, 2) X(64, 4) X(64, 8)     \
   X(256, 1) X(256, 2) X(256, 4) X(256, 8) \
   X(512, 1) X(512, 2) X(512, 4) X(512, 8)
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const char** kernel) {
   const int group = a.hq / a.hkv;
-#define X(D, G) \
-  if (a.d == D && group == G) return launch_one<DecodeCfg<D, G, DC_NST, (DC_WAVES < D / 16 ? DC_WAVES : D / 16)>>(a, stream);
+  const bool alias = a.k_cache == a.v_cache;
+#define X(D, G)                                                                          \
+  if (a.d == D && group == G) {                                                          \
+    *kernel = alias ? "decode_chunk_kernel<KvAliasOf<" #D "," #G ">>+decode_merge_kernel<" #D ">" \
+                    : "decode_chunk_kernel<" #D "," #G ">+decode_merge_kernel<" #D ">";  \
+    return launch_one<DecodeCfg<D, G, kDecodeRing, (D / 16 < 4 ? D / 16 : 4)>>(a, stream); \
+  }
   INVATTN_DECODE_TABLE(X)
 #undef X
   return hipErrorInvalidValue;

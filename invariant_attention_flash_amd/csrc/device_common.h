@@ -12,7 +12,6 @@ typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
@@ -24,13 +23,6 @@ constexpr float kNegInf = -__builtin_inff();
 // Word 3 of a raw buffer resource (gfx9 family): 32-bit data format, no
 // swizzle, no index stride.  Loads past num_records return zeros.
 constexpr int kBufferFlags = 0x00020000;
-
-// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
-// Operand layout (lane l): A row l%32, k 8*(l/32)+s; B column l%32, same k.
-// Result: lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15.
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
 // Operand layout (lane l): A row l%16, k 8*(l/16)+s; B column l%16, same k.
@@ -108,95 +100,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// acc *= a for a 16x16 accumulator held in AGPRs (one wave per SIMD): each
-// element moves to a VGPR, is multiplied, and moves back.  The elements are
-// taken apart and put back so the vector itself never needs an address.
-__device__ __forceinline__ void scale_acc4(f32x4& acc, float a) {
-  float e[4] = {acc[0], acc[1], acc[2], acc[3]};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float t;
-    __asm__ volatile(
-        "v_accvgpr_read_b32 %1, %0\n\t"
-        "v_mul_f32 %1, %1, %2\n\t"
-        "v_accvgpr_write_b32 %0, %1"
-        : "+a"(e[i]), "=&v"(t)
-        : "v"(a));
-  }
-  acc = f32x4{e[0], e[1], e[2], e[3]};
-}
-
-// acc (=|+=) A * B on v_mfma_f32_16x16x32_bf16 with the accumulator in
-// VGPRs.  With one wave per SIMD the compiler puts every builtin MFMA
-// accumulator in AGPRs, and on gfx950 a read of an AGPR (v_accvgpr_read)
-// while MFMAs are in flight stalls for about ten cycles, so accumulators
-// that VALU code reads (attention scores) are formed here instead.  Hazards
-// are the caller's: A and B are not rewritten during the MFMA's first
-// passes (they come from LDS reads waited for before, or stay fixed), acc is
-// only chained through these MFMAs, and the caller waits (mfma_drain) before
-// VALU code reads it.
-__device__ __forceinline__ void mfma16_vacc_first(f32x4& acc, bf16x8 a, bf16x8 b) {
-  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma16_vacc(f32x4& acc, bf16x8 a, bf16x8 b) {
-  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-
-// acc (=|+=) A * B on v_mfma_f32_16x16x32_bf16 with the accumulator pinned
-// to AGPRs (one wave per SIMD keeps large accumulators there).  Written as
-// volatile inline asm so the register allocator never moves accumulators
-// through VGPRs and LDS reads keep their source order around the MFMAs (the
-// caller places operand reads ahead by hand).  Hazard distances are the
-// caller's: no VALU write of a or b in the two cycles before, no VALU read
-// of acc within 18 cycles after.
-__device__ __forceinline__ void mfma16_agpr_first(f32x4& acc, bf16x8 a, bf16x8 b) {
-  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma16_agpr(f32x4& acc, bf16x8 a, bf16x8 b) {
-  __asm__ volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Wait states between the last accumulator MFMA and VALU reads of it.
-__device__ __forceinline__ void mfma_drain() {
-  __asm__ volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
-}
-
-// A zero accumulator created in AGPRs (a 16x16x32 MFMA of zero operands with
-// an inline-constant zero addend), so a loop-carried accumulator is AGPR from
-// its first definition on.
-__device__ __forceinline__ f32x4 agpr_zero4() {
-  f32x4 r;
-  const bf16x8 z = {};
-  // The nop keeps the zero operand's VALU writes three wait states away.
-  __asm__("s_nop 2\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(r) : "v"(z));
-  return r;
-}
-
 // Wait until every vector-memory load of this wave (including direct
 // HBM -> LDS loads) has completed.
 __device__ __forceinline__ void wait_vmem() {
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// acc *= a.  With one wave per SIMD the accumulators live in AGPRs; the
-// scaling is written on AGPR operands so they stay there (each element moves
-// to a VGPR, is multiplied, and moves back).
-template <int OCC>
-__device__ __forceinline__ void scale_acc(f32x16& acc, float a) {
-  if constexpr (OCC == 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float t;
-      __asm__ volatile(
-          "v_accvgpr_read_b32 %1, %0\n\t"
-          "v_mul_f32 %1, %1, %2\n\t"
-          "v_accvgpr_write_b32 %0, %1"
-          : "+a"(acc[i]), "=&v"(t)
-          : "v"(a));
-    }
-  } else {
-    acc *= a;
-  }
 }
 
 // Wait until at most `n` vector-memory loads of this wave are outstanding

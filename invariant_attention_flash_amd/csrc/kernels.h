@@ -67,6 +67,7 @@ struct PrefillSchedule {
   int positions;  // sequence positions per workgroup
   int bn;         // keys per KV tile
   int threads;
+  const char* kernel;  // the kernel instance: name<head dim, group, parameters>
 };
 
 // Prefill block order.  The hardware hands consecutive workgroups to the 8
@@ -93,16 +94,8 @@ __device__ inline long long xcd_logical_block(long long i) {
 bool prefill_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
-// Head dim 512 (prefill_wide.hip); prefill_schedule / launch_prefill
-// dispatch to these.
-bool prefill_wide_schedule(int d, int group, PrefillSchedule* s);
-hipError_t launch_prefill_wide(const PrefillArgs& a, hipStream_t stream);
-
-// Head dim 256 (prefill_split.hip): the PV product split over head-dim
-// columns across the waves of a workgroup.
-bool prefill_split_schedule(int d, int group, PrefillSchedule* s);
-hipError_t launch_prefill_split(const PrefillArgs& a, hipStream_t stream);
-// Head dim 256 (prefill_ws.hip): score waves and PV waves, two per SIMD.
+// Head dims 256 and 512 (prefill_ws.hip): score waves and PV waves, two per
+// SIMD; prefill_schedule / launch_prefill dispatch to these.
 bool prefill_ws_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream);
 
@@ -132,12 +125,14 @@ struct BackwardArgs {
   float c2;  // fl32(scale * log2(e))
 };
 int backward_rows_per_tile(int d);
-hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+// *kernel: the instances launched (a static string).
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream, const char** kernel);
 
 constexpr int kDecodeChunk = 512;  // keys per split chunk (fixed; ATTN_DECODE_CHUNK)
 constexpr int kDecodeStage = 16;   // keys per pipeline stage inside a chunk (one cache block)
 constexpr int decode_record_floats(int d) { return d + 4; }  // acc[d], m, l, pad
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// *kernel: the instances launched (a static string).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const char** kernel);
 
 }  // namespace invattn

@@ -1,7 +1,7 @@
 // prefill.hip -- batch-invariant attention forward over packed
 // variable-length sequences (sliding-window and global layers, GQA,
-// bidirectional spans), bf16 MFMA on gfx950.  Head dims 64 and 256 run the
-// kernel below; head dim 512 runs prefill_wide.hip.
+// bidirectional spans), bf16 MFMA on gfx950.  Head dim 64 runs the kernel
+// below; head dims 256 and 512 run prefill_ws.hip.
 //
 // Sources: sliding and global attention cores are separate layer types with
 // their own head geometry and masks ("RFC: Gemma-4-31B-it train/rollout
@@ -425,55 +425,34 @@ static hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One kernel instance per (head_dim, group).  Parameters after (D, G): row
-// blocks of 16 per wave, stage ring depth.  All fixed per instance.
-#ifndef PF_CFG64
-#define PF_CFG64 4, 5
-#endif
-#ifndef PF_CFG256
-#define PF_CFG256 2, 5
-#endif
-#define INVATTN_PREFILL_TABLE(X)                                              \
-  X(64, 1, PF_CFG64) X(64, 2, PF_CFG64) X(64, 4, PF_CFG64) X(64, 8, PF_CFG64) \
-  X(256, 1, PF_CFG256) X(256, 2, PF_CFG256) X(256, 4, PF_CFG256)              \
-  X(256, 8, PF_CFG256)
-
-#ifndef PF_SPLIT256
-#define PF_SPLIT256 1
-#endif
-#ifndef PF_WS256
-#define PF_WS256 1
-#endif
-#ifndef PF_WS512
-#define PF_WS512 1
-#endif
-
-static bool use_ws(int d) { return (d == 256 && PF_WS256) || (d == 512 && PF_WS512); }
+// One kernel instance per group at head dim 64: four row blocks of 16 per
+// wave, a ring of five stage buffers.  Head dims 256 and 512 run the
+// two-kind kernel of prefill_ws.hip.
+#define INVATTN_PREFILL64_TABLE(X) X(64, 1) X(64, 2) X(64, 4) X(64, 8)
 
 bool prefill_schedule(int d, int group, PrefillSchedule* s) {
-  if (use_ws(d) && prefill_ws_schedule(d, group, s)) return true;
-  if (PF_SPLIT256 && prefill_split_schedule(d, group, s)) return true;
-#define X(D, G, ...)                                                          \
+  if (prefill_ws_schedule(d, group, s)) return true;
+#define X(D, G)                                                               \
   if (d == D && group == G) {                                                 \
-    using C = Pf16Cfg<D, G, __VA_ARGS__>;                                     \
-    *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads};        \
+    using C = Pf16Cfg<D, G, 4, 5>;                                            \
+    *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads,         \
+                         "prefill_kernel<" #D "," #G ",4,5>"};                \
     return true;                                                              \
   }
-  INVATTN_PREFILL_TABLE(X)
+  INVATTN_PREFILL64_TABLE(X)
 #undef X
-  return prefill_wide_schedule(d, group, s);
+  return false;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
   PrefillSchedule sp;
-  if (use_ws(a.d) && prefill_ws_schedule(a.d, group, &sp)) return launch_prefill_ws(a, stream);
-  if (PF_SPLIT256 && prefill_split_schedule(a.d, group, &sp)) return launch_prefill_split(a, stream);
-#define X(D, G, ...) \
-  if (a.d == D && group == G) return launch_one<Pf16Cfg<D, G, __VA_ARGS__>>(a, stream);
-  INVATTN_PREFILL_TABLE(X)
+  if (prefill_ws_schedule(a.d, group, &sp)) return launch_prefill_ws(a, stream);
+#define X(D, G) \
+  if (a.d == D && group == G) return launch_one<Pf16Cfg<D, G, 4, 5>>(a, stream);
+  INVATTN_PREFILL64_TABLE(X)
 #undef X
-  return launch_prefill_wide(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace invattn

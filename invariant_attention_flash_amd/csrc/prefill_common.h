@@ -1,5 +1,5 @@
 // prefill_common.h -- pieces shared by the 16x16x32 prefill kernels
-// (prefill.hip, prefill_split.hip): per-lane constants, the direct
+// (prefill.hip, prefill_ws.hip) and decode: per-lane constants, the direct
 // HBM -> LDS tile loads and the online softmax of one 32-key tile.
 //
 // Sources: the numerical contract of "RFC: Gemma-4-31B-it train/rollout
@@ -347,7 +347,8 @@ __device__ __forceinline__ uint32_t softmax_move(const f32x4 (*s)[2], int k0, co
 //   * a row's reference max m moves when some p = 2^(fma(s, c, -m)) of the
 //     tile exceeds 2^kRescale (the tile max exceeds m by more than kRescale,
 //     up to the rounding of the exponent), or, while m = -inf, when the tile
-//     holds an allowed key; the fast path then needs no row max;
+//     holds an allowed key (whatever its p against the provisional 0); the
+//     fast path then needs no row max;
 //   * the running sum is kept per lane: each lane adds its 8 slots of a tile
 //     in slot order, (((p0 + p1) + p2) + ...) + p7, to its own l (scaled by
 //     alpha on a move), and the four lanes of a row are combined once, after
@@ -399,6 +400,7 @@ struct TileSoftmax {
   static constexpr int kStages = 8 * RB;
   float part[RB];   // the lane's tile sum (slot order)
   float pmax[RB];   // the lane's largest p
+  bool anyok[RB];   // MASK: some slot of the lane holds an allowed key
   bf16x8 pb[RB];    // P operand
   int wbase[RB], sbase[RB];
   uint32_t slen[RB];
@@ -426,6 +428,7 @@ struct TileSoftmax {
       const bool ok = ((uint32_t)(wbase[rb] - c) < (uint32_t)ln.wlim) |
                       ((uint32_t)(sbase[rb] + c) < slen[rb]);
       x = ok ? x : kNegInf;
+      anyok[rb] = e == 0 ? ok : (anyok[rb] | ok);
     }
     const float p = fast_exp2(__builtin_fmaf(x, ln.c2, -st.msub[rb]));
     pb[rb][e] = to_bf16(p);
@@ -439,11 +442,18 @@ struct TileSoftmax {
   }
 
   // After the stages: true when some row of the wave may move (then move()
-  // finishes the tile), else every lane adds its tile sum.
+  // finishes the tile), else every lane adds its tile sum.  A row may move
+  // when one of its p exceeds the threshold, or, while its m = -inf (thr =
+  // 0), when one of its keys in the tile is allowed: its scores may all be
+  // so low that every p underflows to 0 against the provisional msub = 0,
+  // and the row must still take its first reference max here.
   __device__ __forceinline__ bool finish(RowStats<RB>& st) {
     bool trig = false;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) trig |= pmax[rb] > st.thr[rb];
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool first = st.thr[rb] == 0.f;
+      trig |= (pmax[rb] > st.thr[rb]) | (first & (MASK ? anyok[rb] : true));
+    }
     if (__builtin_amdgcn_ballot_w64(trig) != 0) return true;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) st.l[rb] += part[rb];
@@ -451,7 +461,8 @@ struct TileSoftmax {
   }
 
   // The rare path.  A row moves when its largest p (over the row's lanes)
-  // exceeds its threshold: m moves to the tile max, the lane sums and the
+  // exceeds its threshold, or, while m = -inf, when the tile holds one of
+  // its allowed keys: m moves to the tile max, the lane sums and the
   // accumulator scale by alpha = 2^(m_old - m_new) (1 when m_old = -inf:
   // both are still exact zeros) and p is recomputed; other rows add their
   // fast-path sums.  Returns the scaling mask (bit rb: some row of block rb
@@ -466,16 +477,19 @@ struct TileSoftmax {
       HalfPair hp = half_pair(pmax[rb]);
       const float t = fmaxf(hp.lo, hp.hi);
       hp = row_pair(t);
-      const bool mv = fmaxf(hp.lo, hp.hi) > st.thr[rb];
-      if (__builtin_amdgcn_ballot_w64(mv) == 0) {
+      bool mv = fmaxf(hp.lo, hp.hi) > st.thr[rb];
+      const float m_old = st.m[rb];
+      const bool first = m_old == kNegInf;
+      if (__builtin_amdgcn_ballot_w64(mv | first) == 0) {
         st.l[rb] += part[rb];
         continue;
       }
       float x[8];
       tile_values<MASK>(s, rb, k0, ln, qpos, ss, se, x);
-      const float m_old = st.m[rb];
-      const float m_new = mv ? row_max_scaled(x, ln.c2) : m_old;
-      const float a = (mv & (m_old != kNegInf)) ? fast_exp2(m_old - m_new) : 1.f;
+      const float tmax = row_max_scaled(x, ln.c2);
+      mv = first ? (tmax != kNegInf) : mv;
+      const float m_new = mv ? tmax : m_old;
+      const float a = (mv & !first) ? fast_exp2(m_old - m_new) : 1.f;
       bf16x8 pnew;
       const float snew = probs_lane(x, ln.c2, mv ? m_new : st.msub[rb], pnew);
       if (mv) {

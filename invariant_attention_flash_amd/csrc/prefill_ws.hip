@@ -39,10 +39,7 @@
 // K and V tiles (32 keys, ascending) stream HBM -> LDS with direct loads into
 // two rings of NR buffers (3 at head dim 256, 2 at 512 where a tile is
 // 32 KB); one LDS barrier per step orders the rings, the P exchange and the
-// flags.  Keys past the sequence end load as zeros and are masked.  At head
-// dim 256 every output element sees the same sequence of MFMAs and scalings
-// as in the one-wave-per-SIMD kernel of prefill_split.hip, so the bytes are
-// the same.
+// flags.  Keys past the sequence end load as zeros and are masked.
 #include <type_traits>
 
 #include "device_common.h"
@@ -507,18 +504,16 @@ static hipError_t launch_ws(const PrefillArgs& a, hipStream_t stream) {
 // row blocks per score wave (Q of 16*RB rows in 64 VGPRs: 2 at head dim 256,
 // 1 at 512), buffers per K/V ring (3 at 256; 2 at 512, where a tile of 32
 // keys is 32 KB).
-#define PF_WS_CFG256 2, 3
-#define PF_WS_CFG512 1, 2
-#define INVATTN_WS_TABLE(X)                                                            \
-  X(256, 1, PF_WS_CFG256) X(256, 2, PF_WS_CFG256) X(256, 4, PF_WS_CFG256)              \
-  X(256, 8, PF_WS_CFG256) X(512, 1, PF_WS_CFG512) X(512, 2, PF_WS_CFG512)              \
-  X(512, 4, PF_WS_CFG512) X(512, 8, PF_WS_CFG512)
+#define INVATTN_WS_TABLE(X)                                       \
+  X(256, 1, 2, 3) X(256, 2, 2, 3) X(256, 4, 2, 3) X(256, 8, 2, 3) \
+  X(512, 1, 1, 2) X(512, 2, 1, 2) X(512, 4, 1, 2) X(512, 8, 1, 2)
 
 bool prefill_ws_schedule(int d, int group, PrefillSchedule* s) {
-#define X(D, G, ...)                                                          \
+#define X(D, G, RB, NR)                                                       \
   if (d == D && group == G) {                                                 \
-    using C = PfWsCfg<D, G, __VA_ARGS__>;                                     \
-    *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads};        \
+    using C = PfWsCfg<D, G, RB, NR>;                                          \
+    *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads,         \
+                         "prefill_ws_kernel<" #D "," #G "," #RB "," #NR ">"}; \
     return true;                                                              \
   }
   INVATTN_WS_TABLE(X)
@@ -528,8 +523,8 @@ bool prefill_ws_schedule(int d, int group, PrefillSchedule* s) {
 
 hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
-#define X(D, G, ...) \
-  if (a.d == D && group == G) return launch_ws<PfWsCfg<D, G, __VA_ARGS__>>(a, stream);
+#define X(D, G, RB, NR) \
+  if (a.d == D && group == G) return launch_ws<PfWsCfg<D, G, RB, NR>>(a, stream);
   INVATTN_WS_TABLE(X)
 #undef X
   return hipErrorInvalidValue;

@@ -117,6 +117,49 @@ def test_single_key_returns_v_exactly(d):
     assert np.array_equal(bits(o), np.repeat(v, 4, axis=1))
 
 
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (256, 8, 4), (512, 8, 1)])
+def test_underflowing_rows_take_their_first_max(d, hq, hkv):
+    """Softmax scale 30: many rows' scaled scores lie below -150, so every p
+    underflows against the provisional reference 0 of a row that has not
+    seen an allowed key yet.  The row must still take its first reference
+    max (from the allowed keys, not from p > 0): with window 1 the output is
+    V to the bit and the LSE is the row's own scaled score; with wider
+    windows it matches the oracle.  Every head dim's kernel and the decode of
+    the last rows agree with the oracle."""
+    scale = 30.0
+    case = synth.prefill_case(23, [1, 70, 33], hq, hkv, d, 1, std=0.5)
+    case.scale = scale
+    packed, o, lse = run_case(case, want_lse=True)
+    q, k, v, cu, _ = packed
+    assert np.array_equal(bits(o), np.repeat(v, hq // hkv, axis=1))
+    ref_o, ref_lse = oracle_of(packed, case, want_lse=True)
+    got_lse = lse.cpu().numpy()
+    assert np.isfinite(got_lse).all()
+    assert (ref_lse < -100).any()                      # the case really underflows
+    assert np.abs(got_lse - ref_lse).max() <= 1e-5 * np.abs(ref_lse).max() + 1e-3
+    for w in (3, 40, synth.NO_WINDOW):
+        case.window = w
+        packed, o, lse = run_case(case, want_lse=True)
+        ref_o, ref_lse = oracle_of(packed, case, want_lse=True)
+        gate(f64(o), ref_o, f"scale 30, window {w}")
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-5 * np.abs(ref_lse).max() + 1e-3
+    # the same rows through the paged decode: each sequence's last row
+    for b in range(len(cu) - 1):
+        L = int(cu[b + 1] - cu[b])
+        nblk = (L + 15) // 16
+        kc = np.zeros((nblk, 16, hkv, d), np.uint16)
+        vc = np.zeros((nblk, 16, hkv, d), np.uint16)
+        kc.reshape(-1, hkv, d)[:L] = k[cu[b]:cu[b + 1]]
+        vc.reshape(-1, hkv, d)[:L] = v[cu[b]:cu[b + 1]]
+        qd = q[cu[b + 1] - 1][None]
+        bt = np.arange(nblk, dtype=np.int32)[None]
+        sl = np.array([L], np.int32)
+        od = ia.attn_decode_paged(bf16_dev(qd), bf16_dev(kc), bf16_dev(vc), i32_dev(bt),
+                                  i32_dev(sl), L, window=synth.NO_WINDOW, softmax_scale=scale)
+        torch.cuda.synchronize()
+        gate(f64(od)[0], ref_o[cu[b + 1] - 1], f"decode seq {b}")
+
+
 def test_window_covering_sequence_is_global_bytes():
     case = synth.prefill_case(4, [200, 333], 8, 4, 256, synth.NO_WINDOW)
     _, og, _ = run_case(case)
@@ -222,4 +265,6 @@ def test_provenance_record():
     assert p["op"] == "attn_prefill_varlen" and p["fallback"] == "none"
     assert p["accumulator_dtype"] == "fp32" and p["layer_type"] == "global"
     assert p["schedule_id"].startswith("prefill_d512_g8")
+    assert p["kernel_id"] == "prefill_ws_kernel<512,8,1,2>"
+    assert p["shape"]["max_len"] == 64
     assert p["arch"].startswith("gfx950")
