@@ -2,19 +2,26 @@
 """Benchmark of the batch-invariant attention forward on one MI355X.
 
 One step = one pass of the whole hot path on synthetic inputs resident in
-HBM: a packed varlen sliding-window prefill (8 sequences, lengths U[512, 4096],
-32 query / 16 KV heads, head dim 256, window 1024, bf16 N(0,1)*0.5), then a
-paged-KV decode of 64 sequences (contexts U[1024, 32768], 32 query / 4 KV
-heads, head dim 512, 16-token blocks, shuffled block tables, global layer).
+HBM: the hybrid multimodal-style prefill (5 sliding-window layers with head
+dim 256, window 1024, 32 query / 16 KV heads, then 1 global layer with head
+dim 512, 32 query / 4 KV heads, over a packed batch of 4 sequences of 4096
+tokens, each holding two bidirectional 256-token spans; independent bf16
+N(0,1)*0.5 Q/K/V per layer), then a paged-KV decode of 64 sequences
+(contexts U[1024, 32768], 32 query / 4 KV heads, head dim 512, 16-token
+blocks, shuffled block tables).
 
-Printed: one JSON line.  ``value`` is the prefill's algorithmic TFLOP/s
-(4 * head_dim * query_heads * allowed query-key pairs, masked work not
-counted) over its HIP-event-timed launches; the decode's algorithmic HBM GB/s
-(K and V of every attended context token, plus q, o and block-table reads) is
-reported beside it with its own roofline, and the backward (dq, dk, dv) of
-the same prefill in a timed region of its own.  The fp64 CPU oracle is timed on a
-bounded sample of the same prefill rows on the host cores (reported baseline,
-not a target), and its outputs double as a parity spot-check.
+``value`` is the hybrid prefill's algorithmic TFLOP/s: 4 * head_dim *
+query_heads * allowed query-key pairs summed over the six layers (masked work
+not counted), over the HIP-event-timed launches of the six layers.  Reported
+beside it, each with its own roofline: every layer; the sliding-window
+prefill over 8 sequences of U[512, 4096] tokens and the global prefill over
+{2048, 4096, 6144, 8192} tokens (their own timed regions); the decode's
+algorithmic HBM GB/s (K and V of every attended context token, plus q, o and
+block-table reads) at batch 64 in the step and at batches 1, 8, 32, 64 with
+the last-level cache flushed before each call; and the backward (dq, dk, dv)
+of the sliding prefill.  The fp64 CPU oracle is timed on bounded samples of
+the same hybrid rows and decode sequences on the host cores (a reported
+baseline, not a target), and its outputs double as parity spot-checks.
 """
 from __future__ import annotations
 
@@ -22,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -32,14 +40,15 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FLUSH_BYTES = 512 << 20     # written between decode calls: twice the 256 MB last-level cache
 
-
-# The prefill kernel the benchmark times (head dim 256, group 2): its name in
-# rocprofv3 output and the key of its HBM traffic in profiles/traffic.json.
-PREFILL_TRAFFIC_KEY = "prefill_ws_kernel<256,2>"
-PREFILL_KERNEL_MATCH = "prefill_ws_kernel<invattn::PfWsCfg<256, 2, "
-PREFILL_KERNEL_FIRST = "prefill_ws_kernel"
-PREFILL_KERNEL_LABEL = "prefill_ws_kernel (head_dim 256, group 2)"
+# Kernel instances, by the name rocprofv3 prints (demangled), and the key of
+# their HBM traffic in profiles/traffic.json.
+KERNELS = {
+    "prefill_ws_kernel<256,2,2,3>": "prefill_ws_kernel<invattn::PfWsCfg<256, 2, 2, 3> >",
+    "prefill_ws_kernel<512,8,1,2>": "prefill_ws_kernel<invattn::PfWsCfg<512, 8, 1, 2> >",
+    "decode_chunk_kernel<512,8>+decode_merge_kernel<512>": "decode_",
+}
 
 
 def kernel_sources_hash() -> str:
@@ -50,6 +59,16 @@ def kernel_sources_hash() -> str:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def allowed_pairs_per_row(L, window, spans=()):
@@ -99,19 +118,13 @@ def load_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-# The backward's two kernels form their five products (and the recomputed
-# scores and dP) as bf16 MFMAs, so their roofline is the bf16 matrix peak.
-BACKWARD_BOUND = "mfma"
-BACKWARD_PEAK = PEAK_BF16_TFLOPS
-BACKWARD_KERNEL_LABEL = "bwd_dq_kernel<256> + bwd_dkv_kernel<256> (one launch pair)"
-
 CALIBRATION_BYTES = 1 << 30   # plain streaming kernel used to scale the HBM byte counters
 
 
 def write_traffic(fetch_dir, write_dir):
     """Turn two rocprofv3 counter runs of `bench.py --calibrate` (FETCH_SIZE,
     then WRITE_SIZE, KiB per dispatch) into profiles/traffic.json: per-launch
-    HBM bytes of the prefill and decode kernels, each counter scaled so the
+    HBM bytes of each benchmarked kernel, each counter scaled so the
     calibration copy of CALIBRATION_BYTES reads (writes) exactly that much."""
     import csv
     import glob
@@ -132,17 +145,17 @@ def write_traffic(fetch_dir, write_dir):
         if not calib:
             raise SystemExit(f"no calibration kernel found in {d}")
         scale = CALIBRATION_BYTES / (1024.0 * float(np.median(calib)))
-        for key, match, first in ((PREFILL_TRAFFIC_KEY, PREFILL_KERNEL_MATCH, PREFILL_KERNEL_FIRST),
-                                  ("decode_chunk_kernel+decode_merge_kernel<512,8>", "decode_",
-                                   "decode_chunk_kernel")):
-            vals = [v for k, v, g in rows if match in k]
-            launches = sum(1 for k, v, g in rows if match in k and first in k)
+        for key, match in KERNELS.items():
+            first = "decode_chunk_kernel" if key.startswith("decode") else match
+            vals = [v for k, v, g in rows if match in k and "KvAliasOf" not in k]
+            launches = sum(1 for k, v, g in rows if first in k and "KvAliasOf" not in k)
             if not vals or not launches:
                 continue
             per_launch = 1024.0 * scale * sum(vals) / launches
             rec = out.setdefault(key, {"sources_hash": kernel_sources_hash()})
             rec[counter.lower() + "_bytes"] = per_launch
             rec[counter.lower() + "_scale"] = scale
+            rec["launches_" + counter.lower()] = launches
     for rec in out.values():
         rec["bytes_per_launch"] = rec.get("fetch_size_bytes", 0.0) + rec.get("write_size_bytes", 0.0)
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -151,16 +164,28 @@ def write_traffic(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+def roofline(bound, achieved, peak, unit, kernel, work, ms, traffic_key=None):
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak,
+            "traffic": load_traffic(traffic_key) if traffic_key else None,
+            "kernel": kernel, "work_per_launch": work, "avg_launch_ms": ms}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--reps", type=int, default=20,
+                    help="timed calls of each reported workload outside the step")
     ap.add_argument("--backward-steps", type=int, default=3,
-                    help="timed calls of the backward on the prefill workload (0 disables)")
+                    help="timed calls of the backward on the sliding workload (0 disables)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target CPU time of the oracle sample (0 disables)")
+                    help="target CPU time of the prefill oracle sample (0 disables every "
+                         "oracle leg)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the step (six hybrid layers + batch-64 decode): the "
+                         "command the kernel traces and counters are taken on")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB copy (scale for the HBM byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -185,16 +210,36 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ia.library()
+    stream = torch.cuda.current_stream()   # the library launches on this stream
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # ---------------- inputs (resident in HBM before timing)
-    lengths = synth.sliding_lengths(2, 8, 512, 4096)
-    HQ, HKV, D, W = 32, 16, 256, 1024
-    pf = synth.prefill_case_device(2, lengths, HQ, HKV, D, W, std=0.5, device=dev)
-    pf_out = torch.empty_like(pf["q"])
-    flops, pairs = prefill_flops(lengths, HQ, D, W)
+    HY_N, HY_LEN = 4, 4096
+    hy_spans = synth.hybrid_spans(5, HY_N, HY_LEN, 256)
+    layers = []
+    for li, (hq, hkv, d, w) in enumerate(synth.HYBRID_LAYERS):
+        case = synth.prefill_case_device(5 * 100 + li, [HY_LEN] * HY_N, hq, hkv, d, w, std=0.5,
+                                         spans=hy_spans, device=dev)
+        fl, pr = prefill_flops([HY_LEN] * HY_N, hq, d, w, hy_spans)
+        case["flops"], case["pairs"] = fl, pr
+        case["out"] = torch.empty_like(case["q"])
+        layers.append(case)
+    hy_flops = sum(c["flops"] for c in layers)
+    log(f"hybrid inputs ready: {hy_flops:.4g} FLOP over {len(layers)} layers")
 
-    DB = args.decode_batch
-    dlen = synth.decode_lengths(4, 64, 1024, 32768)[:DB]
+    sl_len = synth.sliding_lengths(2, 8, 512, 4096)
+    sl = synth.prefill_case_device(2, sl_len, 32, 16, 256, 1024, std=0.5, device=dev)
+    sl["flops"], sl["pairs"] = prefill_flops(sl_len, 32, 256, 1024)
+    sl["out"] = torch.empty_like(sl["q"])
+    gl_len = [2048, 4096, 6144, 8192]
+    gl = synth.prefill_case_device(3, gl_len, 32, 4, 512, -1, std=0.5, device=dev)
+    gl["flops"], gl["pairs"] = prefill_flops(gl_len, 32, 512, -1)
+    gl["out"] = torch.empty_like(gl["q"])
+
+    DB = 64
+    dlen = synth.decode_lengths(4, DB, 1024, 32768)
     dc = synth.decode_case_device(4, dlen, batch=DB, hq=32, hkv=4, d=512, device=dev)
     d_bt = torch.from_numpy(dc["block_table"]).to(dev)
     d_sl = torch.from_numpy(dc["seq_lens"]).to(dev)
@@ -202,16 +247,19 @@ def main():
     ws = torch.empty(ia.attn_decode_workspace_size(DB, d_max, 32, 512), dtype=torch.uint8,
                      device=dev)
     d_out = torch.empty_like(dc["q"])
-    dbytes = decode_bytes(dlen, 32, 4, 512)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    log("all inputs resident")
 
-    def prefill():
-        ia.attn_prefill_varlen(pf["q"], pf["k"], pf["v"], pf["cu_seqlens"], pf["max_seqlen"],
-                               window=W, softmax_scale=pf["scale"], out=pf_out)
+    def prefill(c):
+        ia.attn_prefill_varlen(c["q"], c["k"], c["v"], c["cu_seqlens"], c["max_seqlen"],
+                               window=c["window"], softmax_scale=c["scale"], spans=c["spans"],
+                               out=c["out"])
 
-    def decode():
-        ia.attn_decode_paged(dc["q"], dc["k_cache"], dc["v_cache"], d_bt, d_sl, d_max,
-                             softmax_scale=dc["scale"], workspace=ws, out=d_out)
+    def decode(B, out=None):
+        ia.attn_decode_paged(dc["q"][:B], dc["k_cache"], dc["v_cache"], d_bt[:B], d_sl[:B],
+                             int(max(dlen[:B])), softmax_scale=dc["scale"], workspace=ws,
+                             out=d_out[:B] if out is None else out)
 
     if args.calibrate:
         # plain streaming kernel of known traffic: reads and writes 1 GiB
@@ -223,121 +271,232 @@ def main():
         del src, dst
 
     for _ in range(args.warmup):
-        prefill()
-        decode()
+        for c in layers:
+            prefill(c)
+        decode(DB)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()   # the library launches on this stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ---------------- the step: six hybrid layers, then the batch-64 decode
+    nl = len(layers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 2)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
         e[0].record(stream)
-        prefill()
-        e[1].record(stream)
-        decode()
-        e[2].record(stream)
+        for li, c in enumerate(layers):
+            prefill(c)
+            e[li + 1].record(stream)
+        decode(DB)
+        e[nl + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pf_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    dc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    layer_ms = [float(np.mean([e[li].elapsed_time(e[li + 1]) for e in evs])) for li in range(nl)]
+    hy_ms = float(np.mean([e[0].elapsed_time(e[nl]) for e in evs]))
+    dc_ms = float(np.mean([e[nl].elapsed_time(e[nl + 1]) for e in evs]))
     ms_step = wall * 1e3 / args.steps
+    hy_tflops = hy_flops / (hy_ms * 1e-3) / 1e12
+    log(f"step: hybrid {hy_ms:.3f} ms ({hy_tflops:.1f} TFLOP/s), decode {dc_ms:.3f} ms")
 
-    pf_tflops = flops / (pf_ms * 1e-3) / 1e12
+    def layer_kernel(c):
+        return ("prefill_ws_kernel<256,2,2,3>" if c["d"] == 256 else "prefill_ws_kernel<512,8,1,2>")
 
-    # ---------------- backward of the same prefill (its own timed region,
-    # not part of the step): dq, dk, dv for a seeded upstream gradient
+    per_layer = []
+    kern_ms, kern_flops = {}, {}
+    for c, ms in zip(layers, layer_ms):
+        tf = c["flops"] / (ms * 1e-3) / 1e12
+        k = layer_kernel(c)
+        kern_ms[k] = kern_ms.get(k, 0.0) + ms
+        kern_flops[k] = kern_flops.get(k, 0.0) + c["flops"]
+        per_layer.append({"kind": "global" if c["window"] < 0 else "sliding", "kernel": k,
+                          "ms": ms, "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS,
+                          "pairs": c["pairs"]})
+    # the dominant kernel of the step: the instance with the most time
+    dom = max(kern_ms, key=kern_ms.get)
+    n_dom = sum(1 for c in layers if layer_kernel(c) == dom)
+    dom_tf = kern_flops[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    hy_roof = roofline("mfma", dom_tf, PEAK_BF16_TFLOPS, "TFLOP/s", dom,
+                       f"{kern_flops[dom] / n_dom:.4g} FLOP per launch ({n_dom} launches per step: "
+                       "4*head_dim*32*allowed pairs)", kern_ms[dom] / n_dom, dom)
+    hy_roof["all_layers"] = {"achieved": hy_tflops, "frac": hy_tflops / PEAK_BF16_TFLOPS,
+                             "flops": hy_flops, "ms": hy_ms}
+
+    # ---------------- the sliding and global prefills (timed regions of their own)
+    def time_calls(fn, reps, before=None):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            if before is not None:
+                before()
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        return [x[0].elapsed_time(x[1]) for x in ev]
+
+    reported = {}
+    for name, c, k in (() if args.step_only else
+                       (("sliding_prefill", sl, "prefill_ws_kernel<256,2,2,3>"),
+                        ("global_prefill", gl, "prefill_ws_kernel<512,8,1,2>"))):
+        prefill(c)
+        t = time_calls(lambda: prefill(c), args.reps)
+        ms = float(np.mean(t))
+        tf = c["flops"] / (ms * 1e-3) / 1e12
+        reported[name] = {
+            "value": tf, "unit": "TFLOP/s", "ms_mean": ms, "ms_min": float(np.min(t)),
+            "tokens": int(sum(c["lengths"])), "lengths": c["lengths"], "pairs": c["pairs"],
+            "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", k,
+                                 f"{c['flops']:.4g} FLOP = 4*{c['d']}*32*{c['pairs']} allowed "
+                                 "pairs", ms, k)}
+        log(f"{name}: {ms:.3f} ms ({tf:.1f} TFLOP/s)")
+
+    # ---------------- decode at every batch size, last-level cache flushed
+    def flush_llc():
+        flush.fill_(1.0)
+
+    sweep = {}
+    for B in () if args.step_only else (1, 8, 32, 64):
+        decode(B)
+        t = time_calls(lambda: decode(B), args.reps, before=flush_llc)
+        ms = float(np.mean(t))
+        nbytes = decode_bytes(dlen[:B], 32, 4, 512)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        sweep[str(B)] = {"GB/s": gbs, "frac": gbs / PEAK_HBM_GBS, "ms_mean": ms,
+                         "ms_min": float(np.min(t)), "bytes": nbytes,
+                         "context_tokens": int(sum(dlen[:B]))}
+        log(f"decode B={B}: {ms * 1e3:.1f} us ({gbs:.0f} GB/s)")
+    # one sequence's output bytes at every batch size (batch invariance, checked live)
+    outs = {}
+    for B in (1, 64) if args.step_only else (1, 8, 32, 64):
+        o = torch.empty_like(dc["q"][:B])
+        decode(B, out=o)
+        outs[B] = o[0].clone()
+    torch.cuda.synchronize()
+    invariant = all(torch.equal(outs[1].view(torch.int16), outs[B].view(torch.int16))
+                    for B in outs)
+    dbytes = decode_bytes(dlen, 32, 4, 512)
+    dc_gbs = dbytes / (dc_ms * 1e-3) / 1e9
+    dkey = "decode_chunk_kernel<512,8>+decode_merge_kernel<512>"
+    dc_roof = roofline("hbm", dc_gbs, PEAK_HBM_GBS, "GB/s", dkey,
+                       f"{dbytes} B: K+V of {sum(dlen)} context tokens x 4 KV heads x 512 x 2 B "
+                       "x 2, plus q, o, block tables", dc_ms, dkey)
+
+    # ---------------- backward of the sliding prefill (its own timed region)
     bw = None
-    if args.backward_steps > 0:
-        lse = torch.empty(pf["q"].shape[:2], dtype=torch.float32, device=dev)
-        ia.attn_prefill_varlen(pf["q"], pf["k"], pf["v"], pf["cu_seqlens"], pf["max_seqlen"],
-                               window=W, softmax_scale=pf["scale"], out=pf_out, lse=lse)
-        g = torch.from_numpy(synth.upstream_grad(2, tuple(pf["q"].shape)).view(np.int16))
+    if args.backward_steps > 0 and not args.step_only:
+        lse = torch.empty(sl["q"].shape[:2], dtype=torch.float32, device=dev)
+        ia.attn_prefill_varlen(sl["q"], sl["k"], sl["v"], sl["cu_seqlens"], sl["max_seqlen"],
+                               window=1024, softmax_scale=sl["scale"], out=sl["out"], lse=lse)
+        g = torch.from_numpy(synth.upstream_grad(2, tuple(sl["q"].shape)).view(np.int16))
         dout = g.view(torch.bfloat16).to(dev)
-        dq = torch.empty(pf["q"].shape, dtype=torch.float32, device=dev)
-        dk = torch.empty(pf["k"].shape, dtype=torch.float32, device=dev)
-        dv = torch.empty(pf["k"].shape, dtype=torch.float32, device=dev)
-        bws = torch.empty(pf["q"].shape[:2], dtype=torch.float32, device=dev)
+        dq = torch.empty(sl["q"].shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(sl["k"].shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(sl["k"].shape, dtype=torch.float32, device=dev)
+        bws = torch.empty(sl["q"].shape[:2], dtype=torch.float32, device=dev)
 
         def backward():
-            ia.attn_prefill_varlen_backward(pf["q"], pf["k"], pf["v"], pf_out, lse, dout,
-                                            pf["cu_seqlens"], pf["max_seqlen"], window=W,
-                                            softmax_scale=pf["scale"], dq=dq, dk=dk, dv=dv,
+            ia.attn_prefill_varlen_backward(sl["q"], sl["k"], sl["v"], sl["out"], lse, dout,
+                                            sl["cu_seqlens"], sl["max_seqlen"], window=1024,
+                                            softmax_scale=sl["scale"], dq=dq, dk=dk, dv=dv,
                                             workspace=bws)
 
         backward()
-        torch.cuda.synchronize()
-        bev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-               for _ in range(args.backward_steps)]
-        for e in bev:
-            e[0].record(stream)
-            backward()
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        bw_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in bev]))
-        bw_flops = 2.5 * flops   # five products of D per allowed pair and head
+        t = time_calls(backward, args.backward_steps)
+        bw_ms = float(np.mean(t))
+        bw_flops = 2.5 * sl["flops"]   # five products of D per allowed pair and head
         bw_tf = bw_flops / (bw_ms * 1e-3) / 1e12
         bw = {"value": bw_tf, "unit": "TFLOP/s", "calls": args.backward_steps,
-              "roofline": {"bound": BACKWARD_BOUND, "achieved": bw_tf, "peak": BACKWARD_PEAK,
-                           "unit": "TFLOP/s", "frac": bw_tf / BACKWARD_PEAK, "traffic": None,
-                           "kernel": BACKWARD_KERNEL_LABEL,
-                           "work_per_launch": f"{bw_flops:.4g} FLOP = 10*256*32*{pairs} "
-                                              "allowed pairs (dq, dk, dv of the prefill)",
-                           "avg_launch_ms": bw_ms}}
+              "roofline": roofline("mfma", bw_tf, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                   "bwd_dq_kernel<256> + bwd_dkv_ws_kernel<256> (one launch pair)",
+                                   f"{bw_flops:.4g} FLOP = 10*256*32*{sl['pairs']} allowed pairs "
+                                   "(dq, dk, dv of the sliding prefill)", bw_ms)}
+        log(f"backward: {bw_ms:.3f} ms ({bw_tf:.1f} TFLOP/s)")
         del dq, dk, dv, bws, dout, lse
-    dc_gbs = dbytes / (dc_ms * 1e-3) / 1e9
 
-    # ---------------- CPU oracle baseline + parity spot-check on sampled rows
+    # ---------------- CPU oracle baselines + parity spot-checks on sampled rows
     cpu = None
     parity = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.step_only:
         import oracle
-        q = pf["q"].cpu().view(torch.int16).numpy().view(np.uint16)
-        k = pf["k"].cpu().view(torch.int16).numpy().view(np.uint16)
-        v = pf["v"].cpu().view(torch.int16).numpy().view(np.uint16)
-        got = pf_out.cpu().view(torch.int16).numpy().view(np.uint16)
-        cu = pf["cu_host"]
-        T = int(cu[-1])
-        per_row = np.concatenate([allowed_pairs_per_row(L, W) for L in lengths])
-        rng = np.random.default_rng(12345)
         threads = oracle.num_threads()
 
-        def run(n):
-            rows = np.stack([rng.integers(0, T, n), rng.integers(0, HQ, n)], 1)
-            t = time.perf_counter()
-            o = oracle.prefill(q, k, v, cu, window=W, scale=pf["scale"], rows=rows)
-            return rows, o, time.perf_counter() - t
+        def host_bits(t):
+            return t.cpu().view(torch.int16).numpy().view(np.uint16)
 
-        rows, o, dt = run(512)
-        rate = (4.0 * D * per_row[rows[:, 0]]).sum() / max(dt, 1e-6)
-        n = int(min(T * HQ, max(512, rate * args.cpu_seconds / (4.0 * D * per_row.mean()))))
-        rows, o, dt = run(n)
-        cpu_flops = float((4.0 * D * per_row[rows[:, 0]]).sum())
-        cpu = {"value": cpu_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{n} seeded (token, head) rows of the same prefill "
-                         f"({n / (T * HQ):.1%} of {T * HQ}), fp64, {dt:.1f} s"}
-        g = synth.bf16_to_f32(got[rows[:, 0], rows[:, 1]]).astype(np.float64)
-        err = float(np.abs(g - o).max())
-        rel = float(np.linalg.norm(g - o) / np.linalg.norm(o))
-        parity = {"rows": n, "max_abs": err, "rel_l2": rel, "pass": err <= 2e-2 and rel <= 1e-2}
+        hosts = []
+        for c in layers:
+            hosts.append({"q": host_bits(c["q"]), "k": host_bits(c["k"]), "v": host_bits(c["v"]),
+                          "out": host_bits(c["out"]), "cu": c["cu_host"],
+                          "spans": c["spans_host"],
+                          "per_row": np.concatenate([allowed_pairs_per_row(HY_LEN, c["window"],
+                                                                           hy_spans[i])
+                                                     for i in range(HY_N)])})
+        rng = np.random.default_rng(12345)
 
-    pf_roof = {"bound": "mfma", "achieved": pf_tflops, "peak": PEAK_BF16_TFLOPS,
-               "unit": "TFLOP/s", "frac": pf_tflops / PEAK_BF16_TFLOPS,
-               "traffic": load_traffic(PREFILL_TRAFFIC_KEY),
-               "kernel": PREFILL_KERNEL_LABEL,
-               "work_per_launch": f"{flops:.4g} FLOP = 4*256*32*{pairs} allowed pairs",
-               "avg_launch_ms": pf_ms}
-    dc_roof = {"bound": "hbm", "achieved": dc_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-               "frac": dc_gbs / PEAK_HBM_GBS,
-               "traffic": load_traffic("decode_chunk_kernel+decode_merge_kernel<512,8>"),
-               "kernel": "decode_chunk_kernel + decode_merge_kernel (head_dim 512, group 8)",
-               "work_per_launch": f"{dbytes} B: K+V of {sum(dlen)} context tokens x 4 KV heads "
-                                  f"x 512 x 2 B x 2, plus q, o, block tables",
-               "avg_launch_ms": dc_ms}
+        def sample(n_per_layer):
+            """n rows per layer; returns (CPU seconds, FLOP, per-layer (max-abs, rel, n))."""
+            dt, fl, par = 0.0, 0.0, []
+            for c, h in zip(layers, hosts):
+                T = int(h["cu"][-1])
+                rows = np.stack([rng.integers(0, T, n_per_layer),
+                                 rng.integers(0, c["hq"], n_per_layer)], 1)
+                t = time.perf_counter()
+                o = oracle.prefill(h["q"], h["k"], h["v"], h["cu"], window=c["window"],
+                                   scale=c["scale"], spans=h["spans"], rows=rows)
+                dt += time.perf_counter() - t
+                fl += float((4.0 * c["d"] * h["per_row"][rows[:, 0]]).sum())
+                got = synth.bf16_to_f32(h["out"][rows[:, 0], rows[:, 1]]).astype(np.float64)
+                err = np.abs(got - o)
+                par.append((err.max(), float((err ** 2).sum()), float((o ** 2).sum())))
+            return dt, fl, par
+
+        # rounds of 256 rows per layer until the oracle has run cpu_seconds
+        dt = fl = 0.0
+        n = 0
+        acc = [[0.0, 0.0, 0.0] for _ in layers]
+        while dt < args.cpu_seconds and n < HY_N * HY_LEN * 32:
+            d_, f_, par = sample(256)
+            dt, fl, n = dt + d_, fl + f_, n + 256
+            for a, (mx, e2, o2) in zip(acc, par):
+                a[0] = max(a[0], mx)
+                a[1] += e2
+                a[2] += o2
+        par = [(a[0], float(np.sqrt(a[1] / a[2])), n) for a in acc]
+        cpu = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(),
+               "sample": f"{n} seeded (token, head) rows of each of the {nl} hybrid layers "
+                         f"({n * nl} rows, {n / (HY_N * HY_LEN * 32):.2%} of each layer), fp64, "
+                         f"{dt:.1f} s"}
+        log(f"prefill oracle: {n * nl} rows in {dt:.1f} s")
+        parity = {"rows_per_layer": n,
+                  "layers": [{"max_abs": a, "rel_l2": r} for a, r, _ in par],
+                  "max_abs": max(a for a, _, _ in par), "rel_l2": max(r for _, r, _ in par)}
+        parity["pass"] = parity["max_abs"] <= 2e-2 and parity["rel_l2"] <= 1e-2
+
+        # decode oracle: the batch-1 decode (sequence 0, whole context) on the host
+        L0 = int(dlen[0])
+        nb0 = (L0 + 15) // 16
+        ids = d_bt[0, :nb0].long()
+        kc0 = host_bits(dc["k_cache"].index_select(0, ids))
+        vc0 = host_bits(dc["v_cache"].index_select(0, ids))
+        q0 = host_bits(dc["q"][:1])
+        bt0 = np.arange(nb0, dtype=np.int32)[None]
+        t = time.perf_counter()
+        od = oracle.decode(q0, kc0, vc0, bt0, np.array([L0], np.int32), scale=dc["scale"])
+        ddt = time.perf_counter() - t
+        got = synth.bf16_to_f32(host_bits(outs[1])).astype(np.float64)
+        cpu["decode"] = {"value": decode_bytes(dlen[:1], 32, 4, 512) / ddt / 1e9, "unit": "GB/s",
+                         "cores": threads, "kind": "oracle",
+                         "sample": f"the batch-1 decode (context {L0}), fp64, {ddt:.2f} s"}
+        parity["decode_batch1"] = {"max_abs": float(np.abs(got - od[0]).max()),
+                                   "rel_l2": float(np.linalg.norm(got - od[0])
+                                                   / np.linalg.norm(od[0]))}
+        parity["pass"] = parity["pass"] and parity["decode_batch1"]["max_abs"] <= 2e-2 and \
+            parity["decode_batch1"]["rel_l2"] <= 1e-2
+
     rec = {
         "metric": "prefill TFLOP/s + decode HBM GB/s at 1 GPU, bitwise batch-invariant",
-        "value": pf_tflops,
+        "value": hy_tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -349,16 +508,23 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "sliding-window prefill: packed varlen batch of 8 sequences, lengths "
-                        f"U[512,4096] (seed 2: {lengths}), 32 query / 16 KV heads, head_dim 256, "
-                        "causal window 1024, bf16 N(0,1)*0.5, fp32 accumulation",
-            "tokens": int(sum(lengths)),
+            "workload": "hybrid multimodal-style prefill: 5 sliding layers (window 1024, head_dim "
+                        "256, 32 query / 16 KV heads) + 1 global layer (head_dim 512, 32 query / "
+                        "4 KV heads) over a packed batch of 4 sequences of 4096 tokens, each with "
+                        "two bidirectional 256-token spans (seed 5), bf16 N(0,1)*0.5, fp32 "
+                        "accumulation; then paged decode, batch 64",
+            "tokens": HY_N * HY_LEN,
+            "spans": hy_spans,
             "decode_workload": f"paged decode: batch {DB}, contexts U[1024,32768] (seed 4), "
                                "32 query / 4 KV heads, head_dim 512, block 16, shuffled tables",
         },
-        "roofline": pf_roof,
+        "roofline": hy_roof,
+        "hybrid_layers": per_layer,
         "decode": {"value": dc_gbs, "unit": "GB/s", "roofline": dc_roof,
-                   "context_tokens": int(sum(dlen))},
+                   "context_tokens": int(sum(dlen)),
+                   "batch_sweep_llc_flushed": sweep,
+                   "seq0_bytes_equal_at_every_batch": bool(invariant)},
+        **reported,
         "backward": bw,
         "cpu_baseline": cpu,
         "parity_sample": parity,
