@@ -297,6 +297,42 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       float softmax_scale, void* workspace,
                       size_t workspace_bytes, void* o, hipStream_t stream);
 
+/* Bytes of the static scratch array attn_decode_paged_noalloc keeps its
+ * chunk records in (held on each GPU the library runs on until the process
+ * ends). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It takes no workspace: the chunk
+ * records go to a static device array of ATTN_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU, so the call allocates nothing (no hipMalloc,
+ * no hipFree).  The caller still passes every input and the output.
+ *
+ * Arguments, layouts, kernels and output bytes are those of
+ * attn_decode_paged (without workspace and workspace_bytes).
+ * Limit: attn_decode_workspace_size(batch, max_seq_len, num_q_heads,
+ * head_dim) must not exceed ATTN_NOALLOC_SCRATCH_BYTES (64 MiB: at 32 query
+ * heads and head dim 512, batch x ceil(max_seq_len / ATTN_DECODE_CHUNK) <=
+ * 1016), else ATTN_E_WORKSPACE and nothing is enqueued.
+ * Sharing: every call on one GPU uses that GPU's one array and leaves its
+ * records there; calls that overlap on one GPU (on two streams, or from two
+ * host threads before the first has finished on the device) race and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero.
+ * The first call on a device looks up the array's device address, with that
+ * device current.  INVATTN_VALIDATE=1 copies the index tensors to the host
+ * and synchronises the stream (not for use under capture).
+ * Errors: as attn_decode_paged.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t batch,
+                              int32_t max_seq_len, int32_t num_blocks,
+                              int32_t block_size, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                              float softmax_scale, void* o, hipStream_t stream);
+
 /* Text of the last failure on this thread ("" if none).  The pointer stays
  * valid until the next call on this thread.  Unsupported input fails closed
  * with a named reason instead of falling back ("RFC: Gemma-4-31B-it

@@ -14,6 +14,9 @@ Entry points (same names as the C ABI):
   attn_prefill_paged   chunked prefill: new query tokens against the keys of
                        a paged KV cache (cached prefix plus the chunk)
   attn_decode_paged    one query token per sequence over a paged KV cache
+  attn_decode_paged_noalloc
+                       the same without a workspace (the library's static
+                       scratch), for callers that cannot allocate
   attn_decode_workspace_size
 """
 from __future__ import annotations
@@ -23,17 +26,19 @@ import json
 import os
 
 __all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_paged",
-           "attn_decode_paged", "attn_decode_workspace_size",
+           "attn_decode_paged", "attn_decode_paged_noalloc", "attn_decode_workspace_size",
+           "ATTN_NOALLOC_SCRATCH_BYTES",
            "last_provenance", "last_error", "AttnError", "library", "LIB_PATH",
            "ATTN_WINDOW_NONE", "ATTN_DECODE_CHUNK", "ERROR_CODES", "EXPORTS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinvattn.so")
 ATTN_WINDOW_NONE = -1
 ATTN_DECODE_CHUNK = 512
+ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 ERROR_CODES = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
                4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP", 7: "ATTN_E_VALIDATE"}
 EXPORTS = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_paged",
-           "attn_decode_workspace_size", "attn_decode_paged",
+           "attn_decode_workspace_size", "attn_decode_paged", "attn_decode_paged_noalloc",
            "attn_last_error", "attn_last_provenance", "attn_version"]
 
 
@@ -71,6 +76,9 @@ def library():
         lib.attn_decode_paged.restype = ctypes.c_int
         lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                           i32, i32, i32, f32, vp, sz, vp, vp]
+        lib.attn_decode_paged_noalloc.restype = ctypes.c_int
+        lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
+                                                  i32, i32, i32, f32, vp, vp]
         lib.attn_last_error.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
         lib.attn_last_provenance.restype = ctypes.c_int
@@ -343,5 +351,40 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seq_len,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(seq_lens), B, int(max_seq_len), nb, bs, hq, hkv, d, int(window),
         float(softmax_scale), _ptr(workspace), wbytes, _ptr(out), _stream(stream))
+    _check(rc)
+    return out
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out,
+                              window=ATTN_WINDOW_NONE, softmax_scale=None, stream=None):
+    """Paged decode without a workspace: the library keeps the chunk records
+    in its static per-GPU scratch (at most ATTN_NOALLOC_SCRATCH_BYTES), so the
+    call allocates nothing; ``out`` bf16 [B, Hq, D] is required.  Calls that
+    overlap on one GPU share that scratch and must be serialised.  Returns
+    out."""
+    import torch
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_cache, "k_cache", torch.bfloat16, 4)
+    _require(v_cache, "v_cache", torch.bfloat16, 4)
+    _require(block_table, "block_table", torch.int32, 2)
+    _require(seq_lens, "seq_lens", torch.int32, 1)
+    _require(out, "out", torch.bfloat16, 3)
+    B, hq, d = q.shape
+    nb, bs, hkv, d2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or d2 != d:
+        raise ValueError("caches must be [NB, BS, Hkv, D] matching q")
+    _shape(seq_lens, "seq_lens", (B,))
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table must have {B} rows (one per sequence), got "
+                         f"{block_table.shape[0]}")
+    _shape(out, "out", q.shape)
+    _on_one_gpu(q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+                seq_lens=seq_lens, out=out)
+    if softmax_scale is None:
+        softmax_scale = d ** -0.5
+    rc = library().attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), B, int(max_seq_len), nb, bs, hq, hkv, d, int(window),
+        float(softmax_scale), _ptr(out), _stream(stream))
     _check(rc)
     return out

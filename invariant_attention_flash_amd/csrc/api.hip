@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -20,6 +21,16 @@
 #include "kernels.h"
 
 using namespace invattn;
+
+// ---------------------------------------------------------------------------
+// Scratch of attn_decode_paged_noalloc: the chunk records of one decode call,
+// in a static device array that every GPU the library runs on holds until the
+// process ends (ATTN_NOALLOC_SCRATCH_BYTES).  In host code `scratch` names a
+// host-side stand-in, never the device memory: its device address is looked
+// up once per device (hipGetSymbolAddress, with that device current) and only
+// that address is used.  Nothing in it needs to start at zero: the chunk
+// kernel writes every record the merge kernel reads.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -161,6 +172,123 @@ int validate_varlen(const int32_t* cu_seqlens, int batch, int max_seqlen, const 
     if (seq >= batch || a < cu[seq] || e > cu[seq + 1])
       return fail(ATTN_E_VALIDATE, "span %d [%d,%d) is not inside one sequence", i, a, e);
   }
+  return ATTN_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_E_UNSUPPORTED, "device %d: the scratch table holds %d devices", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(ATTN_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return ATTN_OK;
+}
+
+// The decode entry points.  own_scratch: the chunk records go to the
+// library's static scratch array (workspace is ignored, workspace_bytes is
+// the array's size); otherwise to the caller's workspace.
+int decode_impl(const char* op, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                int32_t batch, int32_t max_seq_len, int32_t num_blocks, int32_t block_size,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                float softmax_scale, void* workspace, size_t workspace_bytes, bool own_scratch,
+                void* o, hipStream_t stream) {
+  g_err.clear();
+  if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
+  int rc = check_heads(num_q_heads, num_kv_heads, head_dim, window, softmax_scale);
+  if (rc != ATTN_OK) return rc;
+  if (block_size != 16) return fail(ATTN_E_UNSUPPORTED, "block_size=%d must be 16", block_size);
+  if (batch > 65535) return fail(ATTN_E_UNSUPPORTED, "batch=%d exceeds 65535", batch);
+  const int group = num_q_heads / num_kv_heads;
+  char sid[128];
+  snprintf(sid, sizeof sid, "decode_d%d_g%d_chunk%d_stage%d_t256+merge_t64", head_dim, group,
+           kDecodeChunk, kDecodeStage);
+  char split[128];
+  snprintf(split, sizeof split, "fixed chunks of %d keys from position 0; ascending merge",
+           kDecodeChunk);
+  if (batch == 0) {
+    set_provenance(op, "none (empty input)", sid, split, window, head_dim,
+                   num_q_heads, num_kv_heads, batch, max_seq_len, 0);
+    return ATTN_OK;
+  }
+  if (max_seq_len <= 0) return fail(ATTN_E_SHAPE, "max_seq_len=%d must be >= 1", max_seq_len);
+  if (max_blocks_per_seq <= 0) return fail(ATTN_E_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
+  if (num_blocks <= 0) return fail(ATTN_E_SHAPE, "num_blocks=%d must be >= 1", num_blocks);
+  if ((long long)max_blocks_per_seq * block_size < max_seq_len)
+    return fail(ATTN_E_SHAPE, "max_blocks_per_seq*block_size=%lld < max_seq_len=%d",
+                (long long)max_blocks_per_seq * block_size, max_seq_len);
+  if (!q) return fail(ATTN_E_NULL, "q is NULL");
+  if (!k_cache) return fail(ATTN_E_NULL, "k_cache is NULL");
+  if (!v_cache) return fail(ATTN_E_NULL, "v_cache is NULL");
+  if (!block_table) return fail(ATTN_E_NULL, "block_table is NULL");
+  if (!seq_lens) return fail(ATTN_E_NULL, "seq_lens is NULL");
+  if (!own_scratch && !workspace) return fail(ATTN_E_NULL, "workspace is NULL");
+  if (!o) return fail(ATTN_E_NULL, "o is NULL");
+  if (!aligned16(q)) return fail(ATTN_E_ALIGN, "q is not 16-byte aligned");
+  if (!aligned16(k_cache)) return fail(ATTN_E_ALIGN, "k_cache is not 16-byte aligned");
+  if (!aligned16(v_cache)) return fail(ATTN_E_ALIGN, "v_cache is not 16-byte aligned");
+  if (!own_scratch && !aligned16(workspace))
+    return fail(ATTN_E_ALIGN, "workspace is not 16-byte aligned");
+  if (!aligned16(o)) return fail(ATTN_E_ALIGN, "o is not 16-byte aligned");
+  if (!aligned4(block_table)) return fail(ATTN_E_ALIGN, "block_table is not 4-byte aligned");
+  if (!aligned4(seq_lens)) return fail(ATTN_E_ALIGN, "seq_lens is not 4-byte aligned");
+  const size_t need = ::attn_decode_workspace_size(batch, max_seq_len, num_q_heads, head_dim);
+  if (workspace_bytes < need) {
+    if (own_scratch)
+      return fail(ATTN_E_WORKSPACE, "the batch needs %zu bytes of chunk records, more than the "
+                  "library's scratch of %zu bytes (use attn_decode_paged with a workspace)", need,
+                  workspace_bytes);
+    return fail(ATTN_E_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
+  }
+  hipStream_t s = stream;
+  if (own_scratch && (rc = scratch_address(&workspace)) != ATTN_OK) return rc;
+
+  long long tokens = -1;
+  if (validate_enabled()) {
+    std::vector<int32_t> sl, bt;
+    if ((rc = fetch_ints(seq_lens, (size_t)batch, sl, s, "copy seq_lens")) != ATTN_OK) return rc;
+    if ((rc = fetch_ints(block_table, (size_t)batch * max_blocks_per_seq, bt, s, "copy block_table")) != ATTN_OK)
+      return rc;
+    tokens = 0;
+    for (int b = 0; b < batch; ++b) {
+      const int L = sl[b];
+      if (L < 1 || L > max_seq_len)
+        return fail(ATTN_E_VALIDATE, "seq_lens[%d]=%d outside [1, max_seq_len=%d]", b, L, max_seq_len);
+      tokens += L;
+      const int lo = window > 0 ? (L - window > 0 ? L - window : 0) : 0;
+      for (int j = lo / block_size; j <= (L - 1) / block_size; ++j) {
+        const int id = bt[(size_t)b * max_blocks_per_seq + j];
+        if (id < 0 || id >= num_blocks)
+          return fail(ATTN_E_VALIDATE, "block_table[%d][%d]=%d outside [0, num_blocks=%d)", b, j,
+                      id, num_blocks);
+      }
+    }
+  }
+
+  DecodeArgs a{q, k_cache, v_cache, block_table, max_blocks_per_seq, seq_lens, batch,
+               max_seq_len, num_blocks, num_q_heads, num_kv_heads, head_dim, window,
+               fold_scale(softmax_scale), reinterpret_cast<float*>(workspace),
+               (max_seq_len + kDecodeChunk - 1) / kDecodeChunk, o};
+  const char* kernel = "";
+  hipError_t e = launch_decode(a, s, &kernel);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  set_provenance(op, kernel, sid, split, window, head_dim, num_q_heads,
+                 num_kv_heads, batch, max_seq_len, tokens);
   return ATTN_OK;
 }
 
@@ -426,81 +554,22 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                       int32_t num_kv_heads, int32_t head_dim, int32_t window,
                       float softmax_scale, void* workspace, size_t workspace_bytes, void* o,
                       hipStream_t stream) {
-  g_err.clear();
-  if (batch < 0) return fail(ATTN_E_SHAPE, "batch=%d must be >= 0", batch);
-  int rc = check_heads(num_q_heads, num_kv_heads, head_dim, window, softmax_scale);
-  if (rc != ATTN_OK) return rc;
-  if (block_size != 16) return fail(ATTN_E_UNSUPPORTED, "block_size=%d must be 16", block_size);
-  if (batch > 65535) return fail(ATTN_E_UNSUPPORTED, "batch=%d exceeds 65535", batch);
-  const int group = num_q_heads / num_kv_heads;
-  char sid[128];
-  snprintf(sid, sizeof sid, "decode_d%d_g%d_chunk%d_stage%d_t256+merge_t64", head_dim, group,
-           kDecodeChunk, kDecodeStage);
-  char split[128];
-  snprintf(split, sizeof split, "fixed chunks of %d keys from position 0; ascending merge",
-           kDecodeChunk);
-  if (batch == 0) {
-    set_provenance("attn_decode_paged", "none (empty input)", sid, split, window, head_dim,
-                   num_q_heads, num_kv_heads, batch, max_seq_len, 0);
-    return ATTN_OK;
-  }
-  if (max_seq_len <= 0) return fail(ATTN_E_SHAPE, "max_seq_len=%d must be >= 1", max_seq_len);
-  if (max_blocks_per_seq <= 0) return fail(ATTN_E_SHAPE, "max_blocks_per_seq=%d must be >= 1", max_blocks_per_seq);
-  if (num_blocks <= 0) return fail(ATTN_E_SHAPE, "num_blocks=%d must be >= 1", num_blocks);
-  if ((long long)max_blocks_per_seq * block_size < max_seq_len)
-    return fail(ATTN_E_SHAPE, "max_blocks_per_seq*block_size=%lld < max_seq_len=%d",
-                (long long)max_blocks_per_seq * block_size, max_seq_len);
-  if (!q) return fail(ATTN_E_NULL, "q is NULL");
-  if (!k_cache) return fail(ATTN_E_NULL, "k_cache is NULL");
-  if (!v_cache) return fail(ATTN_E_NULL, "v_cache is NULL");
-  if (!block_table) return fail(ATTN_E_NULL, "block_table is NULL");
-  if (!seq_lens) return fail(ATTN_E_NULL, "seq_lens is NULL");
-  if (!workspace) return fail(ATTN_E_NULL, "workspace is NULL");
-  if (!o) return fail(ATTN_E_NULL, "o is NULL");
-  if (!aligned16(q)) return fail(ATTN_E_ALIGN, "q is not 16-byte aligned");
-  if (!aligned16(k_cache)) return fail(ATTN_E_ALIGN, "k_cache is not 16-byte aligned");
-  if (!aligned16(v_cache)) return fail(ATTN_E_ALIGN, "v_cache is not 16-byte aligned");
-  if (!aligned16(workspace)) return fail(ATTN_E_ALIGN, "workspace is not 16-byte aligned");
-  if (!aligned16(o)) return fail(ATTN_E_ALIGN, "o is not 16-byte aligned");
-  if (!aligned4(block_table)) return fail(ATTN_E_ALIGN, "block_table is not 4-byte aligned");
-  if (!aligned4(seq_lens)) return fail(ATTN_E_ALIGN, "seq_lens is not 4-byte aligned");
-  const size_t need = attn_decode_workspace_size(batch, max_seq_len, num_q_heads, head_dim);
-  if (workspace_bytes < need)
-    return fail(ATTN_E_WORKSPACE, "workspace_bytes=%zu < required %zu", workspace_bytes, need);
-  hipStream_t s = stream;
+  return decode_impl("attn_decode_paged", q, k_cache, v_cache, block_table, max_blocks_per_seq,
+                     seq_lens, batch, max_seq_len, num_blocks, block_size, num_q_heads,
+                     num_kv_heads, head_dim, window, softmax_scale, workspace, workspace_bytes,
+                     false, o, stream);
+}
 
-  long long tokens = -1;
-  if (validate_enabled()) {
-    std::vector<int32_t> sl, bt;
-    if ((rc = fetch_ints(seq_lens, (size_t)batch, sl, s, "copy seq_lens")) != ATTN_OK) return rc;
-    if ((rc = fetch_ints(block_table, (size_t)batch * max_blocks_per_seq, bt, s, "copy block_table")) != ATTN_OK)
-      return rc;
-    tokens = 0;
-    for (int b = 0; b < batch; ++b) {
-      const int L = sl[b];
-      if (L < 1 || L > max_seq_len)
-        return fail(ATTN_E_VALIDATE, "seq_lens[%d]=%d outside [1, max_seq_len=%d]", b, L, max_seq_len);
-      tokens += L;
-      const int lo = window > 0 ? (L - window > 0 ? L - window : 0) : 0;
-      for (int j = lo / block_size; j <= (L - 1) / block_size; ++j) {
-        const int id = bt[(size_t)b * max_blocks_per_seq + j];
-        if (id < 0 || id >= num_blocks)
-          return fail(ATTN_E_VALIDATE, "block_table[%d][%d]=%d outside [0, num_blocks=%d)", b, j,
-                      id, num_blocks);
-      }
-    }
-  }
-
-  DecodeArgs a{q, k_cache, v_cache, block_table, max_blocks_per_seq, seq_lens, batch,
-               max_seq_len, num_blocks, num_q_heads, num_kv_heads, head_dim, window,
-               fold_scale(softmax_scale), reinterpret_cast<float*>(workspace),
-               (max_seq_len + kDecodeChunk - 1) / kDecodeChunk, o};
-  const char* kernel = "";
-  hipError_t e = launch_decode(a, s, &kernel);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  set_provenance("attn_decode_paged", kernel, sid, split, window, head_dim, num_q_heads,
-                 num_kv_heads, batch, max_seq_len, tokens);
-  return ATTN_OK;
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                              int32_t num_blocks, int32_t block_size, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t window,
+                              float softmax_scale, void* o, hipStream_t stream) {
+  return decode_impl("attn_decode_paged_noalloc", q, k_cache, v_cache, block_table,
+                     max_blocks_per_seq, seq_lens, batch, max_seq_len, num_blocks, block_size,
+                     num_q_heads, num_kv_heads, head_dim, window, softmax_scale, nullptr,
+                     (size_t)ATTN_NOALLOC_SCRATCH_BYTES, true, o, stream);
 }
 
 }  // extern "C"

@@ -252,3 +252,17 @@ def test_backward_empty_input_needs_no_pointers():
     assert rc == 0, msg
     rc, msg = call_backward(max_seqlen=0, **none)
     assert rc == 0, msg
+
+
+def test_noalloc_decode_rejects_beyond_scratch_before_any_gpu_call():
+    """The allocation-free decode keeps its chunk records in a static scratch
+    of ATTN_NOALLOC_SCRATCH_BYTES: a batch needing more is refused on the
+    host (ATTN_E_WORKSPACE), before the scratch is looked up on a device."""
+    need = ia.attn_decode_workspace_size(64, 32768, 32, 512)
+    assert need > ia.ATTN_NOALLOC_SCRATCH_BYTES
+    assert ia.attn_decode_workspace_size(1, 1016 * 512, 32, 512) <= ia.ATTN_NOALLOC_SCRATCH_BYTES
+    x = ctypes.c_void_p(1 << 20)
+    rc = ia.library().attn_decode_paged_noalloc(x, x, x, x, 2048, x, 64, 32768, 100, 16, 32, 4,
+                                                512, -1, ctypes.c_float(0.044), x, None)
+    assert rc == E["ATTN_E_WORKSPACE"]
+    assert "scratch" in ia.last_error()
