@@ -17,10 +17,10 @@
  *   s_j  = fp32 MFMA dot product of bf16 q_i and bf16 k_j, head dim in
  *          ascending MFMA steps of 32
  *   m    = reference max (scaled units), -inf before the first allowed key;
- *          it moves to the tile's scaled max only when the row would
- *          otherwise see p > 2^8 (head dims 256 and 512: tested on p
- *          itself; head dim 64 and decode: tile max > m + 8), or at the
- *          first allowed key
+ *          it moves to the tile's scaled max at the first allowed key, and
+ *          after that only when the row would otherwise see large p (head
+ *          dims 256 and 512: one of the row's four lanes' sums of the
+ *          tile's p exceeds 2^8; head dim 64 and decode: tile max > m + 8)
  *   p_j  = exp2(fma(s_j, c, -m))          (hardware exp2, fp32; m -> 0
  *          while m = -inf)
  *   l    = l * alpha + (sum of the tile's p in a fixed order); head dims

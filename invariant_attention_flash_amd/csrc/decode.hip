@@ -35,15 +35,17 @@ namespace invattn {
 // Reference-max hysteresis inside a chunk (log2 units), as in prefill.
 constexpr float kDecodeRescale = 8.0f;
 
-// Two waves per SIMD: registers are capped at 256 per lane, and two
-// workgroups share a CU (two 32 KB stages each at head dim 512), so one
-// workgroup's loads land while the other computes.
+// Two waves per SIMD with the two-stage ring: registers are capped at 256 per
+// lane, and two workgroups share a CU (two 32 KB stages each at head dim
+// 512), so one workgroup's loads land while the other computes.
 constexpr int kDecodeOcc = 2;
 
 template <int D_, int G_, int NST_, int WAVES_>
 struct DecodeCfg {
   static constexpr bool kAliasKV = false;  // V read from the K cache (KvAliasOf<> sets it)
-  static constexpr int kOcc = kDecodeOcc;     // waves per SIMD the registers are sized for
+  // Waves per SIMD the registers are sized for: the deep ring (four 32 KB
+  // stages at head dim 512) leaves room for one workgroup per CU.
+  static constexpr int kOcc = NST_ >= 4 ? 1 : kDecodeOcc;
   static constexpr int D = D_, G = G_;
   static constexpr int kWaves = WAVES_;
   static constexpr int kThreads = 64 * kWaves;
@@ -139,8 +141,14 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
   const uint32_t slot_stride = (uint32_t)hkv * D;
   const uint32_t head_off = (uint32_t)g * D;
   const size_t block_elems = (size_t)C::kKeys * hkv * D;
+  // Table entries are read with scalar loads (constant address space; the
+  // index is wave-uniform), waited on with the LDS/scalar counter.  A vector
+  // load here would make the compiler wait for every vector load in flight,
+  // the direct block loads it cannot see included, and so drain the ring at
+  // every step.
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
   auto block_base = [&](int kb) {
-    int id = table[kb];
+    int id = ((ConstI32*)table)[kb];
     id = min(max(id, 0), num_blocks - 1);  // a bad id reads some block, never out of bounds
     return (size_t)id * block_elems;
   };
@@ -189,12 +197,23 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
     const bf16* ks = cur;
     const bf16* vs = C::kAliasKV ? cur : cur + C::kTile;
     const int k0 = kb * C::kKeys;
-    // S^T for keys k0 + [0, 16): lane holds head col, keys 4*grp + i.
-    f32x4 sacc = f32x4{};
+    // S^T for keys k0 + [0, 16): lane holds head col, keys 4*grp + i.  The
+    // MFMAs form one dependent chain over the head dim, so every K operand is
+    // read from LDS before the chain starts (the chain then waits on no LDS
+    // latency), and the V operands of the PV product right after.
     const bf16* krow = ks + col * D;
+    bf16x8 kop[C::kSteps];
 #pragma unroll
     for (int t = 0; t < C::kSteps; ++t)
-      sacc = mfma16(ld_lds_x8(krow + (((4 * t + grp) ^ (col & C::kSwK)) << 3)), qr[t], sacc);
+      kop[t] = ld_lds_x8(krow + (((4 * t + grp) ^ (col & C::kSwK)) << 3));
+    const bf16* vr = vs + vrow * D + 4 * (lg & 1);
+    bf16x4 vop[C::kDBlk];
+#pragma unroll
+    for (int db = 0; db < C::kDBlk; ++db) vop[db] = ld_lds_tr(vr + (((vc1 + 2 * db) ^ vsw) << 3));
+    __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the chain
+    f32x4 sacc = f32x4{};
+#pragma unroll
+    for (int t = 0; t < C::kSteps; ++t) sacc = mfma16(kop[t], qr[t], sacc);
     float x[4];
     float tmax = kNegInf;
 #pragma unroll
@@ -204,8 +223,12 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
       tmax = fmaxf(tmax, x[i]);
     }
     // Reduce over the four lane groups holding the same query (xor 16, 32).
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    {
+      HalfPair hp = row_pair(tmax);  // lanes l, l^16
+      tmax = fmaxf(hp.lo, hp.hi);
+      hp = half_pair(tmax);          // lanes l, l^32
+      tmax = fmaxf(hp.lo, hp.hi);
+    }
     tmax *= c2;
     const bool move = tmax > m + kDecodeRescale || (m == kNegInf && tmax != kNegInf);
     const float m_new = move ? tmax : m;
@@ -219,8 +242,14 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
       psum += p;
       pb[i] = to_bf16(p);
     }
-    psum = psum + __shfl_xor(psum, 16);
-    psum = psum + __shfl_xor(psum, 32);
+    {
+      // Each step adds the two lanes' sums; addition commutes exactly, so
+      // both lanes hold the same value.
+      HalfPair hp = row_pair(psum);
+      psum = hp.lo + hp.hi;
+      hp = half_pair(psum);
+      psum = hp.lo + hp.hi;
+    }
     l = l * alpha + psum;
     m = m_new;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
@@ -229,10 +258,8 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
     }
     // O^T += V^T P^T for this wave's quarter of the head dim; operand slot
     // s covers key 4*grp + s on both sides.
-    const bf16* vr = vs + vrow * D + 4 * (lg & 1);
 #pragma unroll
-    for (int db = 0; db < C::kDBlk; ++db)
-      oacc[db] = mfma16k16(ld_lds_tr(vr + (((vc1 + 2 * db) ^ vsw) << 3)), pb, oacc[db]);
+    for (int db = 0; db < C::kDBlk; ++db) oacc[db] = mfma16k16(vop[db], pb, oacc[db]);
   };
   for (int kb = kb0; kb < kb1;) {
     if constexpr (C::kStages == 2) {
@@ -268,41 +295,63 @@ void decode_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kc
   }
 }
 
+// Merge kernel: one workgroup per (query head, sequence); thread t owns
+// head-dim element t.  The fold over chunks is a dependent chain, so the
+// records are loaded up to kBatch chunks at a time ahead of their folds: each
+// thread its element of every chunk, and lane c of every wave the running max
+// and sum of chunk c (read back as wave-uniform values).  A chunk index past
+// the last is clamped to it and never folded.  Every element sees the same
+// operations in the same chunk order whatever the thread layout.
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(64, 64)))
+struct MergeCfg {
+  static constexpr int kThreads = D;
+  static constexpr int kBatch = 64;  // one round for contexts up to 64 chunks
+  static_assert(kThreads % 64 == 0 && kThreads <= 1024, "merge layout");
+};
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(MergeCfg<D>::kThreads,
+                                                      MergeCfg<D>::kThreads)))
 void decode_merge_kernel(const float* __restrict__ ws, const int32_t* __restrict__ seq_lens,
                          int max_seq_len, int max_blocks, int hq, int window, int n_chunks,
                          bf16* __restrict__ o) {
-  constexpr int kPer = D / 64;
+  constexpr int kBatch = MergeCfg<D>::kBatch;
   constexpr int kRec = decode_record_floats(D);
-  const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  bf16* orow = o + ((size_t)b * hq + head) * D + tid * kPer;
+  const int head = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  bf16* orow = o + ((size_t)b * hq + head) * D + tid;
   int L = seq_lens[b];
   L = min(L, min(max_seq_len, max_blocks * 16));
   if (L <= 0) {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) orow[e] = to_bf16(0.f);
+    *orow = to_bf16(0.f);
     return;
   }
   const int kv_lo = window > 0 ? max(0, L - window) : 0;
   const int c_lo = kv_lo / kDecodeChunk, c_hi = (L - 1) / kDecodeChunk;
   const float* base = ws + ((size_t)b * hq + head) * n_chunks * kRec;
-  float m = kNegInf, l = 0.f, acc[kPer];
+  float m = kNegInf, l = 0.f, acc = 0.f;
+  for (int c0 = c_lo; c0 <= c_hi; c0 += kBatch) {
+    float x[kBatch];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-  for (int c = c_lo; c <= c_hi; ++c) {
-    const float* rec = base + (size_t)c * kRec;
-    const float mc = rec[D], lc = rec[D + 1];
-    const float m_new = fmaxf(m, mc);
-    const float a = fast_exp2(m - m_new);
-    const float bc = fast_exp2(mc - m_new);
-    l = l * a + lc * bc;
+    for (int u = 0; u < kBatch; ++u) x[u] = base[(size_t)min(c0 + u, c_hi) * kRec + tid];
+    const float* own = base + (size_t)min(c0 + lane, c_hi) * kRec;
+    const float mv = own[D], lv = own[D + 1];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] = acc[e] * a + rec[tid * kPer + e] * bc;
-    m = m_new;
+    for (int u = 0; u < kBatch; ++u) {
+      if (c0 + u <= c_hi) {
+        const float mc = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mv), u));
+        const float lc = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), u));
+        const float m_new = fmaxf(m, mc);
+        const float a = fast_exp2(m - m_new);
+        const float bc = fast_exp2(mc - m_new);
+        l = l * a + lc * bc;
+        acc = acc * a + x[u] * bc;
+        m = m_new;
+      }
+    }
   }
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) orow[e] = to_bf16(acc[e] / l);
+  *orow = to_bf16(acc / l);
 }
 
 template <class C>
@@ -320,29 +369,53 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
                        a.hq, a.hkv, a.window, a.c2, a.workspace, a.n_chunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel<C::D>, dim3(a.hq, a.batch), dim3(64), 0, stream,
+  hipLaunchKernelGGL(decode_merge_kernel<C::D>, dim3(a.hq, a.batch),
+                     dim3(MergeCfg<C::D>::kThreads), 0, stream,
                      (const float*)a.workspace, a.seq_lens, a.max_seq_len, a.max_blocks, a.hq,
                      a.window, a.n_chunks, (bf16*)a.o);
   return hipGetLastError();
 }
 
-// Ring depth (kDecodeRing stages of one cache block) and waves per
-// workgroup (four, or one per 16 head-dim columns at head dim 64): fixed
-// constants.
+// Ring depth and waves per workgroup.  A launch whose chunk grid fits one
+// workgroup per CU (small batches) gives each workgroup a ring of four
+// stages (more bytes in flight per CU); larger grids use two stages, so two
+// workgroups share a CU.  The depth only changes when loads are issued,
+// never an operation on the data: both give the same bytes.  Waves: four, or
+// one per 16 head-dim columns at head dim 64.
+constexpr int kDecodeRingDeep = 4;
 constexpr int kDecodeRing = 2;
 #define INVATTN_DECODE_TABLE(X) \
   X(64, 1) X(64, 2) X(64, 4) X(64, 8)     \
   X(256, 1) X(256, 2) X(256, 4) X(256, 8) \
   X(512, 1) X(512, 2) X(512, 4) X(512, 8)
 
+namespace {
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cached[dev] = n > 0 ? n : -1;
+  }
+  return cached[dev];
+}
+}  // namespace
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, const char** kernel) {
   const int group = a.hq / a.hkv;
   const bool alias = a.k_cache == a.v_cache;
+  const long long grid = (long long)a.hkv * a.n_chunks * a.batch;
+  const bool deep = grid <= device_cus();
 #define X(D, G)                                                                          \
   if (a.d == D && group == G) {                                                          \
+    constexpr int W = D / 16 < 4 ? D / 16 : 4;                                           \
     *kernel = alias ? "decode_chunk_kernel<KvAliasOf<" #D "," #G ">>+decode_merge_kernel<" #D ">" \
                     : "decode_chunk_kernel<" #D "," #G ">+decode_merge_kernel<" #D ">";  \
-    return launch_one<DecodeCfg<D, G, kDecodeRing, (D / 16 < 4 ? D / 16 : 4)>>(a, stream); \
+    return deep ? launch_one<DecodeCfg<D, G, kDecodeRingDeep, W>>(a, stream)            \
+                : launch_one<DecodeCfg<D, G, kDecodeRing, W>>(a, stream);                \
   }
   INVATTN_DECODE_TABLE(X)
 #undef X

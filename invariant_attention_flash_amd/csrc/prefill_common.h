@@ -344,11 +344,11 @@ __device__ __forceinline__ uint32_t softmax_move(const f32x4 (*s)[2], int k0, co
 // and max and the bf16 cast, a dependent chain.
 //
 // Two rules differ from the one-shot form above:
-//   * a row's reference max m moves when some p = 2^(fma(s, c, -m)) of the
-//     tile exceeds 2^kRescale (the tile max exceeds m by more than kRescale,
-//     up to the rounding of the exponent), or, while m = -inf, when the tile
-//     holds an allowed key (whatever its p against the provisional 0); the
-//     fast path then needs no row max;
+//   * a row's reference max m moves when one of its lanes' sums of the
+//     tile's p = 2^(fma(s, c, -m)) (eight slots) exceeds 2^kRescale (so no
+//     p of the row exceeds it without a move), or, while m = -inf, when the
+//     tile holds an allowed key (whatever its p against the provisional 0);
+//     the fast path then needs no row max;
 //   * the running sum is kept per lane: each lane adds its 8 slots of a tile
 //     in slot order, (((p0 + p1) + p2) + ...) + p7, to its own l (scaled by
 //     alpha on a move), and the four lanes of a row are combined once, after
@@ -398,8 +398,7 @@ __device__ __forceinline__ float probs_lane(const float* v, float c2, float msub
 template <int RB, bool MASK>
 struct TileSoftmax {
   static constexpr int kStages = 8 * RB;
-  float part[RB];   // the lane's tile sum (slot order)
-  float pmax[RB];   // the lane's largest p
+  float part[RB];   // the lane's tile sum (slot order); also the move test
   bool anyok[RB];   // MASK: some slot of the lane holds an allowed key
   bf16x8 pb[RB];    // P operand
   int wbase[RB], sbase[RB];
@@ -432,27 +431,22 @@ struct TileSoftmax {
     }
     const float p = fast_exp2(__builtin_fmaf(x, ln.c2, -st.msub[rb]));
     pb[rb][e] = to_bf16(p);
-    if (e == 0) {
-      part[rb] = p;
-      pmax[rb] = p;
-    } else {
-      part[rb] = part[rb] + p;
-      pmax[rb] = fmaxf(pmax[rb], p);
-    }
+    part[rb] = e == 0 ? p : part[rb] + p;
   }
 
   // After the stages: true when some row of the wave may move (then move()
   // finishes the tile), else every lane adds its tile sum.  A row may move
-  // when one of its p exceeds the threshold, or, while its m = -inf (thr =
-  // 0), when one of its keys in the tile is allowed: its scores may all be
-  // so low that every p underflows to 0 against the provisional msub = 0,
-  // and the row must still take its first reference max here.
+  // when one of its lanes' tile sums exceeds the threshold (every p of the
+  // lane is at most that sum), or, while its m = -inf (thr = 0), when one of
+  // its keys in the tile is allowed: its scores may all be so low that every
+  // p underflows to 0 against the provisional msub = 0, and the row must
+  // still take its first reference max here.
   __device__ __forceinline__ bool finish(RowStats<RB>& st) {
     bool trig = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const bool first = st.thr[rb] == 0.f;
-      trig |= (pmax[rb] > st.thr[rb]) | (first & (MASK ? anyok[rb] : true));
+      trig |= (part[rb] > st.thr[rb]) | (first & (MASK ? anyok[rb] : true));
     }
     if (__builtin_amdgcn_ballot_w64(trig) != 0) return true;
 #pragma unroll
@@ -460,9 +454,10 @@ struct TileSoftmax {
     return false;
   }
 
-  // The rare path.  A row moves when its largest p (over the row's lanes)
-  // exceeds its threshold, or, while m = -inf, when the tile holds one of
-  // its allowed keys: m moves to the tile max, the lane sums and the
+  // The rare path.  A row moves when its largest lane tile sum (over the
+  // row's four lanes) exceeds its threshold, or, while m = -inf, when the
+  // tile holds one of its allowed keys: m moves to the tile max, the lane
+  // sums and the
   // accumulator scale by alpha = 2^(m_old - m_new) (1 when m_old = -inf:
   // both are still exact zeros) and p is recomputed; other rows add their
   // fast-path sums.  Returns the scaling mask (bit rb: some row of block rb
@@ -474,7 +469,7 @@ struct TileSoftmax {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       alpha[rb] = 1.f;
-      HalfPair hp = half_pair(pmax[rb]);
+      HalfPair hp = half_pair(part[rb]);
       const float t = fmaxf(hp.lo, hp.hi);
       hp = row_pair(t);
       bool mv = fmaxf(hp.lo, hp.hi) > st.thr[rb];

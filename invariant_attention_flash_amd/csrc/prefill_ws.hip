@@ -70,6 +70,11 @@ struct PfWsCfg {
   static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
   static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
   static constexpr int kRing = NR_;                    // buffers per K / V ring
+  // Who issues the K tile loads.  Head dim 256: the PV waves (the score waves
+  // are the critical path and the PV waves have slack).  Head dim 512: the
+  // score waves (each kind carries 32 MFMAs per step, and the PV waves' own V
+  // loads already fill their issue slots).
+  static constexpr bool kPvLoadsK = D <= 256;
   static_assert(D % 64 == 0 && kRowsPerWave % G == 0, "row map");
   static_assert(kLoads >= 1 && BN * kChunks % (64 * kRoleWaves) == 0, "tile load split");
   static_assert(BN == 32 && kRoleWaves == 4, "KvTiles: loader w reads tile rows [8w, 8w+8)");
@@ -80,10 +85,11 @@ struct PfWsCfg {
 
 // Score wave, one step: S^T(t+1) = K Q^T for its RB row blocks on the K tile
 // `kt`, in 2*kSt groups (one K operand each), with stage i of the previous
-// tile's softmax (sm) after group i's MFMAs and the K(t+3) loads spread over
-// the groups.  The MFMAs are compiler builtins with VGPR accumulators (the
-// kernel uses no AGPRs), so the compiler tracks their result latency and
-// schedules the softmax's vector work around them freely.
+// tile's softmax (sm) after group i's MFMAs and, when DMA (the score waves
+// load K), the K(t+NR) loads spread over the groups.  The MFMAs are compiler
+// builtins with VGPR accumulators (the kernel uses no AGPRs), so the
+// compiler tracks their result latency and schedules the softmax's vector
+// work around them freely.
 template <class C, bool DMA, class SM>
 __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_t kpre,
                                             const u32x4& krs, int kk0, uint32_t rs_bytes,
@@ -121,22 +127,27 @@ __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_
 
 // PV wave, one step: O^T += V^T P^T for its kDbW output blocks of every row
 // block, V from the tile `vt`, P^T from the exchange buffer `pt`, with the
-// V(t+1) loads spread over the MFMAs.
+// step's tile loads (K first when this wave loads K, then V; kLoads of each
+// per lane) spread over the MFMA groups.
 //   V operand (output block db): rows 4*gq + x/4 and +16, logical chunk
 //     2*(kDbW*p + db) + (x%4)/2, physical chunk ^ ((2*row) & kSwV),
 //     element 4*(x%2);
 //   P^T operand (row block r): 16 bytes of lane l at pt[64*r + l].
 template <class C, bool DMA>
 __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
-                                         const bf16x8* __restrict__ pt, uint32_t vpre,
+                                         const bf16x8* __restrict__ pt, uint32_t kpre,
+                                         const u32x4& krs, int kk0, uint32_t vpre,
                                          const u32x4& vrs, int vk0, uint32_t rs_bytes, int widx,
-                                         int lane, uint32_t vrow, uint32_t vc16w,
-                                         f32x4 (*o)[C::kDbW]) {
+                                         int lane,
+                                         uint32_t vrow, uint32_t vc16w, f32x4 (*o)[C::kDbW]) {
   constexpr int kN = C::kRowBlocks;           // one row block per group
+  // Loads of the step: K (when this wave loads K) then V.
+  constexpr int kKL = C::kPvLoadsK ? C::kLoads : 0;
+  constexpr int kL = kKL + C::kLoads;
   // Direct loads spread evenly: one every kEvery groups, or kPer per group.
-  constexpr int kEvery = kN >= C::kLoads ? kN / C::kLoads : 1;
-  constexpr int kPer = kN >= C::kLoads ? 1 : C::kLoads / kN;
-  static_assert(kN % C::kLoads == 0 || C::kLoads % kN == 0, "loads spread evenly over the groups");
+  constexpr int kEvery = kN >= kL ? kN / kL : 1;
+  constexpr int kPer = kN >= kL ? 1 : kL / kN;
+  static_assert(kN % kL == 0 || kL % kN == 0, "loads spread evenly over the groups");
   const char* vb0 = reinterpret_cast<const char*>(vt) + vrow;
   bf16x8 vop[C::kDbW];
 #pragma unroll
@@ -152,9 +163,14 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
     if constexpr (DMA) {
       if (r % kEvery == 0) {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u)
-          dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, (r / kEvery) * kPer + u,
-                                                      rs_bytes, widx, lane);
+        for (int u = 0; u < kPer; ++u) {
+          const int j = (r / kEvery) * kPer + u;
+          if (j < kKL)
+            dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kpre, krs, kk0, j, rs_bytes, widx, lane);
+          else
+            dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, j - kKL, rs_bytes, widx,
+                                                        lane);
+        }
       }
     }
 #pragma unroll
@@ -274,22 +290,25 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int st = 0; st < C::kSt; ++st) qr[rb][st] = ld_global_x8(qrow + 32 * st);
     }
-    auto load_k = [&](int slot, int kt) {
-      u32x4 krsc, vrsc;
-      int k0r;
-      src.get(kt, kt < kt1, widx, krsc, vrsc, k0r);
-#pragma unroll
-      for (int i = 0; i < C::kLoads; ++i)
-        dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(ks_lds + slot * kTileBytes, krsc, k0r, i,
-                                                    rs_bytes, widx, lane);
-    };
     RowStats<RB> rs;
     rs.init();
 
-    // Prologue: K(kt0) .. K(kt0+NR-1); wait for K(kt0) and form S(kt0).
+    constexpr bool kLoadK = !C::kPvLoadsK;  // this wave loads the K ring
+    // Prologue: K(kt0) .. K(kt0+NR-1) in flight, K(kt0) landed before the
+    // first barrier (issued here, or by the PV waves); form S(kt0).
+    if constexpr (kLoadK) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) load_k(i, kt0 + i);
-    wait_vmcnt<(NR - 1) * C::kLoads>();
+      for (int i = 0; i < NR; ++i) {
+        u32x4 krsc, vrsc;
+        int k0r;
+        src.get(kt0 + i, kt0 + i < kt1, widx, krsc, vrsc, k0r);
+#pragma unroll
+        for (int j = 0; j < C::kLoads; ++j)
+          dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(ks_lds + i * kTileBytes, krsc, k0r, j,
+                                                      rs_bytes, widx, lane);
+      }
+      wait_vmcnt<(NR - 1) * C::kLoads>();
+    }
     lds_barrier();
     f32x4 sa[RB][2], sb[RB][2];
     {
@@ -297,26 +316,28 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       score_phase<C, false>(ks[0], 0, none, 0, rs_bytes, widx, lane, ln.krow, ln.kq16, qr, sa,
                             [](int) {});
     }
-    // Step kt: wait for K(kt+1) (loaded NR-1 steps ago), then S(kt+1) on the
-    // MFMAs with the K(kt+NR) loads among them (into the buffer of K(kt), free
-    // once every wave is past the barrier), while the VALU takes the softmax
-    // of tile kt; the rare reference-max moves are handled after the MFMAs
-    // are issued, and P(kt) goes to the exchange buffer.  After the last tile
-    // the scores formed are never used (the K buffer holds zeros or an older
+    // Step kt: K(kt+1) has landed (waited for before the barrier by the wave
+    // that loaded it), then S(kt+1) on the MFMAs (with the K(kt+NR) loads
+    // among them when this wave loads K, into the buffer of K(kt), free once
+    // every wave is past the barrier) while the VALU takes the softmax of
+    // tile kt; the rare reference-max moves are handled after the MFMAs are
+    // issued, and P(kt) goes to the exchange buffer.  After the last tile the
+    // scores formed are never used (the K buffer holds zeros or an older
     // tile); forming them keeps the step branch-free.
     auto step = [&] __device__(int kt, f32x4(&sc)[RB][2], f32x4(&sn)[RB][2]) {
       const int r = (kt - kt0) % NR;
       const bf16* __restrict__ kcur = ks[(r + 1) % NR];  // K(kt+1)
       const uint32_t kpre = ks_lds + r * kTileBytes;      // K(kt+NR)
       const int k0 = kt * BN;
-      wait_vmcnt<(NR - 2) * C::kLoads>();
+      if constexpr (kLoadK) wait_vmcnt<(NR - 2) * C::kLoads>();
       lds_barrier();
       const bool need_mask =
           !(wave_full && k0 + BN - 1 <= pw0 && (!windowed || pw1 - 1 - k0 < window));
       const uint32_t kq16 = opaque(ln.kq16);
       u32x4 krs, unused;
-      int kk0;
-      src.get(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
+      int kk0 = 0;
+      if constexpr (kLoadK) src.get(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
+      else krs = unused = u32x4{};
       float alpha[RB];
       uint32_t smask = 0;
       bf16x8 pc[RB];
@@ -324,8 +345,8 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         constexpr bool MASK = decltype(mask_tag)::value;
         TileSoftmax<RB, MASK> ts;
         ts.init(k0, ln, qpos, my_ss, my_se);
-        score_phase<C, true>(kcur, kpre, krs, kk0, rs_bytes, widx, lane, ln.krow, kq16, qr, sn,
-                             [&](int i) { ts.stage(i, sc, ln, rs); });
+        score_phase<C, kLoadK>(kcur, kpre, krs, kk0, rs_bytes, widx, lane, ln.krow, kq16, qr, sn,
+                               [&](int i) { ts.stage(i, sc, ln, rs); });
         if (ts.finish(rs)) smask = ts.move(sc, k0, ln, qpos, my_ss, my_se, rs, alpha);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) pc[rb] = ts.pb[rb];
@@ -363,7 +384,7 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) lrow[C::kRowsPerWave * widx + 16 * rb + ln.x] = lsum[rb];
     }
-    wait_vmcnt<0>();
+    if constexpr (kLoadK) wait_vmcnt<0>();
     lds_barrier();
     if (lse != nullptr && ln.gq == 0) {
 #pragma unroll
@@ -378,14 +399,24 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // ---------------------------------------------------------------- PV wave
   // V operand base of this wave's first output block.
   const uint32_t vc16w = ln.vc16 ^ (uint32_t)((C::kDbW * widx) << 5);
-  auto load_v = [&](int slot, int kt) {
+  // Loads of tile kt into ring buffer `slot`: K rows (WHICH & 1) and V rows
+  // (WHICH & 2), this wave's share of each.
+  auto load_tile = [&](int slot, int kt, int which) {
     u32x4 krsc, vrsc;
     int k0r;
     src.get(kt, kt < kt1, widx, krsc, vrsc, k0r);
+    if (which & 1) {
 #pragma unroll
-    for (int i = 0; i < C::kLoads; ++i)
-      dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vs_lds + slot * kTileBytes, vrsc, k0r, i,
-                                                  rs_bytes, widx, lane);
+      for (int i = 0; i < C::kLoads; ++i)
+        dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(ks_lds + slot * kTileBytes, krsc, k0r, i,
+                                                    rs_bytes, widx, lane);
+    }
+    if (which & 2) {
+#pragma unroll
+      for (int i = 0; i < C::kLoads; ++i)
+        dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vs_lds + slot * kTileBytes, vrsc, k0r, i,
+                                                    rs_bytes, widx, lane);
+    }
   };
   // Accumulators start at +0: the first PV product adds to +0, which is the
   // product itself (as with a zero addend).
@@ -414,37 +445,57 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   };
 
-  // Prologue: V(kt0) .. V(kt0+NR-3) (what the steps before kt0 would load);
-  // the barrier matches the score waves' prologue barrier.
+  // Tile loads.  Step kt issues K(kt+NR) (by the PV waves at head dim 256,
+  // else by the score waves) and V(kt+NR-2); K(kt+NR) goes to the buffer of
+  // K(kt) (read by the score waves in step kt-1), V(kt+NR-2) to the buffer of
+  // V(kt-2) (read by PV(kt-2) in step kt-1), both free once every wave is
+  // past the step's barrier.  Before the barrier of step kt the loading
+  // waves wait for K(kt+1) (for the score waves) and V(kt-1) (for PV(kt-1)),
+  // the loads of step kt+1-NR, so the NR-2 newer steps' loads may stay in
+  // flight.  Prologue: the loads of the steps before kt0 -- K(kt0) ..
+  // K(kt0+NR-1) when this wave loads K, then V(kt0) .. V(kt0+NR-3); K(kt0)
+  // must land before the first barrier.
+  constexpr bool kLoadK = C::kPvLoadsK;
+  constexpr int kStepLoads = (kLoadK ? 2 : 1) * C::kLoads;
+  if constexpr (kLoadK) {
 #pragma unroll
-  for (int i = 0; i + 2 < NR; ++i) load_v(i, kt0 + i);
+    for (int i = 0; i < NR; ++i) load_tile(i, kt0 + i, 1);
+  }
+#pragma unroll
+  for (int i = 0; i + 2 < NR; ++i) load_tile(i, kt0 + i, 2);
+  if constexpr (kLoadK) wait_vmcnt<(2 * NR - 3) * C::kLoads>();
   lds_barrier();
 
-  // Step kt: wait for V(kt-1) (loaded NR-1 steps ago), scale for the moves
-  // of tile kt-1, then PV(kt-1) with the V(kt+NR-2) loads among the MFMAs
-  // (into the buffer of V(kt-2), free once every wave is past the barrier).
-  // MODE 0: first tile (no PV yet); 1: first PV (nothing to scale yet);
-  // 2: steady state.
+  // Step kt: wait, barrier, scale for the moves of tile kt-1, then PV(kt-1)
+  // with the step's loads among the MFMAs.  MODE 0: first tile (no PV yet);
+  // 1: first PV (nothing to scale yet); 2: steady state.
   auto step = [&] __device__(int kt, auto mode) {
     constexpr int MODE = decltype(mode)::value;
     const int r = (kt - kt0) % NR;
-    const bf16* __restrict__ vcur = vs[(r + NR - 1) % NR];       // V(kt-1)
+    const bf16* __restrict__ vcur = vs[(r + NR - 1) % NR];           // V(kt-1)
+    const uint32_t kpre = ks_lds + r * kTileBytes;                    // K(kt+NR)
     const uint32_t vpre = vs_lds + ((r + NR - 2) % NR) * kTileBytes;  // V(kt+NR-2)
-    const bf16x8* __restrict__ pcur = pl[(kt - 1) & 1];         // P(kt-1)
-    wait_vmcnt<(NR - 2) * C::kLoads>();
+    const bf16x8* __restrict__ pcur = pl[(kt - 1) & 1];             // P(kt-1)
+    wait_vmcnt<(NR - 2) * kStepLoads>();
     lds_barrier();
-    u32x4 vrs, unused;
-    int vk0;
+    u32x4 krs{}, vrs, unused;
+    int kk0 = 0, vk0;
+    if constexpr (kLoadK) src.get(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
     src.get(kt + NR - 2, kt + NR - 2 < kt1, widx, unused, vrs, vk0);
     if constexpr (MODE == 0) {
-      // No PV yet: only the V(kt0+NR-2) loads.
+      // No PV yet: only the loads.
+      if constexpr (kLoadK) {
+#pragma unroll
+        for (int i = 0; i < C::kLoads; ++i)
+          dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kpre, krs, kk0, i, rs_bytes, widx, lane);
+      }
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i)
         dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, i, rs_bytes, widx, lane);
     } else {
       if constexpr (MODE == 2) rescale_from(kt - 1);
-      pv_phase<C, true>(vcur, pcur, vpre, vrs, vk0, rs_bytes, widx, lane, ln.vrow,
-                        opaque(vc16w), oacc);
+      pv_phase<C, true>(vcur, pcur, kpre, krs, kk0, vpre, vrs, vk0, rs_bytes, widx, lane,
+                        ln.vrow, opaque(vc16w), oacc);
     }
   };
   step(kt0, Mode0{});
@@ -457,8 +508,11 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   wait_vmcnt<0>();
   lds_barrier();
   if (kl > kt0) rescale_from(kl);
-  pv_phase<C, false>(vs[(kl - kt0) % NR], pl[kl & 1], 0, buffer_rsrc(v, 0), 0, rs_bytes, widx,
-                     lane, ln.vrow, vc16w, oacc);
+  {
+    const u32x4 none = buffer_rsrc(v, 0);
+    pv_phase<C, false>(vs[(kl - kt0) % NR], pl[kl & 1], 0, none, 0, 0, none, 0, rs_bytes, widx,
+                       lane, ln.vrow, vc16w, oacc);
+  }
 
   // Epilogue: o = acc / l (IEEE fp32 division), bf16 RNE, store this wave's
   // columns of every row.
