@@ -45,8 +45,8 @@ FLUSH_BYTES = 512 << 20     # read between decode calls: twice the 256 MB last-l
 # Kernel instances, by the name rocprofv3 prints (demangled), and the key of
 # their HBM traffic in profiles/traffic.json.
 KERNELS = {
-    "prefill_ws_kernel<256,2,2,3>": "prefill_ws_kernel<invattn::PfWsCfg<256, 2, 2, 3> >",
-    "prefill_ws_kernel<512,8,1,2>": "prefill_ws_kernel<invattn::PfWsCfg<512, 8, 1, 2> >",
+    "prefill_ws_kernel<256,2,2,3,32>": "prefill_ws_kernel<invattn::PfWsCfg<256, 2, 2, 3, 32> >",
+    "prefill_ws_kernel<512,8,1,2,32>": "prefill_ws_kernel<invattn::PfWsCfg<512, 8, 1, 2, 32> >",
     "decode_chunk_kernel<512,8>+decode_merge_kernel<512>": "decode_",
 }
 
@@ -147,8 +147,18 @@ def write_traffic(fetch_dir, write_dir):
         scale = CALIBRATION_BYTES / (1024.0 * float(np.median(calib)))
         for key, match in KERNELS.items():
             first = "decode_chunk_kernel" if key.startswith("decode") else match
-            vals = [v for k, v, g in rows if match in k and "KvAliasOf" not in k]
-            launches = sum(1 for k, v, g in rows if first in k and "KvAliasOf" not in k)
+            sel = [(k, v, g) for k, v, g in rows if match in k and "KvAliasOf" not in k]
+            if key.startswith("decode"):
+                # the step's batch-64 decode: the largest grid of the chunk
+                # kernels and of the merge kernels (the --step-only run also
+                # decodes batch 1, with a chunk kernel of another ring depth)
+                fam = lambda k: "chunk" if "decode_chunk_kernel" in k else "merge"
+                big = {}
+                for k, v, g in sel:
+                    big[fam(k)] = max(big.get(fam(k), 0), g)
+                sel = [(k, v, g) for k, v, g in sel if g == big[fam(k)]]
+            vals = [v for k, v, g in sel]
+            launches = sum(1 for k, v, g in sel if first in k)
             if not vals or not launches:
                 continue
             per_launch = 1024.0 * scale * sum(vals) / launches
@@ -300,7 +310,7 @@ def main():
     log(f"step: hybrid {hy_ms:.3f} ms ({hy_tflops:.1f} TFLOP/s), decode {dc_ms:.3f} ms")
 
     def layer_kernel(c):
-        return ("prefill_ws_kernel<256,2,2,3>" if c["d"] == 256 else "prefill_ws_kernel<512,8,1,2>")
+        return ("prefill_ws_kernel<256,2,2,3,32>" if c["d"] == 256 else "prefill_ws_kernel<512,8,1,2,32>")
 
     per_layer = []
     kern_ms, kern_flops = {}, {}
@@ -337,8 +347,8 @@ def main():
 
     reported = {}
     for name, c, k in (() if args.step_only else
-                       (("sliding_prefill", sl, "prefill_ws_kernel<256,2,2,3>"),
-                        ("global_prefill", gl, "prefill_ws_kernel<512,8,1,2>"))):
+                       (("sliding_prefill", sl, "prefill_ws_kernel<256,2,2,3,32>"),
+                        ("global_prefill", gl, "prefill_ws_kernel<512,8,1,2,32>"))):
         prefill(c)
         t = time_calls(lambda: prefill(c), args.reps)
         ms = float(np.mean(t))
@@ -404,7 +414,7 @@ def main():
         gbs = dbytes / (ms * 1e-3) / 1e9
         strict = {"value": gbs, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "ms_mean": ms,
                   "ms_min": float(np.min(t)), "batch": DB,
-                  "kernel": "PagedOf prefill_ws_kernel<512,8,1,2> (one-token chunks)",
+                  "kernel": "PagedOf prefill_ws_kernel<512,8,1,2,32> (one-token chunks)",
                   "note": "bytes equal to the prefill row L-1 (tested); the split decode agrees "
                           "within the parity tolerance"}
         log(f"strict decode B={DB}: {ms:.3f} ms ({gbs:.0f} GB/s)")

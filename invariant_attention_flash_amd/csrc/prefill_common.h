@@ -144,10 +144,11 @@ __device__ __forceinline__ SeqGeo seq_geo(const int32_t* cu, const PagedKv& pk, 
   return s;
 }
 
-// Sources of the direct loads of one 32-key tile.  With four waves, wave w
-// loads tile rows [8w, 8w+8), which in the paged layout (16-key cache blocks)
-// lie in block 2*kt + w/2.  `live` = false gives empty resources (the loads
-// write zeros).  k0 is the row offset dma_rows adds to the tile row.
+// Sources of the direct loads of one tile of BN keys.  With four loading
+// waves, wave w loads tile rows [RPW*w, RPW*w + RPW), which in the paged
+// layout (16-key cache blocks) lie in block (BN*kt + RPW*w) / 16.  `live` =
+// false gives empty resources (the loads write zeros).  k0 is the row offset
+// dma_rows adds to the tile row.
 //
 // Paged layout: only cache blocks holding keys in [klo, L) are read (klo =
 // the first key the sequence's first query row may attend); the other rows of
@@ -166,17 +167,22 @@ struct KvTiles {
   int L;
   uint32_t rs_bytes;   // bytes between consecutive keys of one KV head
 
+  // BN: keys per tile; RPW: tile rows each loading wave loads (wave w loads
+  // rows [RPW*w, RPW*w + RPW), all inside one 16-key cache block).
+  template <int BN = 32, int RPW = 8>
   __device__ __forceinline__ void get(int kt, bool live, int wave, u32x4& krs, u32x4& vrs,
                                       int& k0) const {
+    static_assert(16 % RPW == 0 && BN % 16 == 0, "a wave's rows lie in one cache block");
     if constexpr (!PAGED) {
       const int nb = live ? (int)((uint32_t)L * rs_bytes) : 0;
       krs = buffer_rsrc(kbase, nb);
       vrs = buffer_rsrc(vbase, nb);
-      k0 = kt * 32;
+      k0 = kt * BN;
     } else {
       // Branch-free: the table entry is always read (its index clamped into
       // the row), then dropped through rows = 0 when the block is not needed.
-      const int j = 2 * kt + (wave >> 1);
+      const int first = RPW * wave;  // first tile row of this wave
+      const int j = (kt * BN + first) >> 4;
       const int left = L - 16 * j;
       int rows = left < 16 ? left : 16;
       const bool need = live && left > 0 && j < max_blocks && 16 * j + 16 > klo;
@@ -194,7 +200,7 @@ struct KvTiles {
       const int nb = (int)((uint32_t)rows * rs_bytes);
       krs = buffer_rsrc(kbase + off, nb);
       vrs = buffer_rsrc(vbase + off, nb);
-      k0 = -16 * (wave >> 1);
+      k0 = -16 * (first >> 4);
     }
   }
 };
@@ -225,22 +231,23 @@ __device__ __forceinline__ KvTiles<PAGED> kv_tiles(const bf16* k, const bf16* v,
   return src;
 }
 
-// Scores of row block rb as 8 slot values, masked when MASK.  Key j is
+// Scores of row block rb as NS slot values (8 for 32-key tiles, 4 for 16),
+// masked when MASK.  Key j is
 // allowed for a row at position qp when 0 <= qp - j < wlim (causal, window)
 // or j lies in the row's span [ss, se); both tests are one unsigned compare
 // each: wbase = qp - k0 - 4*gq, sbase = k0 + 4*gq - ss.
-template <bool MASK>
+template <bool MASK, int NS = 8>
 __device__ __forceinline__ void tile_values(const f32x4 (*s)[2], int rb, int k0, const Lane16& ln,
                                             const int* qpos, const int* ss, const int* se,
                                             float* v) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = s[rb][e >> 2][e & 3];
+  for (int e = 0; e < NS; ++e) v[e] = s[rb][e >> 2][e & 3];
   if constexpr (MASK) {
     const int wbase = qpos[rb] - k0 - 4 * ln.gq;
     const int sbase = k0 + 4 * ln.gq - ss[rb];
     const uint32_t slen = (uint32_t)(se[rb] - ss[rb]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NS; ++e) {
       const int c = 16 * (e >> 2) + (e & 3);  // key j = k0 + 4*gq + c
       const bool ok = ((uint32_t)(wbase - c) < (uint32_t)ln.wlim) | ((uint32_t)(sbase + c) < slen);
       v[e] = ok ? v[e] : kNegInf;
@@ -265,10 +272,11 @@ __device__ __forceinline__ float probs(const float* v, float c2, float msub, bf1
   return hp.lo + hp.hi;
 }
 
-// Scaled tile max of a row (max over the 8 slots, then lanes l^32, l^16).
+// Scaled tile max of a row (max over the NS slots, then lanes l^32, l^16).
+template <int NS = 8>
 __device__ __forceinline__ float row_max_scaled(const float* v, float c2) {
-  float t = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                  fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+  float t = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+  if constexpr (NS == 8) t = fmaxf(t, fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
   HalfPair hp = half_pair(t);
   t = fmaxf(hp.lo, hp.hi);
   hp = row_pair(t);
@@ -349,8 +357,8 @@ __device__ __forceinline__ uint32_t softmax_move(const f32x4 (*s)[2], int k0, co
 //     p of the row exceeds it without a move), or, while m = -inf, when the
 //     tile holds an allowed key (whatever its p against the provisional 0);
 //     the fast path then needs no row max;
-//   * the running sum is kept per lane: each lane adds its 8 slots of a tile
-//     in slot order, (((p0 + p1) + p2) + ...) + p7, to its own l (scaled by
+//   * the running sum is kept per lane: each lane adds its NS slots of a
+//     tile in slot order, ((p0 + p1) + p2) + ..., to its own l (scaled by
 //     alpha on a move), and the four lanes of a row are combined once, after
 //     the last tile, as (l + l^32) then + l^16 (each step: lower lane's value
 //     + upper lane's value).
@@ -380,24 +388,25 @@ struct RowStats {
 };
 
 // p of one row block (recomputed on the rare path) and the lane's sum of its
-// 8 slots in slot order.
+// NS slots in slot order.
+template <int NS = 8>
 __device__ __forceinline__ float probs_lane(const float* v, float c2, float msub, bf16x8& pb) {
-  float p[8];
+  float p[NS];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = fast_exp2(__builtin_fmaf(v[e], c2, -msub));
+  for (int e = 0; e < NS; ++e) p[e] = fast_exp2(__builtin_fmaf(v[e], c2, -msub));
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pb[e] = to_bf16(p[e]);
+  for (int e = 0; e < NS; ++e) pb[e] = to_bf16(p[e]);
   float sum = p[0];
 #pragma unroll
-  for (int e = 1; e < 8; ++e) sum = sum + p[e];
+  for (int e = 1; e < NS; ++e) sum = sum + p[e];
   return sum;
 }
 
-// Fast-path state of one tile: stage g (g < 8*RB) takes slot g%8 of row
-// block g/8.
-template <int RB, bool MASK>
+// Fast-path state of one tile: stage g (g < NS*RB) takes slot g%NS of row
+// block g/NS (NS = 8 slots for 32-key tiles, 4 for 16-key tiles).
+template <int RB, bool MASK, int NS = 8>
 struct TileSoftmax {
-  static constexpr int kStages = 8 * RB;
+  static constexpr int kStages = NS * RB;
   float part[RB];   // the lane's tile sum (slot order); also the move test
   bool anyok[RB];   // MASK: some slot of the lane holds an allowed key
   bf16x8 pb[RB];    // P operand
@@ -420,7 +429,7 @@ struct TileSoftmax {
   __device__ __forceinline__ void stage(int g, const f32x4 (*s)[2], const Lane16& ln,
                                         const RowStats<RB>& st) {
     if (g < 0 || g >= kStages) return;
-    const int rb = g / 8, e = g % 8;
+    const int rb = g / NS, e = g % NS;
     float x = s[rb][e >> 2][e & 3];
     if constexpr (MASK) {
       const int c = 16 * (e >> 2) + (e & 3);  // key k0 + 4*gq + c
@@ -479,14 +488,14 @@ struct TileSoftmax {
         st.l[rb] += part[rb];
         continue;
       }
-      float x[8];
-      tile_values<MASK>(s, rb, k0, ln, qpos, ss, se, x);
-      const float tmax = row_max_scaled(x, ln.c2);
+      float x[NS];
+      tile_values<MASK, NS>(s, rb, k0, ln, qpos, ss, se, x);
+      const float tmax = row_max_scaled<NS>(x, ln.c2);
       mv = first ? (tmax != kNegInf) : mv;
       const float m_new = mv ? tmax : m_old;
       const float a = (mv & !first) ? fast_exp2(m_old - m_new) : 1.f;
-      bf16x8 pnew;
-      const float snew = probs_lane(x, ln.c2, mv ? m_new : st.msub[rb], pnew);
+      bf16x8 pnew = {};
+      const float snew = probs_lane<NS>(x, ln.c2, mv ? m_new : st.msub[rb], pnew);
       if (mv) {
         pb[rb] = pnew;
         st.l[rb] = st.l[rb] * a + snew;

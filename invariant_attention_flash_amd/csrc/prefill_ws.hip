@@ -48,14 +48,19 @@
 
 namespace invattn {
 
-template <int D_, int G_, int RB_, int NR_>
+template <int D_, int G_, int RB_, int NR_, int BN_>
 struct PfWsCfg {
   static constexpr bool kPaged = false;  // contiguous keys (PagedOf<> sets it)
   static constexpr int D = D_, G = G_;
   static constexpr int kRoleWaves = 4;                 // waves of each kind
   static constexpr int kWaves = 2 * kRoleWaves;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int BN = 32;                        // keys per KV tile
+  static constexpr int BN = BN_;                       // keys per KV tile: 32 or 16
+  static constexpr int kHalves = BN / 16;              // 16-key halves of a tile
+  static constexpr int kSlots = 4 * kHalves;           // scores per lane per row block
+  // P^T exchange element of one lane and row block: 8 bf16 (32-key tiles,
+  // 16x16x32 PV MFMAs) or 4 bf16 (16-key tiles, 16x16x16 PV MFMAs).
+  using PT = typename std::conditional<BN == 32, bf16x8, bf16x4>::type;
   static constexpr int RB = RB_;                       // score row blocks per score wave
   static constexpr int kRowsPerWave = 16 * RB;
   static constexpr int kRows = kRoleWaves * kRowsPerWave;  // rows per workgroup
@@ -67,6 +72,7 @@ struct PfWsCfg {
   static constexpr int kChunks = D / 8;                // 16-byte chunks per row
   static constexpr int kTile = BN * D;                 // elements of one K (or V) tile
   static constexpr int kLoads = BN * kChunks / (64 * kRoleWaves);  // per lane per tile
+  static constexpr int kRowsPerLoader = kLoads * 64 / kChunks;       // tile rows per loading wave
   static constexpr int kSwK = kChunks >= 16 ? 15 : kChunks - 1;
   static constexpr int kSwV = kChunks >= 16 ? 14 : kChunks - 2;
   static constexpr int kRing = NR_;                    // buffers per K / V ring
@@ -77,14 +83,17 @@ struct PfWsCfg {
   static constexpr bool kPvLoadsK = D <= 256;
   static_assert(D % 64 == 0 && kRowsPerWave % G == 0, "row map");
   static_assert(kLoads >= 1 && BN * kChunks % (64 * kRoleWaves) == 0, "tile load split");
-  static_assert(BN == 32 && kRoleWaves == 4, "KvTiles: loader w reads tile rows [8w, 8w+8)");
-  static_assert(kRing == 2 || kRing == 3, "ring of two or three tiles");
-  static_assert(kRing * 2 * kTile * 2 + 2 * kRowBlocks * 64 * 16 + 3 * kRows * 4 + 32 <= 163840,
+  static_assert(BN == 16 || BN == 32, "tiles of 16 or 32 keys");
+  static_assert(kRowsPerLoader * kRoleWaves == BN && 16 % kRowsPerLoader == 0,
+                "KvTiles: loading wave w reads tile rows [RPW*w, RPW*w + RPW) of one cache block");
+  static_assert(kRing >= 2 && kRing <= 4, "ring of two to four tiles");
+  static_assert(kRing * 2 * kTile * 2 + 2 * kRowBlocks * 64 * (int)sizeof(PT) + 3 * kRows * 4 +
+                        32 <= 163840,
                 "LDS budget");
 };
 
 // Score wave, one step: S^T(t+1) = K Q^T for its RB row blocks on the K tile
-// `kt`, in 2*kSt groups (one K operand each), with stage i of the previous
+// `kt`, in kHalves*kSt groups (one K operand each), with stage i of the previous
 // tile's softmax (sm) after group i's MFMAs and, when DMA (the score waves
 // load K), the K(t+NR) loads spread over the groups.  The MFMAs are compiler
 // builtins with VGPR accumulators (the kernel uses no AGPRs), so the
@@ -95,21 +104,22 @@ __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_
                                             const u32x4& krs, int kk0, uint32_t rs_bytes,
                                             int widx, int lane, uint32_t krow, uint32_t kq16,
                                             const bf16x8 (*q)[C::kSt], f32x4 (*s)[2], SM&& sm) {
-  constexpr int kN = 2 * C::kSt;              // groups
+  constexpr int kN = C::kHalves * C::kSt;     // groups (one K operand each)
   constexpr int kEvery = kN / C::kLoads;      // groups per direct load
   constexpr int kAhead = 3;
   static_assert(kN % C::kLoads == 0, "loads spread evenly over the groups");
   const char* kb0 = reinterpret_cast<const char*>(kt) + krow;
+  // Group i: k-step i / kHalves, 16-key half i % kHalves.
   auto kread = [&](int i) {
     return ld_lds_x8(reinterpret_cast<const bf16*>(
-        kb0 + (kq16 ^ (uint32_t)((i >> 1) << 6)) + (i & 1) * 32 * C::D));
+        kb0 + (kq16 ^ (uint32_t)((i / C::kHalves) << 6)) + (i % C::kHalves) * 32 * C::D));
   };
   bf16x8 kop[kAhead];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) kop[i] = kread(i);
 #pragma unroll
   for (int i = 0; i < kN; ++i) {
-    const int st = i >> 1, kb = i & 1;
+    const int st = i / C::kHalves, kb = i % C::kHalves;
     const bf16x8 a = kop[i % kAhead];
     if (i + kAhead < kN) kop[i % kAhead] = kread(i + kAhead);
     if constexpr (DMA) {
@@ -129,13 +139,15 @@ __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_
 // block, V from the tile `vt`, P^T from the exchange buffer `pt`, with the
 // step's tile loads (K first when this wave loads K, then V; kLoads of each
 // per lane) spread over the MFMA groups.
-//   V operand (output block db): rows 4*gq + x/4 and +16, logical chunk
-//     2*(kDbW*p + db) + (x%4)/2, physical chunk ^ ((2*row) & kSwV),
-//     element 4*(x%2);
-//   P^T operand (row block r): 16 bytes of lane l at pt[64*r + l].
+//   V operand (output block db): rows 4*gq + x/4 (and +16 for 32-key tiles),
+//     logical chunk 2*(kDbW*p + db) + (x%4)/2, physical chunk ^ ((2*row) &
+//     kSwV), element 4*(x%2);
+//   P^T operand (row block r): lane l's element pt[64*r + l]; 16x16x32 MFMAs
+//     over the 32 keys of a tile, or 16x16x16 MFMAs over the 16 of a
+//     16-key tile.
 template <class C, bool DMA>
 __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
-                                         const bf16x8* __restrict__ pt, uint32_t kpre,
+                                         const typename C::PT* __restrict__ pt, uint32_t kpre,
                                          const u32x4& krs, int kk0, uint32_t vpre,
                                          const u32x4& vrs, int vk0, uint32_t rs_bytes, int widx,
                                          int lane,
@@ -148,14 +160,16 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
   constexpr int kEvery = kN >= kL ? kN / kL : 1;
   constexpr int kPer = kN >= kL ? 1 : kL / kN;
   static_assert(kN % kL == 0 || kL % kN == 0, "loads spread evenly over the groups");
+  using PT = typename C::PT;
   const char* vb0 = reinterpret_cast<const char*>(vt) + vrow;
-  bf16x8 vop[C::kDbW];
+  PT vop[C::kDbW];
 #pragma unroll
   for (int db = 0; db < C::kDbW; ++db) {
     const bf16* p = reinterpret_cast<const bf16*>(vb0 + (vc16w ^ (uint32_t)(db << 5)));
-    vop[db] = cat8(ld_lds_tr(p), ld_lds_tr(p + 16 * C::D));
+    if constexpr (C::BN == 32) vop[db] = cat8(ld_lds_tr(p), ld_lds_tr(p + 16 * C::D));
+    else vop[db] = ld_lds_tr(p);
   }
-  bf16x8 pop[2];
+  PT pop[2];
   pop[0] = pt[lane];
 #pragma unroll
   for (int r = 0; r < kN; ++r) {
@@ -174,8 +188,10 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
       }
     }
 #pragma unroll
-    for (int db = 0; db < C::kDbW; ++db)
-      o[r][db] = mfma16(vop[db], pop[r & 1], o[r][db]);
+    for (int db = 0; db < C::kDbW; ++db) {
+      if constexpr (C::BN == 32) o[r][db] = mfma16(vop[db], pop[r & 1], o[r][db]);
+      else o[r][db] = mfma16k16(vop[db], pop[r & 1], o[r][db]);
+    }
   }
 }
 
@@ -194,7 +210,7 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // tile kt (index kt & 1); the final row sums.
   __shared__ __attribute__((aligned(1024))) bf16 ks[NR][C::kTile];
   __shared__ __attribute__((aligned(1024))) bf16 vs[NR][C::kTile];
-  __shared__ __attribute__((aligned(1024))) bf16x8 pl[2][kRB * 64];
+  __shared__ __attribute__((aligned(1024))) typename C::PT pl[2][kRB * 64];
   __shared__ __attribute__((aligned(16))) float al[2][C::kRows];
   __shared__ __attribute__((aligned(16))) uint32_t fl[2][4];
   __shared__ __attribute__((aligned(16))) float lrow[C::kRows];
@@ -301,7 +317,8 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int i = 0; i < NR; ++i) {
         u32x4 krsc, vrsc;
         int k0r;
-        src.get(kt0 + i, kt0 + i < kt1, widx, krsc, vrsc, k0r);
+        src.template get<C::BN, C::kRowsPerLoader>(kt0 + i, kt0 + i < kt1, widx, krsc, vrsc,
+                                                   k0r);
 #pragma unroll
         for (int j = 0; j < C::kLoads; ++j)
           dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(ks_lds + i * kTileBytes, krsc, k0r, j,
@@ -336,14 +353,15 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const uint32_t kq16 = opaque(ln.kq16);
       u32x4 krs, unused;
       int kk0 = 0;
-      if constexpr (kLoadK) src.get(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
+      if constexpr (kLoadK)
+        src.template get<C::BN, C::kRowsPerLoader>(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
       else krs = unused = u32x4{};
       float alpha[RB];
       uint32_t smask = 0;
       bf16x8 pc[RB];
       auto run = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        TileSoftmax<RB, MASK> ts;
+        TileSoftmax<RB, MASK, C::kSlots> ts;
         ts.init(k0, ln, qpos, my_ss, my_se);
         score_phase<C, kLoadK>(kcur, kpre, krs, kk0, rs_bytes, widx, lane, ln.krow, kq16, qr, sn,
                                [&](int i) { ts.stage(i, sc, ln, rs); });
@@ -357,9 +375,12 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         run(std::false_type{});
       // Exchange: P(kt) of this wave's row blocks, its scaling flags and
       // (when set) the row factors.
-      bf16x8* pw = pl[kt & 1];
+      typename C::PT* pw = pl[kt & 1];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) pw[64 * (RB * widx + rb) + lane] = pc[rb];
+      for (int rb = 0; rb < RB; ++rb) {
+        if constexpr (C::BN == 32) pw[64 * (RB * widx + rb) + lane] = pc[rb];
+        else pw[64 * (RB * widx + rb) + lane] = bf16x4{pc[rb][0], pc[rb][1], pc[rb][2], pc[rb][3]};
+      }
       if (smask != 0) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -404,7 +425,7 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   auto load_tile = [&](int slot, int kt, int which) {
     u32x4 krsc, vrsc;
     int k0r;
-    src.get(kt, kt < kt1, widx, krsc, vrsc, k0r);
+    src.template get<C::BN, C::kRowsPerLoader>(kt, kt < kt1, widx, krsc, vrsc, k0r);
     if (which & 1) {
 #pragma unroll
       for (int i = 0; i < C::kLoads; ++i)
@@ -475,13 +496,15 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bf16* __restrict__ vcur = vs[(r + NR - 1) % NR];           // V(kt-1)
     const uint32_t kpre = ks_lds + r * kTileBytes;                    // K(kt+NR)
     const uint32_t vpre = vs_lds + ((r + NR - 2) % NR) * kTileBytes;  // V(kt+NR-2)
-    const bf16x8* __restrict__ pcur = pl[(kt - 1) & 1];             // P(kt-1)
+    const typename C::PT* __restrict__ pcur = pl[(kt - 1) & 1];     // P(kt-1)
     wait_vmcnt<(NR - 2) * kStepLoads>();
     lds_barrier();
     u32x4 krs{}, vrs, unused;
     int kk0 = 0, vk0;
-    if constexpr (kLoadK) src.get(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
-    src.get(kt + NR - 2, kt + NR - 2 < kt1, widx, unused, vrs, vk0);
+    if constexpr (kLoadK)
+      src.template get<C::BN, C::kRowsPerLoader>(kt + NR, kt + NR < kt1, widx, krs, unused, kk0);
+    src.template get<C::BN, C::kRowsPerLoader>(kt + NR - 2, kt + NR - 2 < kt1, widx, unused, vrs,
+                                               vk0);
     if constexpr (MODE == 0) {
       // No PV yet: only the loads.
       if constexpr (kLoadK) {
@@ -556,19 +579,22 @@ static hipError_t launch_ws(const PrefillArgs& a, hipStream_t stream) {
 
 // One kernel instance per (head_dim, group).  Parameters after (D, G): score
 // row blocks per score wave (Q of 16*RB rows in 64 VGPRs: 2 at head dim 256,
-// 1 at 512), buffers per K/V ring (3 at 256; 2 at 512, where a tile of 32
-// keys is 32 KB).
-#define INVATTN_WS_TABLE(X)                                       \
-  X(256, 1, 2, 3) X(256, 2, 2, 3) X(256, 4, 2, 3) X(256, 8, 2, 3) \
-  X(512, 1, 1, 2) X(512, 2, 1, 2) X(512, 4, 1, 2) X(512, 8, 1, 2)
+// 1 at 512), buffers per K/V ring (3 at 256; 2 at 512, where a 32-key tile
+// is 32 KB), keys per tile.  (Head dim 512 on 16-key tiles in rings of four
+// runs its loads three 16-key steps ahead instead of one 32-key step: the
+// one-token chunks of the paged entry point gain, but the prefill loses to
+// the doubled per-step cost, so 32-key tiles stay.)
+#define INVATTN_WS_TABLE(X)                                               \
+  X(256, 1, 2, 3, 32) X(256, 2, 2, 3, 32) X(256, 4, 2, 3, 32) X(256, 8, 2, 3, 32) \
+  X(512, 1, 1, 2, 32) X(512, 2, 1, 2, 32) X(512, 4, 1, 2, 32) X(512, 8, 1, 2, 32)
 
 bool prefill_ws_schedule(int d, int group, PrefillSchedule* s) {
-#define X(D, G, RB, NR)                                                       \
-  if (d == D && group == G) {                                                 \
-    using C = PfWsCfg<D, G, RB, NR>;                                          \
-    *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads,         \
-                         "prefill_ws_kernel<" #D "," #G "," #RB "," #NR ">"}; \
-    return true;                                                              \
+#define X(D, G, RB, NR, TBN)                                                         \
+  if (d == D && group == G) {                                                        \
+    using C = PfWsCfg<D, G, RB, NR, TBN>;                                            \
+    *s = PrefillSchedule{C::kRows, C::kPositions, C::BN, C::kThreads,                \
+                         "prefill_ws_kernel<" #D "," #G "," #RB "," #NR "," #TBN ">"}; \
+    return true;                                                                     \
   }
   INVATTN_WS_TABLE(X)
 #undef X
@@ -577,8 +603,8 @@ bool prefill_ws_schedule(int d, int group, PrefillSchedule* s) {
 
 hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream) {
   const int group = a.hq / a.hkv;
-#define X(D, G, RB, NR) \
-  if (a.d == D && group == G) return launch_ws<PfWsCfg<D, G, RB, NR>>(a, stream);
+#define X(D, G, RB, NR, TBN) \
+  if (a.d == D && group == G) return launch_ws<PfWsCfg<D, G, RB, NR, TBN>>(a, stream);
   INVATTN_WS_TABLE(X)
 #undef X
   return hipErrorInvalidValue;

@@ -265,6 +265,6 @@ def test_provenance_record():
     assert p["op"] == "attn_prefill_varlen" and p["fallback"] == "none"
     assert p["accumulator_dtype"] == "fp32" and p["layer_type"] == "global"
     assert p["schedule_id"].startswith("prefill_d512_g8")
-    assert p["kernel_id"] == "prefill_ws_kernel<512,8,1,2>"
+    assert p["kernel_id"].startswith("prefill_ws_kernel<512,8,")
     assert p["shape"]["max_len"] == 64
     assert p["arch"].startswith("gfx950")
