@@ -60,6 +60,10 @@ def open_library(path: str):
     lib.oracle_prefill_backward.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp,
                                             ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, i32,
                                             i32, dbl, vp, i32, i32]
+    lib.oracle_prefill_backward_units.restype = ctypes.c_int
+    lib.oracle_prefill_backward_units.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp,
+                                                  ctypes.c_int, vp, vp, vp, vp, i32, i32, i32,
+                                                  i32, i32, dbl, vp, i32, vp, i64, vp, i64, i32]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = [i32]
     return lib
@@ -161,10 +165,15 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, window=NO_WINDOW, scale=N
 
 
 def prefill_backward(q, k, v, dout, cu_seqlens, window=NO_WINDOW, scale=None, spans=None,
-                     threads=0, lib=None):
+                     threads=0, lib=None, dq_units=None, kv_units=None):
     """Gradients (dq, dk, dv) of prefill attention for the upstream gradient
     ``dout`` = dL/dO.  q/dout [T,Hq,D], k/v [T,Hkv,D]; outputs float64 in the
-    same shapes.  Same mask, spans and scale conventions as ``prefill``."""
+    same shapes.  Same mask, spans and scale conventions as ``prefill``.
+
+    ``dq_units``: optional (token, query head) pairs; dq is then [n, D], one
+    row per pair.  ``kv_units``: optional (token, KV head) pairs; dk and dv
+    are then [n, D].  Only the softmax statistics those units read are
+    formed, so a sample of a long sequence is cheap."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)
@@ -183,13 +192,22 @@ def prefill_backward(q, k, v, dout, cu_seqlens, window=NO_WINDOW, scale=None, sp
     if spans is not None and len(spans):
         sp = np.ascontiguousarray(spans, dtype=np.int32).reshape(-1, 2)
         ns = sp.shape[0]
-    dq = np.zeros((T, hq, d), np.float64)
-    dk = np.zeros((T, hkv, d), np.float64)
-    dv = np.zeros((T, hkv, d), np.float64)
-    rc = (lib or _load()).oracle_prefill_backward(
+
+    def flat(units, heads):
+        if units is None:
+            return None, 0
+        u = np.asarray(units, dtype=np.int64).reshape(-1, 2)
+        return np.ascontiguousarray(u[:, 0] * heads + u[:, 1]), u.shape[0]
+
+    dqu, n_dq = flat(dq_units, hq)
+    kvu, n_kv = flat(kv_units, hkv)
+    dq = np.zeros((T, hq, d) if dqu is None else (n_dq, d), np.float64)
+    dk = np.zeros((T, hkv, d) if kvu is None else (n_kv, d), np.float64)
+    dv = np.zeros_like(dk)
+    rc = (lib or _load()).oracle_prefill_backward_units(
         _ptr(q), _code(q), _ptr(k), _ptr(v), _code(k), _ptr(dout), _code(dout), _ptr(dq),
         _ptr(dk), _ptr(dv), _ptr(cu), cu.shape[0] - 1, hq, hkv, d, int(window), float(scale),
-        _ptr(sp), ns, int(threads))
+        _ptr(sp), ns, _ptr(dqu), n_dq, _ptr(kvu), n_kv, int(threads))
     if rc != 0:
-        raise ValueError("oracle_prefill_backward rejected its arguments")
+        raise ValueError("oracle_prefill_backward_units rejected its arguments")
     return dq, dk, dv

@@ -233,18 +233,29 @@ int oracle_decode(const void* q, int qdtype, const void* k_cache,
  *     dK[j,:] += scale * ds_j Q[i,:]                  (rows i ascending, then
  *     dV[j,:] += p_j dout[i,:]                         the group's heads)
  *
- * Same mask, GQA map and layouts as oracle_prefill.  dq [T, hq, d],
- * dk / dv [T, hkv, d] are fp64 outputs.  Two passes: rows (softmax, delta,
- * dq), then keys (dk, dv summed over every row and query head that admits
- * the key).  Returns 0, or -1 on bad arguments.
+ * Same mask, GQA map and layouts as oracle_prefill.  Three passes: the
+ * softmax statistics (lse, delta) of every (row, query head) needed, then
+ * dq per (row, query head), then dk and dv per (key row, KV head), summed
+ * over every row and query head that admits the key.
+ *
+ * dq_units / kv_units: optional lists of n_dq (token * hq + head) and n_kv
+ * (token * hkv + kv head) indices; NULL means every one.  With a list, dq
+ * (or dk and dv) is indexed by list position: dq [n_dq, d], dk / dv
+ * [n_kv, d]; without, dq [T, hq, d] and dk / dv [T, hkv, d].  Statistics
+ * are formed only for the rows the listed units read, so a few units of a
+ * long sequence cost a few rows.  Outputs are fp64.  Returns 0, or -1 on bad
+ * arguments.
  */
-int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void* v,
-                            int kvdtype, const void* dout, int dodtype,
-                            double* dq, double* dk, double* dv,
-                            const int32_t* cu_seqlens, int32_t batch, int32_t hq,
-                            int32_t hkv, int32_t d, int32_t window, double scale,
-                            const int32_t* spans, int32_t num_spans, int32_t threads) {
-    if (batch < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv) return -1;
+int oracle_prefill_backward_units(const void* q, int qdtype, const void* k, const void* v,
+                                  int kvdtype, const void* dout, int dodtype,
+                                  double* dq, double* dk, double* dv,
+                                  const int32_t* cu_seqlens, int32_t batch, int32_t hq,
+                                  int32_t hkv, int32_t d, int32_t window, double scale,
+                                  const int32_t* spans, int32_t num_spans,
+                                  const int64_t* dq_units, int64_t n_dq,
+                                  const int64_t* kv_units, int64_t n_kv, int32_t threads) {
+    if (batch < 0 || hq <= 0 || hkv <= 0 || d <= 0 || hq % hkv || n_dq < 0 || n_kv < 0)
+        return -1;
     const int64_t total = cu_seqlens[batch];
     const int32_t group = hq / hkv;
     int64_t max_len = 1;
@@ -253,12 +264,20 @@ int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void
         if (len < 0) return -1;
         if (len > max_len) max_len = len;
     }
+    if (!dq_units) n_dq = total * hq;
+    if (!kv_units) n_kv = total * hkv;
+    for (int64_t u = 0; dq_units && u < n_dq; ++u)
+        if (dq_units[u] < 0 || dq_units[u] >= total * hq) return -1;
+    for (int64_t u = 0; kv_units && u < n_kv; ++u)
+        if (kv_units[u] < 0 || kv_units[u] >= total * hkv) return -1;
     const int64_t nt = total > 0 ? total : 1;
     int32_t* seq_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)nt);
     int64_t* span_lo = (int64_t*)malloc(sizeof(int64_t) * (size_t)nt);
     int64_t* span_hi = (int64_t*)malloc(sizeof(int64_t) * (size_t)nt);
     double* lse = (double*)malloc(sizeof(double) * (size_t)(nt * hq));
     double* delta = (double*)malloc(sizeof(double) * (size_t)(nt * hq));
+    char* need = (char*)calloc((size_t)(nt * hq), 1);
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nt * hq));
     for (int32_t b = 0; b < batch; ++b)
         for (int64_t t = cu_seqlens[b]; t < cu_seqlens[b + 1]; ++t) {
             seq_of[t] = b;
@@ -269,18 +288,32 @@ int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void
                     span_hi[t] = spans[2 * sp + 1] - cu_seqlens[b];
                 }
         }
+    /* Which (row, query head) statistics the listed units read. */
+    for (int64_t u = 0; u < n_dq; ++u) need[dq_units ? dq_units[u] : u] = 1;
+    for (int64_t u = 0; u < n_kv; ++u) {
+        int64_t w = kv_units ? kv_units[u] : u, tj = w / hkv;
+        int32_t g = (int32_t)(w % hkv), b = seq_of[tj];
+        int64_t start = cu_seqlens[b], len = cu_seqlens[b + 1] - start, j = tj - start;
+        for (int64_t i = 0; i < len; ++i)
+            if (allowed(i, j, window, span_lo[start + i], span_hi[start + i]))
+                for (int32_t h = g * group; h < (g + 1) * group; ++h)
+                    need[(start + i) * hq + h] = 1;
+    }
+    int64_t n_rows = 0;
+    for (int64_t w = 0; w < total * hq; ++w)
+        if (need[w]) rows[n_rows++] = w;
 #ifdef _OPENMP
     if (threads > 0) omp_set_num_threads(threads);
 #endif
-    /* Pass 1: per (row, query head). */
+    /* Pass 1: softmax statistics per needed (row, query head). */
 #pragma omp parallel
     {
         double* s = (double*)malloc(sizeof(double) * (size_t)max_len);
         int64_t* key_off = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_len);
         double* o = (double*)malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(dynamic, 16)
-        for (int64_t w = 0; w < total * hq; ++w) {
-            int64_t t = w / hq;
+        for (int64_t r = 0; r < n_rows; ++r) {
+            int64_t w = rows[r], t = w / hq;
             int32_t h = (int32_t)(w % hq), g = h / group, b = seq_of[t];
             int64_t start = cu_seqlens[b], len = cu_seqlens[b + 1] - start, i = t - start;
             int64_t n = 0;
@@ -293,7 +326,26 @@ int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void
             double del = 0.0;
             for (int32_t c = 0; c < d; ++c) del += load_elem(dout, dodtype, w * (int64_t)d + c) * o[c];
             delta[w] = del;
-            double* dqi = dq + w * (int64_t)d;
+        }
+        free(s);
+        free(key_off);
+        free(o);
+    }
+    /* Pass 2: dq per listed (row, query head). */
+#pragma omp parallel
+    {
+        int64_t* key_off = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_len);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t u = 0; u < n_dq; ++u) {
+            int64_t w = dq_units ? dq_units[u] : u, t = w / hq;
+            int32_t h = (int32_t)(w % hq), g = h / group, b = seq_of[t];
+            int64_t start = cu_seqlens[b], len = cu_seqlens[b + 1] - start, i = t - start;
+            int64_t n = 0;
+            for (int64_t j = 0; j < len; ++j)
+                if (allowed(i, j, window, span_lo[t], span_hi[t]))
+                    key_off[n++] = ((start + j) * hkv + g) * (int64_t)d;
+            double del = delta[w];
+            double* dqi = dq + u * (int64_t)d;
             for (int32_t c = 0; c < d; ++c) dqi[c] = 0.0;
             for (int64_t a = 0; a < n; ++a) {
                 double dot = 0.0, dp = 0.0;
@@ -301,23 +353,21 @@ int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void
                     dot += load_elem(q, qdtype, w * (int64_t)d + c) * load_elem(k, kvdtype, key_off[a] + c);
                     dp += load_elem(dout, dodtype, w * (int64_t)d + c) * load_elem(v, kvdtype, key_off[a] + c);
                 }
-                double p = exp(scale * dot - l);
+                double p = exp(scale * dot - lse[w]);
                 double ds = p * (dp - del);
                 for (int32_t c = 0; c < d; ++c) dqi[c] += scale * ds * load_elem(k, kvdtype, key_off[a] + c);
             }
         }
-        free(s);
         free(key_off);
-        free(o);
     }
-    /* Pass 2: per (key row, KV head). */
+    /* Pass 3: dk, dv per listed (key row, KV head). */
 #pragma omp parallel for schedule(dynamic, 16)
-    for (int64_t w = 0; w < total * hkv; ++w) {
-        int64_t tj = w / hkv;
+    for (int64_t u = 0; u < n_kv; ++u) {
+        int64_t w = kv_units ? kv_units[u] : u, tj = w / hkv;
         int32_t g = (int32_t)(w % hkv), b = seq_of[tj];
         int64_t start = cu_seqlens[b], len = cu_seqlens[b + 1] - start, j = tj - start;
-        double* dkj = dk + w * (int64_t)d;
-        double* dvj = dv + w * (int64_t)d;
+        double* dkj = dk + u * (int64_t)d;
+        double* dvj = dv + u * (int64_t)d;
         for (int32_t c = 0; c < d; ++c) dkj[c] = dvj[c] = 0.0;
         for (int64_t i = 0; i < len; ++i) {
             int64_t ti = start + i;
@@ -343,7 +393,21 @@ int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void
     free(span_hi);
     free(lse);
     free(delta);
+    free(need);
+    free(rows);
     return 0;
+}
+
+/* Every dq, dk and dv: dq [T, hq, d], dk / dv [T, hkv, d]. */
+int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void* v,
+                            int kvdtype, const void* dout, int dodtype,
+                            double* dq, double* dk, double* dv,
+                            const int32_t* cu_seqlens, int32_t batch, int32_t hq,
+                            int32_t hkv, int32_t d, int32_t window, double scale,
+                            const int32_t* spans, int32_t num_spans, int32_t threads) {
+    return oracle_prefill_backward_units(q, qdtype, k, v, kvdtype, dout, dodtype, dq, dk, dv,
+                                         cu_seqlens, batch, hq, hkv, d, window, scale, spans,
+                                         num_spans, NULL, 0, NULL, 0, threads);
 }
 
 /* Number of threads an OpenMP region of this library runs with. */

@@ -249,7 +249,7 @@ def pin_decode(lib=None):
 
 # ------------------------------------------------------------------ backward
 def _loss(q, k, v, dout, cu, window, spans, lib):
-    """L = sum(dout * O) through the forward oracle (fp64 inputs)."""
+    """L = sum(dout * O) through the forward oracle (fp64 inputs, scale 0.4)."""
     o = oracle.prefill(q, k, v, cu, window=window, scale=0.4, spans=spans, lib=lib)
     return float((dout * o).sum())
 
@@ -319,6 +319,39 @@ def pin_backward_gqa_is_mha_summed(lib=None):
 # consistency", section 4 item 5: inputs in their declared dtype; "Gated
 # RMSNorm CUDA kernel for the GDN block", accuracy against FP64 on the exact
 # stored inputs).  These pins fix the oracle's widening of those patterns.
+
+def pin_backward_units(lib=None):
+    """A list of (row, head) and (key, KV head) units: each listed entry of
+    dq, dk, dv equals the central difference of L = sum(dout * O) through
+    the forward oracle, and equals the same entry of the unlisted call."""
+    rng = np.random.default_rng(44)
+    cu = [0, 7, 13]
+    spans = [[8, 11]]
+    q = rng.standard_normal((13, 4, 5))
+    k = rng.standard_normal((13, 2, 5))
+    v = rng.standard_normal((13, 2, 5))
+    dout = rng.standard_normal((13, 4, 5))
+    dq_units = [(6, 3), (0, 0), (9, 1), (12, 2)]
+    kv_units = [(2, 1), (8, 0), (12, 1), (0, 0)]
+    dq, dk, dv = oracle.prefill_backward(q, k, v, dout, cu, window=4, scale=0.4, spans=spans,
+                                         lib=lib, dq_units=dq_units, kv_units=kv_units)
+    fq, fk, fv = oracle.prefill_backward(q, k, v, dout, cu, window=4, scale=0.4, spans=spans,
+                                         lib=lib)
+    assert np.array_equal(dq, np.stack([fq[t, h] for t, h in dq_units]))
+    assert np.array_equal(dk, np.stack([fk[t, g] for t, g in kv_units]))
+    assert np.array_equal(dv, np.stack([fv[t, g] for t, g in kv_units]))
+    eps = 1e-5
+    for x, units, g in ((q, dq_units, dq), (k, kv_units, dk), (v, kv_units, dv)):
+        for u, (t, h) in enumerate(units):
+            for c in range(x.shape[2]):
+                old = x[t, h, c]
+                x[t, h, c] = old + eps
+                up = _loss(q, k, v, dout, cu, 4, spans, lib)
+                x[t, h, c] = old - eps
+                dn = _loss(q, k, v, dout, cu, 4, spans, lib)
+                x[t, h, c] = old
+                assert abs((up - dn) / (2 * eps) - g[u, c]) <= 1e-7
+
 
 def _bf16_exact(bits):
     """Exact value of one bf16 pattern from its fields, in Fractions."""
@@ -403,5 +436,5 @@ ALL_PINS = [pin_golden, pin_bruteforce, pin_rows_sum_to_one,
             pin_zero_query_is_mean, pin_dominant_key, pin_gqa_reduces_to_mha,
             pin_packing_invariance, pin_row_subset, pin_decode,
             pin_backward_finite_differences, pin_backward_single_key,
-            pin_backward_gqa_is_mha_summed, pin_bf16_widening,
+            pin_backward_gqa_is_mha_summed, pin_backward_units, pin_bf16_widening,
             pin_bruteforce_stored_formats]

@@ -37,6 +37,13 @@ int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void
                             double* dv, const int32_t* cu_seqlens, int32_t batch, int32_t hq,
                             int32_t hkv, int32_t d, int32_t window, double scale,
                             const int32_t* spans, int32_t num_spans, int32_t threads);
+int oracle_prefill_backward_units(const void* q, int qdtype, const void* k, const void* v,
+                                  int kvdtype, const void* dout, int dodtype, double* dq,
+                                  double* dk, double* dv, const int32_t* cu_seqlens,
+                                  int32_t batch, int32_t hq, int32_t hkv, int32_t d,
+                                  int32_t window, double scale, const int32_t* spans,
+                                  int32_t num_spans, const int64_t* dq_units, int64_t n_dq,
+                                  const int64_t* kv_units, int64_t n_kv, int32_t threads);
 
 static double frand(unsigned* s) {
   *s = *s * 1103515245u + 12345u;
@@ -104,6 +111,20 @@ int main(void) {
   CHECK(oracle_prefill_backward(q, 2, k, v, 2, dout, 2, dq, dk, dv, cu, 3, HQ, HKV, D, 5, 0.35,
                                 &spans[0][0], 2, 2) == 0);
   for (int i = 0; i < T * HKV * D; ++i) CHECK(isfinite(dk[i]) && isfinite(dv[i]));
+  /* a few listed units: the same values as the full call */
+  const int64_t dq_units[3] = {0, 7 * HQ + 1, (T - 1) * HQ + HQ - 1};
+  const int64_t kv_units[2] = {HKV - 1, (T - 1) * HKV};
+  double uq[3 * D], uk[2 * D], uv[2 * D];
+  CHECK(oracle_prefill_backward_units(q, 2, k, v, 2, dout, 2, uq, uk, uv, cu, 3, HQ, HKV, D, 5,
+                                      0.35, &spans[0][0], 2, dq_units, 3, kv_units, 2, 2) == 0);
+  for (int u = 0; u < 3; ++u)
+    for (int c = 0; c < D; ++c) CHECK(uq[u * D + c] == dq[dq_units[u] * D + c]);
+  for (int u = 0; u < 2; ++u)
+    for (int c = 0; c < D; ++c)
+      CHECK(uk[u * D + c] == dk[kv_units[u] * D + c] && uv[u * D + c] == dv[kv_units[u] * D + c]);
+  const int64_t bad_unit[1] = {(int64_t)T * HQ};
+  CHECK(oracle_prefill_backward_units(q, 2, k, v, 2, dout, 2, uq, uk, uv, cu, 3, HQ, HKV, D, 5,
+                                      0.35, &spans[0][0], 2, bad_unit, 1, NULL, 0, 2) == -1);
   printf("oracle driver ok\n");
   return 0;
 }

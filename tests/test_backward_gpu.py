@@ -186,11 +186,35 @@ def test_rows_outside_sequences_untouched_and_empty():
     torch.cuda.synchronize()
 
 
+def sampled_parity(full, cu, case, i, seed, n_dq=48, n_kv=32, kv_from=0, kv_heads=None):
+    """Gradients of sequence i of a full-size launch against the oracle on
+    that sequence alone, at seeded units: dq at n_dq (row, query head) pairs,
+    dk and dv at n_kv (key, KV head) pairs with keys in [kv_from, L) and
+    heads from kv_heads (default all).  The first and last rows and the last
+    key are always among them."""
+    s = case.seqs[i]
+    L = s.length
+    rng = np.random.default_rng([seed, i])
+    heads = np.arange(case.hkv) if kv_heads is None else np.asarray(kv_heads)
+    dq_units = np.stack([rng.integers(0, L, n_dq), rng.integers(0, case.hq, n_dq)], 1)
+    dq_units[0], dq_units[1] = (0, 0), (L - 1, case.hq - 1)
+    kv_units = np.stack([rng.integers(kv_from, L, n_kv), rng.choice(heads, n_kv)], 1)
+    kv_units[0] = (L - 1, heads[0])
+    rq, rk, rv = oracle.prefill_backward(s.q, s.k, s.v, case.dout_of[i], [0, L],
+                                         window=case.window, scale=case.scale,
+                                         dq_units=dq_units, kv_units=kv_units)
+    o = cu[i]
+    grad_gate(full[0][o + dq_units[:, 0], dq_units[:, 1]], rq, f"seq {i} (L {L}) dq")
+    grad_gate(full[1][o + kv_units[:, 0], kv_units[:, 1]], rk, f"seq {i} (L {L}) dk")
+    grad_gate(full[2][o + kv_units[:, 0], kv_units[:, 1]], rv, f"seq {i} (L {L}) dv")
+
+
 def test_full_size_sliding_workload():
     """The benchmark's sliding prefill (8 sequences, lengths U[512, 4096],
     32/16 heads, head dim 256, window 1024) in the launch the benchmark
     times: every sequence's dq, dk and dv alone equal its rows of the packed
-    batch to the bit, and the shortest sequence matches the oracle."""
+    batch to the bit, the shortest sequence matches the oracle everywhere and
+    the longest at seeded units spread over the whole sequence."""
     case = synth.sliding_case()
     case.dout_of = [synth.upstream_grad(900 + i, (s.length, case.hq, case.d))
                     for i, s in enumerate(case.seqs)]
@@ -217,6 +241,7 @@ def test_full_size_sliding_workload():
     grad_gate(full[0][sl], rq, "full dq")
     grad_gate(full[1][sl], rk, "full dk")
     grad_gate(full[2][sl], rv, "full dv")
+    sampled_parity(full, cu, case, int(np.argmax(lengths)), 77)
 
 
 def test_validation_rejects_bad_indices(monkeypatch):
@@ -247,11 +272,13 @@ def test_validation_rejects_bad_indices(monkeypatch):
     assert np.isfinite(dq.cpu().numpy()).all()
 
 
-def test_full_size_global_workload_invariance():
+def test_full_size_global_workload():
     """The global-layer prefill (4 sequences of 2048-8192 tokens, 32/4 heads,
     head dim 512): every sequence's dq, dk and dv alone equal its rows of the
-    packed batch to the bit (oracle parity at this head dim is covered by the
-    small cases)."""
+    packed batch to the bit, and the shortest and longest sequences match the
+    oracle at seeded units: dq at rows spread over the sequence, dk and dv at
+    keys of the last 256 positions of two KV heads (a key's gradient reads
+    every later row, so keys near the end keep the oracle's cost small)."""
     case = synth.global_case()
     case.dout_of = [synth.upstream_grad(950 + i, (s.length, case.hq, case.d))
                     for i, s in enumerate(case.seqs)]
@@ -270,3 +297,7 @@ def test_full_size_global_workload_invariance():
         for a, b_, what in zip(full, sg, ("dq", "dk", "dv")):
             assert np.array_equal(a[cu[i]:cu[i + 1]].view(np.uint32),
                                   b_.cpu().numpy().view(np.uint32)), f"seq {i} {what}"
+    lengths = [s.length for s in case.seqs]
+    for i in (int(np.argmin(lengths)), int(np.argmax(lengths))):
+        sampled_parity(full, cu, case, i, 78, n_dq=32, n_kv=24,
+                       kv_from=lengths[i] - 256, kv_heads=(1, 3))

@@ -39,6 +39,8 @@ MUTANTS = [
     ("bf16 element index off", "((const uint16_t*)base)[idx])", "((const uint16_t*)base)[idx ^ 1])"),
     ("fp32 element index off", "((const float*)base)[idx];", "((const float*)base)[idx ^ 1];"),
     ("fp32 read as bf16", "if (dtype == ORACLE_F32)", "if (dtype == -5)"),
+    ("backward units: statistics of one head per group",
+     "h < (g + 1) * group; ++h)\n                    need[", "h < g * group + 1; ++h)\n                    need["),
     ("backward: ds sign", "double ds = p * (dp - del);", "double ds = p * (del - dp);"),
     ("backward: dk misses scale", "dkj[c] += scale * ds *", "dkj[c] += ds *"),
     ("backward: dv uses ds", "dvj[c] += p * load_elem(dout", "dvj[c] += ds * load_elem(dout"),
