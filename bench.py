@@ -379,6 +379,21 @@ def main():
                          "ms_min": float(np.min(t)), "bytes": nbytes,
                          "context_tokens": int(sum(dlen[:B]))}
         log(f"decode B={B}: {ms * 1e3:.1f} us ({gbs:.0f} GB/s)")
+    # K = V (one cache holds both): each block is loaded once
+    alias = {}
+    for B in () if args.step_only else (8, 64):
+        def decode_alias():
+            ia.attn_decode_paged(dc["q"][:B], dc["k_cache"], dc["k_cache"], d_bt[:B], d_sl[:B],
+                                 int(max(dlen[:B])), softmax_scale=dc["scale"], workspace=ws,
+                                 out=d_out[:B])
+        decode_alias()
+        t = time_calls(decode_alias, args.reps, before=flush_llc)
+        ms = float(np.mean(t))
+        nbytes = decode_bytes(dlen[:B], 32, 4, 512) - sum(dlen[:B]) * 4 * 512 * 2
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        alias[str(B)] = {"GB/s": gbs, "frac": gbs / PEAK_HBM_GBS, "ms_mean": ms,
+                         "ms_min": float(np.min(t)), "bytes": nbytes}
+        log(f"decode K=V B={B}: {ms * 1e3:.1f} us ({gbs:.0f} GB/s on the K bytes)")
     # one sequence's output bytes at every batch size (batch invariance, checked live)
     outs = {}
     for B in (1, 64) if args.step_only else (1, 8, 32, 64):
@@ -449,6 +464,36 @@ def main():
                                    f"{bw_flops:.4g} FLOP = 10*256*32*{sl['pairs']} allowed pairs "
                                    "(dq, dk, dv of the sliding prefill)", bw_ms)}
         log(f"backward: {bw_ms:.3f} ms ({bw_tf:.1f} TFLOP/s)")
+        del dq, dk, dv, bws, dout, lse
+
+        # the global prefill's backward (head dim 512)
+        lse = torch.empty(gl["q"].shape[:2], dtype=torch.float32, device=dev)
+        ia.attn_prefill_varlen(gl["q"], gl["k"], gl["v"], gl["cu_seqlens"], gl["max_seqlen"],
+                               softmax_scale=gl["scale"], out=gl["out"], lse=lse)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(3)
+        dout = (torch.randn(gl["q"].shape, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+        dq = torch.empty(gl["q"].shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(gl["k"].shape, dtype=torch.float32, device=dev)
+        dv = torch.empty(gl["k"].shape, dtype=torch.float32, device=dev)
+        bws = torch.empty(gl["q"].shape[:2], dtype=torch.float32, device=dev)
+
+        def backward_global():
+            ia.attn_prefill_varlen_backward(gl["q"], gl["k"], gl["v"], gl["out"], lse, dout,
+                                            gl["cu_seqlens"], gl["max_seqlen"],
+                                            softmax_scale=gl["scale"], dq=dq, dk=dk, dv=dv,
+                                            workspace=bws)
+
+        backward_global()
+        t = time_calls(backward_global, args.backward_steps)
+        ms = float(np.mean(t))
+        fl = 2.5 * gl["flops"]
+        tf = fl / (ms * 1e-3) / 1e12
+        bw["global"] = {"value": tf, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                        "ms_mean": ms, "calls": args.backward_steps,
+                        "kernel": "bwd_dq_kernel<512> + bwd_dkv_kernel<512>",
+                        "work": f"{fl:.4g} FLOP = 10*512*32*{gl['pairs']} allowed pairs"}
+        log(f"backward (global, head dim 512): {ms:.3f} ms ({tf:.1f} TFLOP/s)")
         del dq, dk, dv, bws, dout, lse
 
     # ---------------- CPU oracle baselines + parity spot-checks on sampled rows
@@ -562,7 +607,8 @@ def main():
                    "context_tokens": int(sum(dlen)),
                    "batch_sweep_llc_flushed": sweep,
                    "seq0_bytes_equal_at_every_batch": bool(invariant),
-                   "strict_prefill_bytes": strict},
+                   "strict_prefill_bytes": strict,
+                   "k_eq_v_llc_flushed": alias},
         **reported,
         "backward": bw,
         "cpu_baseline": cpu,
