@@ -496,6 +496,22 @@ def main():
         log(f"backward (global, head dim 512): {ms:.3f} ms ({tf:.1f} TFLOP/s)")
         del dq, dk, dv, bws, dout, lse
 
+    # ---------------- a measured ceiling beside the published peak: a large
+    # bf16 GEMM through the vendor library (torch.matmul)
+    ceilings = None
+    if not args.step_only:
+        n = 8192
+        ga = torch.randn((n, n), device=dev).to(torch.bfloat16)
+        gb = torch.randn((n, n), device=dev).to(torch.bfloat16)
+        gc = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+        torch.matmul(ga, gb, out=gc)
+        t = time_calls(lambda: torch.matmul(ga, gb, out=gc), args.reps)
+        gemm_tf = 2.0 * n ** 3 / (float(np.median(t)) * 1e-3) / 1e12
+        del ga, gb, gc
+        ceilings = {"gemm_bf16_tflops": gemm_tf, "gemm": f"torch.matmul bf16 {n}x{n}x{n}, median",
+                    "prefill_frac_of_gemm": hy_tflops / gemm_tf}
+        log(f"ceiling: bf16 GEMM {gemm_tf:.0f} TFLOP/s")
+
     # ---------------- CPU oracle baselines + parity spot-checks on sampled rows
     cpu = None
     parity = None
@@ -611,6 +627,7 @@ def main():
                    "k_eq_v_llc_flushed": alias},
         **reported,
         "backward": bw,
+        "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
         "parity_sample": parity,
         "kernel_sources": kernel_sources_hash(),
