@@ -93,11 +93,11 @@ __device__ __forceinline__ float masked_exp2(bool ok, float arg) {
 // one workgroup fills a CU, consecutive tiles spread over the XCDs balance
 // better (46.1 against 49.3 ms on the global workload).
 template <int D>
-__device__ __forceinline__ long long bwd_item() {
+__device__ __forceinline__ long long bwd_item(int tiles) {
   if constexpr (D == 512)
     return blockIdx.x;
   else
-    return xcd_logical_block(blockIdx.x);
+    return xcd_logical_block(blockIdx.x, tiles);
 }
 
 __device__ __forceinline__ void st_lds_x8(bf16* p, bf16x8 x) {
@@ -168,7 +168,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // XCD-aware so that neighbouring row tiles (which share most of their
   // keys) share an L2; row tiles run from the end of the sequence (longest
   // causal rows first).
-  const long long item = bwd_item<D>();
+  const long long item = bwd_item<D>(tiles);
   if (item >= (long long)tiles * hq * nseq) return;
   const int b = (int)(item / ((long long)tiles * hq));
   const int h = (int)((item / tiles) % hq), kvh = h / (hq / hkv);
@@ -326,7 +326,7 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Logical item = (key tile, KV head, sequence), tile fastest, placed
   // XCD-aware (neighbouring key tiles share most of their rows); key tiles
   // run from the start of the sequence (the most rows first).
-  const long long item = bwd_item<D>();
+  const long long item = bwd_item<D>(tiles);
   if (item >= (long long)tiles * hkv * nseq) return;
   const int b = (int)(item / ((long long)tiles * hkv));
   const int kvh = (int)((item / tiles) % hkv), G = hq / hkv;
@@ -553,7 +553,7 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Logical item = (key tile, KV head, sequence), tile fastest, placed
   // XCD-aware (neighbouring key tiles share most of their rows); key tiles
   // run from the start of the sequence (the most rows first).
-  const long long item = bwd_item<D>();
+  const long long item = bwd_item<D>(tiles);
   if (item >= (long long)tiles * hkv * nseq) return;
   const int b = (int)(item / ((long long)tiles * hkv));
   const int kvh = (int)((item / tiles) % hkv), G = hq / hkv;

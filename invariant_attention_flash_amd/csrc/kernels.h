@@ -73,11 +73,18 @@ struct PrefillSchedule {
 // Prefill block order.  The hardware hands consecutive workgroups to the 8
 // XCDs in turn (each XCD has its own L2); workgroups that read the same K/V
 // rows (consecutive position tiles of one sequence and KV head) should share
-// an L2.  Block i therefore takes logical work item
-//   chunk (i/8)/kXcdChunk * 8 + i%8, item (i/8) % kXcdChunk of that chunk,
-// so each XCD walks runs of kXcdChunk consecutive tiles.  The grid is padded
-// to a multiple of 8*kXcdChunk; items past the end exit at once.  Only the
-// placement changes: a row's arithmetic never depends on its block.
+// an L2.  So the logical items are cut into runs of kXcdChunk consecutive
+// tiles, and the c-th run an XCD walks is run 8c + (x + r) % 8 for XCD x,
+// with block i: x = i % 8, c = (i/8) / kXcdChunk, item (i/8) % kXcdChunk of
+// the run.  r is the index of the (sequence, KV head) that the run group c
+// starts in (tiles items each).  Without the rotation by r, a (sequence, KV
+// head) of exactly 8 runs would give XCD x the same position range of every
+// sequence, and since the first tiles of a sliding or causal sequence are the
+// cheapest, the XCDs would finish far apart; rotating by the group index
+// alone spreads those runs too, but changes which runs of a long sequence
+// share an XCD.  The grid is padded to a multiple of 8*kXcdChunk; items past
+// the end exit at once.  Only the placement changes: a row's arithmetic never
+// depends on its block.
 constexpr int kXcds = 8;
 constexpr int kXcdChunk = 8;
 
@@ -86,9 +93,10 @@ __host__ __device__ inline long long xcd_padded_blocks(long long n) {
   return (n + q - 1) / q * q;
 }
 
-__device__ inline long long xcd_logical_block(long long i) {
-  const long long x = i % kXcds, j = i / kXcds;
-  return ((j / kXcdChunk) * kXcds + x) * kXcdChunk + j % kXcdChunk;
+__device__ inline long long xcd_logical_block(long long i, int tiles) {
+  const long long x = i % kXcds, j = i / kXcds, c = j / kXcdChunk;
+  const long long r = (c * kXcds * kXcdChunk) / (tiles > 0 ? tiles : 1);
+  return (c * kXcds + (x + r) % kXcds) * kXcdChunk + j % kXcdChunk;
 }
 
 bool prefill_schedule(int d, int group, PrefillSchedule* s);

@@ -210,7 +210,7 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // Logical item = (tile, KV head, sequence), tile fastest; tiles run from
   // the end of the sequence (longest causal rows first).
-  const long long item = xcd_logical_block(blockIdx.x);
+  const long long item = xcd_logical_block(blockIdx.x, tiles);
   if (item >= (long long)tiles * hkv * nseq) return;
   const int g = (int)((item / tiles) % hkv);
   const int b = (int)(item / ((long long)tiles * hkv));

@@ -220,7 +220,7 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // the end of the sequence (longest causal rows first).  Tile t covers
   // positions [t*P, (t+1)*P), counted from the first tile holding a query
   // row of the sequence.
-  const long long item = xcd_logical_block(blockIdx.x);
+  const long long item = xcd_logical_block(blockIdx.x, tiles);
   if (item >= (long long)tiles * hkv * nseq) return;
   const int g = (int)((item / tiles) % hkv);
   const int b = (int)(item / ((long long)tiles * hkv));
