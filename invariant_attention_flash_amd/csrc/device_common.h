@@ -133,6 +133,20 @@ __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// x / l rounded as the IEEE fp32 division rounds it, given y = RN(1/l):
+// q0 = RN(x*y) is within one ulp of x/l, the residual x - q0*l is exact as
+// an FMA, and RN(q0 + residual*y) is then the correctly rounded quotient
+// (Markstein's correction step with a correctly rounded reciprocal).  This
+// holds while nothing underflows: for l in [1, 2^40) and a quotient of
+// magnitude at least kRecipDivMin.  Callers check the result against that
+// bound and divide directly when it fails (or is NaN).
+constexpr float kRecipDivMin = 0x1p-100f;
+__device__ __forceinline__ float div_by_recip(float x, float l, float y) {
+  const float q0 = x * y;
+  const float r = __builtin_fmaf(-q0, l, x);
+  return __builtin_fmaf(r, y, q0);
+}
+
 // Find the span holding packed token `tok` in a sorted, disjoint list of
 // [start, end) pairs.  Returns true and the bounds if found.
 __device__ __forceinline__ bool find_span(const int32_t* __restrict__ spans, int n, int tok,

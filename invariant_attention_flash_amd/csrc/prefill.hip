@@ -388,16 +388,34 @@ void prefill_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     pv_last<C, true>(kvs[0] + C::kTile, ln.vrow, ln.vc16, pa, oacc);
   }
 
-  // Epilogue: o = acc / l (IEEE fp32 division), bf16 RNE, store.
+  // Epilogue: o = acc / l (the IEEE fp32 quotient, formed as in the other
+  // prefill kernel: reciprocal and one correction, dividing where a live
+  // quotient is below kRecipDivMin, zero or NaN), bf16 RNE, store.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
+    const float y = 1.0f / l[rb];
+    float qv[C::kDb][4];
+    bool small = false;
+#pragma unroll
+    for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qv[db][i] = div_by_recip(oacc[rb][db][i], l[rb], y);
+        small |= !(__builtin_fabsf(qv[db][i]) >= kRecipDivMin);
+      }
+    if (__builtin_amdgcn_ballot_w64(qpos[rb] >= 0 && small) != 0) {
+#pragma unroll
+      for (int db = 0; db < C::kDb; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[db][i] = oacc[rb][db][i] / l[rb];
+    }
     if (qpos[rb] < 0) continue;
     bf16* orow = o + ((size_t)(seq0 + qpos[rb]) * hq + qhead[rb]) * D + 4 * ln.gq;
 #pragma unroll
     for (int db = 0; db < C::kDb; ++db) {
       bf16x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = to_bf16(oacc[rb][db][i] / l[rb]);
+      for (int i = 0; i < 4; ++i) w[i] = to_bf16(qv[db][i]);
       *reinterpret_cast<bf16x4*>(orow + 16 * db) = w;
     }
     if (lse != nullptr && ln.gq == 0)

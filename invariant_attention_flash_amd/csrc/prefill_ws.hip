@@ -537,24 +537,46 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                        lane, ln.vrow, vc16w, oacc);
   }
 
-  // Epilogue: o = acc / l (IEEE fp32 division), bf16 RNE, store this wave's
-  // columns of every row.
+  // Epilogue: o = acc / l (the IEEE fp32 quotient), bf16 RNE, store this
+  // wave's columns of every row.  The quotients come from the row's
+  // correctly rounded reciprocal and one correction each (div_by_recip): the
+  // same bits as dividing, at a quarter of the instructions.  A row block in
+  // which some live row's quotient is below kRecipDivMin, zero or NaN divides
+  // instead.
 #pragma unroll
   for (int r = 0; r < kRB; ++r) {
     const int row = 16 * r + ln.x;
     const int pos = p0 + row / G;
-    if (pos < sg.qlo || pos >= sg.qhi) continue;
+    const bool live = pos >= sg.qlo && pos < sg.qhi;
     const float lr = lrow[row];
-    bf16* orow = o + ((size_t)(seq0 + pos) * hq + g * G + row % G) * D + 16 * C::kDbW * widx +
-                 4 * ln.gq;
+    const float y = 1.0f / lr;
+    float qv[C::kDbW][4];
+    bool small = false;
 #pragma unroll
-    for (int db = 0; db < C::kDbW; ++db) {
-      bf16x4 w;
+    for (int db = 0; db < C::kDbW; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = to_bf16(oacc[r][db][i] / lr);
-      *reinterpret_cast<bf16x4*>(orow + 16 * db) = w;
+      for (int i = 0; i < 4; ++i) {
+        qv[db][i] = div_by_recip(oacc[r][db][i], lr, y);
+        small |= !(__builtin_fabsf(qv[db][i]) >= kRecipDivMin);
+      }
+    if (__builtin_amdgcn_ballot_w64(live && small) != 0) {
+#pragma unroll
+      for (int db = 0; db < C::kDbW; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[db][i] = oacc[r][db][i] / lr;
     }
-    __builtin_amdgcn_sched_barrier(0);  // one row block's divisions at a time
+    if (live) {
+      bf16* orow = o + ((size_t)(seq0 + pos) * hq + g * G + row % G) * D +
+                   16 * C::kDbW * widx + 4 * ln.gq;
+#pragma unroll
+      for (int db = 0; db < C::kDbW; ++db) {
+        bf16x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = to_bf16(qv[db][i]);
+        *reinterpret_cast<bf16x4*>(orow + 16 * db) = w;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one row block at a time
   }
 }
 
