@@ -474,16 +474,17 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // waves wait for K(kt+1) (for the score waves) and V(kt-1) (for PV(kt-1)),
   // the loads of step kt+1-NR, so the NR-2 newer steps' loads may stay in
   // flight.  Prologue: the loads of the steps before kt0 -- K(kt0) ..
-  // K(kt0+NR-1) when this wave loads K, then V(kt0) .. V(kt0+NR-3); K(kt0)
-  // must land before the first barrier.
+  // K(kt0+NR-1) when this wave loads K, and V(kt0) .. V(kt0+NR-3), issued in
+  // the order those steps would have issued them (step kt0-NR+i: K(kt0+i),
+  // then V(kt0+i-2)), so that from the first step on the loads a step waits
+  // for are the oldest in flight; K(kt0) must land before the first barrier.
   constexpr bool kLoadK = C::kPvLoadsK;
   constexpr int kStepLoads = (kLoadK ? 2 : 1) * C::kLoads;
-  if constexpr (kLoadK) {
 #pragma unroll
-    for (int i = 0; i < NR; ++i) load_tile(i, kt0 + i, 1);
+  for (int i = 0; i < NR; ++i) {
+    if constexpr (kLoadK) load_tile(i, kt0 + i, 1);
+    if (i >= 2) load_tile(i - 2, kt0 + i - 2, 2);
   }
-#pragma unroll
-  for (int i = 0; i + 2 < NR; ++i) load_tile(i, kt0 + i, 2);
   if constexpr (kLoadK) wait_vmcnt<(2 * NR - 3) * C::kLoads>();
   lds_barrier();
 
