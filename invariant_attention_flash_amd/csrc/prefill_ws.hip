@@ -81,6 +81,13 @@ struct PfWsCfg {
   // score waves (each kind carries 32 MFMAs per step, and the PV waves' own V
   // loads already fill their issue slots).
   static constexpr bool kPvLoadsK = D <= 256;
+  // When a step's tile loads are issued.  Head dim 512 (rings of two 64 KB
+  // stages): all at the start of the step, since the next step waits for
+  // them (7 % shorter steps on the global prefill).  Head dim 256 (three
+  // stages): spread over the MFMA groups, which keeps the issue slots of the
+  // step's first groups for the MFMAs (4 % shorter steps than issuing them
+  // together).
+  static constexpr bool kLoadsFirst = D >= 512;
   static_assert(D % 64 == 0 && kRowsPerWave % G == 0, "row map");
   static_assert(kLoads >= 1 && BN * kChunks % (64 * kRoleWaves) == 0, "tile load split");
   static_assert(BN == 16 || BN == 32, "tiles of 16 or 32 keys");
@@ -95,7 +102,8 @@ struct PfWsCfg {
 // Score wave, one step: S^T(t+1) = K Q^T for its RB row blocks on the K tile
 // `kt`, in kHalves*kSt groups (one K operand each), with stage i of the previous
 // tile's softmax (sm) after group i's MFMAs and, when DMA (the score waves
-// load K), the K(t+NR) loads spread over the groups.  The MFMAs are compiler
+// load K), the K(t+NR) loads (before the first group, or spread over the
+// groups; kLoadsFirst).  The MFMAs are compiler
 // builtins with VGPR accumulators (the kernel uses no AGPRs), so the
 // compiler tracks their result latency and schedules the softmax's vector
 // work around them freely.
@@ -123,9 +131,16 @@ __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_
     const bf16x8 a = kop[i % kAhead];
     if (i + kAhead < kN) kop[i % kAhead] = kread(i + kAhead);
     if constexpr (DMA) {
-      if (i % kEvery == 0)
+      if constexpr (C::kLoadsFirst) {
+        if (i == 0) {
+#pragma unroll
+          for (int j = 0; j < C::kLoads; ++j)
+            dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kpre, krs, kk0, j, rs_bytes, widx, lane);
+        }
+      } else if (i % kEvery == 0) {
         dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kpre, krs, kk0, i / kEvery, rs_bytes, widx,
                                                     lane);
+      }
     }
 #pragma unroll
     for (int rb = 0; rb < C::RB; ++rb) {
@@ -138,7 +153,7 @@ __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_
 // PV wave, one step: O^T += V^T P^T for its kDbW output blocks of every row
 // block, V from the tile `vt`, P^T from the exchange buffer `pt`, with the
 // step's tile loads (K first when this wave loads K, then V; kLoads of each
-// per lane) spread over the MFMA groups.
+// per lane) before the first group or spread over the groups (kLoadsFirst).
 //   V operand (output block db): rows 4*gq + x/4 (and +16 for 32-key tiles),
 //     logical chunk 2*(kDbW*p + db) + (x%4)/2, physical chunk ^ ((2*row) &
 //     kSwV), element 4*(x%2);
@@ -175,10 +190,11 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
   for (int r = 0; r < kN; ++r) {
     if (r + 1 < kN) pop[(r + 1) & 1] = pt[64 * (r + 1) + lane];
     if constexpr (DMA) {
-      if (r % kEvery == 0) {
+      constexpr bool kFirst = C::kLoadsFirst;
+      if (kFirst ? r == 0 : r % kEvery == 0) {
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          const int j = (r / kEvery) * kPer + u;
+        for (int u = 0; u < (kFirst ? kL : kPer); ++u) {
+          const int j = kFirst ? u : (r / kEvery) * kPer + u;
           if (j < kKL)
             dma_rows<C::kChunks, C::kLoads, 0, C::kSwK>(kpre, krs, kk0, j, rs_bytes, widx, lane);
           else
