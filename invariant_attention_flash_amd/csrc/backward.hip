@@ -89,15 +89,13 @@ __device__ __forceinline__ float masked_exp2(bool ok, float arg) {
 }
 
 // Logical work item of this workgroup: XCD-aware placement (runs of
-// consecutive tiles share an XCD's L2) at head dims up to 256; at 512, where
-// one workgroup fills a CU, consecutive tiles spread over the XCDs balance
-// better (46.1 against 49.3 ms on the global workload).
+// consecutive tiles share an XCD's L2, the runs rotated over the XCDs per
+// sequence and head).  At head dim 512 the unrotated runs had left the XCDs
+// unevenly loaded (slower than no runs at all); rotated, the global
+// workload's backward takes 36.9 ms against 45.7 with blocks in plain order.
 template <int D>
 __device__ __forceinline__ long long bwd_item(int tiles) {
-  if constexpr (D == 512)
-    return blockIdx.x;
-  else
-    return xcd_logical_block(blockIdx.x, tiles);
+  return xcd_logical_block(blockIdx.x, tiles);
 }
 
 __device__ __forceinline__ void st_lds_x8(bf16* p, bf16x8 x) {
