@@ -34,6 +34,7 @@
 // same key order with transpose reads.
 #include "device_common.h"
 #include "kernels.h"
+#include "prefill_common.h"
 
 namespace invattn {
 
@@ -54,8 +55,9 @@ struct BwdCfg {
   // dk/dv: 32-pair halves per step (two independent halves where the LDS
   // budget allows); each half is one MFMA group of the fixed pair order.
   static constexpr int kHalves = D <= 256 ? 2 : 1;
-  // dk/dv: next pair tile's loads held in registers during the current one
-  // (at head dim 512 the accumulators leave no room: staged after the step).
+  // dk/dv: next pair tile's loads held in registers during the current one.
+  // At head dim 512 the accumulators leave no room for that: the next tile
+  // goes straight to LDS with direct loads instead (bwd_dkv_kernel, dma_row).
   static constexpr bool kPrefetch = D <= 256;
   static constexpr int kPairs = kBwdTile * kHalves;
   static_assert(D % 32 == 0, "head dim in MFMA k-steps");
@@ -100,6 +102,23 @@ __device__ __forceinline__ long long bwd_item(int tiles) {
 
 __device__ __forceinline__ void st_lds_x8(bf16* p, bf16x8 x) {
   *reinterpret_cast<bf16x8*>(p) = x;
+}
+
+// Direct HBM -> LDS load of one 1 KB row (head dim 512, bf16): lane i's 16
+// bytes, from byte voff + 16*i of the resource `rs`, land at LDS byte
+// address lds + 16*i; out-of-range bytes load as zeros.  Issued from inline
+// assembly (see dma_rows): the kernel waits for it explicitly before the
+// barrier that publishes the tile, and leaves M0 to these loads.
+__device__ __forceinline__ void dma_row(uint32_t lds, const u32x4& rs, uint32_t voff, int lane) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  const uint32_t vo = voff + 16u * (uint32_t)lane;
+  __asm__ volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(vo), "s"(rs)
+      : "memory");
 }
 
 // A operand of the gradient products: X^T for 16 columns [c0, c0 + 16) of
@@ -370,17 +389,41 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   // (row, head) pairs in order: rows ascending, the group's heads ascending.
   const int n_pairs = (hi - lo) * G;
-  TileRegs<D, NP> qr, dr;
+  constexpr bool kDma = !C::kPrefetch;
+  TileRegs<D, kDma ? kBwdTile : NP> qr, dr;  // unused with direct loads
   int mrow = -1, mss = 0, mse = 0;
   float ml2 = 0.f, mdl = 0.f;
+  // Direct loads (head dim 512): the Q and dout rows of rows [lo, hi) of
+  // this sequence, so that the pairs past the last one load as zeros.
+  u32x4 qrs{}, drs{};
+  if constexpr (kDma) {
+    static_assert(D * 2 == 1024 && NP % 4 == 0, "one 1 KB row per direct load");
+    const size_t base = ((size_t)(seq0 + lo) * hq + kvh * G) * D;
+    const int nb = (hi - lo) * hq * D * 2;
+    qrs = buffer_rsrc(q + base, nb);
+    drs = buffer_rsrc(dout + base, nb);
+  }
+  // Pair rows 8w .. 8w + 7 of tile w0 (this wave's share) into buffer `buf`.
+  auto dma_tile = [&](int w0, int buf) {
+#pragma unroll
+    for (int i = 0; i < NP / 4; ++i) {
+      const int r = (NP / 4) * w + i;
+      const int pw = w0 + r;
+      const uint32_t off = (uint32_t)(((pw / G) * hq + pw % G) * D * 2);
+      dma_row(lds_addr(qts[buf] + r * C::kLd), qrs, off, lane);
+      dma_row(lds_addr(dts[buf] + r * C::kLd), drs, off, lane);
+    }
+  };
   auto fetch = [&](int w0) {
     auto pair_src = [&](const bf16* base, int r) -> const bf16* {
       const int pw = w0 + r;
       if (pw >= n_pairs) return nullptr;
       return base + ((size_t)(seq0 + lo + pw / G) * hq + kvh * G + pw % G) * D;
     };
-    qr.fetch([&](int r) { return pair_src(q, r); }, tid);
-    dr.fetch([&](int r) { return pair_src(dout, r); }, tid);
+    if constexpr (!kDma) {
+      qr.fetch([&](int r) { return pair_src(q, r); }, tid);
+      dr.fetch([&](int r) { return pair_src(dout, r); }, tid);
+    }
     if (tid < NP) {
       const int pw = w0 + tid;
       mrow = -1;
@@ -399,8 +442,10 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   };
   auto put = [&](int buf) {
-    qr.put(qts[buf], tid);
-    dr.put(dts[buf], tid);
+    if constexpr (!kDma) {
+      qr.put(qts[buf], tid);
+      dr.put(dts[buf], tid);
+    }
     if (tid < NP) {
       prows[buf][tid] = mrow;
       psss[buf][tid] = mss;
@@ -409,21 +454,20 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       pdels[buf][tid] = mdl;
     }
   };
-  // Pair tile t sits in buffer t & 1; with prefetch, tile t+1's loads fly
-  // while tile t is used.
-  if (C::kPrefetch && n_pairs > 0) {
+  // Pair tile t sits in buffer t & 1; tile t+1's loads fly while tile t is
+  // used (in registers with prefetch; straight to LDS with direct loads).
+  if (n_pairs > 0) {
+    if constexpr (kDma) dma_tile(0, 0);
     fetch(0);
     put(0);
   }
+  if constexpr (kDma) wait_vmem();
   __syncthreads();
   for (int w0 = 0, t = 0; w0 < n_pairs; w0 += NP, ++t) {
     const bool more = w0 + NP < n_pairs;
-    if constexpr (C::kPrefetch) {
-      if (more) fetch(w0 + NP);
-    } else {
-      fetch(w0);
-      put(t & 1);
-      __syncthreads();
+    if (more) {
+      if constexpr (kDma) dma_tile(w0 + NP, (t & 1) ^ 1);
+      fetch(w0 + NP);
     }
     const int cb = t & 1;
     const bf16* qt = qts[cb];
@@ -493,9 +537,8 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         }
       }
     }
-    if constexpr (C::kPrefetch) {
-      if (more) put(cb ^ 1);
-    }
+    if (more) put(cb ^ 1);
+    if constexpr (kDma) wait_vmem();
     __syncthreads();
   }
 #pragma unroll

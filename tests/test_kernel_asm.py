@@ -40,7 +40,7 @@ def _compile_asm(src, tmp_path):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("name", ["prefill.hip", "prefill_ws.hip", "decode.hip"])
+@pytest.mark.parametrize("name", ["prefill.hip", "prefill_ws.hip", "decode.hip", "backward.hip"])
 def test_m0_only_in_direct_loads(name, tmp_path):
     assert name in ia_build.SOURCES
     text = _compile_asm(os.path.join(CSRC, name), tmp_path)
