@@ -244,7 +244,19 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int rb = 0; rb < 4; ++rb) acc[db][rb] = f32x4{};
   }
 
-  TileRegs<D> kr, vr;
+  // Tile loads: through registers, or at head dim 512 (where the
+  // accumulators and operands fill the registers) straight to LDS with
+  // direct loads of one 1 KB key row each, from a resource that ends at key
+  // hi (keys past it load as zeros).
+  constexpr bool kDma = D * 2 == 1024;
+  TileRegs<D> kr, vr;  // unused with direct loads
+  u32x4 krs{}, vrs{};
+  if constexpr (kDma) {
+    const size_t base = ((size_t)seq0 * hkv + kvh) * D;
+    const int nb = hi * hkv * D * 2;
+    krs = buffer_rsrc(k + base, nb);
+    vrs = buffer_rsrc(v + base, nb);
+  }
   auto fetch = [&](int k0) {
     kr.fetch([&](int r) -> const bf16* {
       return k0 + r < hi ? k + ((size_t)(seq0 + k0 + r) * hkv + kvh) * D : nullptr;
@@ -253,15 +265,33 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       return k0 + r < hi ? v + ((size_t)(seq0 + k0 + r) * hkv + kvh) * D : nullptr;
     }, tid);
   };
+  // Key rows 8w .. 8w + 7 of the tile at k0 (this wave's share) into `buf`.
+  auto dma_tile = [&](int k0, int buf) {
+#pragma unroll
+    for (int r8 = 0; r8 < kBwdTile / 4; ++r8) {
+      const int r = (kBwdTile / 4) * w + r8;
+      const uint32_t off = (uint32_t)((k0 + r) * hkv * D * 2);
+      dma_row(lds_addr(kts[buf] + r * C::kLd), krs, off, lane);
+      dma_row(lds_addr(vts[buf] + r * C::kLd), vrs, off, lane);
+    }
+  };
   // Tile t sits in buffer t & 1; tile t+1's loads fly while tile t is used,
   // one barrier per tile.
-  fetch(lo);
-  kr.put(kts[0], tid);
-  vr.put(vts[0], tid);
+  if constexpr (kDma) {
+    dma_tile(lo, 0);
+    wait_vmem();
+  } else {
+    fetch(lo);
+    kr.put(kts[0], tid);
+    vr.put(vts[0], tid);
+  }
   __syncthreads();
   for (int k0 = lo, t = 0; k0 < hi; k0 += kBwdTile, ++t) {
     const bool more = k0 + kBwdTile < hi;
-    if (more) fetch(k0 + kBwdTile);
+    if (more) {
+      if constexpr (kDma) dma_tile(k0 + kBwdTile, (t + 1) & 1);
+      else fetch(k0 + kBwdTile);
+    }
     const bf16* kt = kts[t & 1];
     const bf16* vt = vts[t & 1];
     // S^T and dP^T: keys 16kb + 4g + e of row x.
@@ -299,7 +329,9 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) acc[db][rb] = mfma16(ak, xch[rb][lane], acc[db][rb]);
     }
-    if (more) {
+    if constexpr (kDma) {
+      wait_vmem();
+    } else if (more) {
       kr.put(kts[(t + 1) & 1], tid);
       vr.put(vts[(t + 1) & 1], tid);
     }
