@@ -90,14 +90,19 @@ __device__ __forceinline__ float masked_exp2(bool ok, float arg) {
   }
 }
 
-// Logical work item of this workgroup: XCD-aware placement (runs of
-// consecutive tiles share an XCD's L2, the runs rotated over the XCDs per
-// sequence and head).  At head dim 512 the unrotated runs had left the XCDs
-// unevenly loaded (slower than no runs at all); rotated, the global
-// workload's backward takes 36.9 ms against 45.7 with blocks in plain order.
-template <int D>
-__device__ __forceinline__ long long bwd_item(int tiles) {
-  return xcd_logical_block(blockIdx.x, tiles);
+// Work item of this workgroup: tile `tile` (numbered most work first) of
+// group `group` = sequence * heads + head, in run-major order (kernels.h):
+// runs of consecutive tiles of one group share an XCD's L2, and the longest
+// tiles of every group start first on every XCD.  At head dim 512 that order
+// took the global workload's backward from 26.6 to 24.6 ms (blocks in group
+// order had left the longest sequence's tiles for last).
+__device__ __forceinline__ bool bwd_item(int tiles, int heads, int nseq, int& tile, int& b,
+                                         int& h) {
+  long long grp;
+  if (!run_major_item(blockIdx.x, tiles, (long long)heads * nseq, tile, grp)) return false;
+  b = (int)(grp / heads);
+  h = (int)(grp % heads);
+  return true;
 }
 
 __device__ __forceinline__ void st_lds_x8(bf16* p, bf16x8 x) {
@@ -181,16 +186,14 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) bf16 kts[2][kBwdTile * C::kLd];
   __shared__ __attribute__((aligned(16))) bf16 vts[2][kBwdTile * C::kLd];
   __shared__ bf16x8 xch[4][64];   // dS of every wave's row block as B operands
-  // Logical item = (row tile, query head, sequence), tile fastest, placed
-  // XCD-aware so that neighbouring row tiles (which share most of their
-  // keys) share an L2; row tiles run from the end of the sequence (longest
-  // causal rows first).
-  const long long item = bwd_item<D>(tiles);
-  if (item >= (long long)tiles * hq * nseq) return;
-  const int b = (int)(item / ((long long)tiles * hq));
-  const int h = (int)((item / tiles) % hq), kvh = h / (hq / hkv);
+  // Item = (row tile, query head, sequence), row tiles numbered from the end
+  // of the sequence (longest causal rows first); neighbouring row tiles share
+  // most of their keys.
+  int tile, b, h;
+  if (!bwd_item(tiles, hq, nseq, tile, b, h)) return;
+  const int kvh = h / (hq / hkv);
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
-  const int r0 = (tiles - 1 - (int)(item % tiles)) * kBwdRows;
+  const int r0 = (tiles - 1 - tile) * kBwdRows;
   if (r0 >= L) return;
   const int r1 = min(r0 + kBwdRows, L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -372,15 +375,14 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) int prows[2][NP], psss[2][NP], pses[2][NP];
   // P and dS of every wave's key block as B operands (bf16x8 per lane).
   __shared__ bf16x8 xch[2][C::kHalves][4][64];
-  // Logical item = (key tile, KV head, sequence), tile fastest, placed
-  // XCD-aware (neighbouring key tiles share most of their rows); key tiles
-  // run from the start of the sequence (the most rows first).
-  const long long item = bwd_item<D>(tiles);
-  if (item >= (long long)tiles * hkv * nseq) return;
-  const int b = (int)(item / ((long long)tiles * hkv));
-  const int kvh = (int)((item / tiles) % hkv), G = hq / hkv;
+  // Item = (key tile, KV head, sequence), key tiles numbered from the start
+  // of the sequence (the most rows first); neighbouring key tiles share most
+  // of their rows.
+  int tile, b, kvh;
+  if (!bwd_item(tiles, hkv, nseq, tile, b, kvh)) return;
+  const int G = hq / hkv;
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
-  const int j0 = (int)(item % tiles) * kBwdRows;
+  const int j0 = tile * kBwdRows;
   if (j0 >= L) return;
   const int j1 = min(j0 + kBwdRows, L);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -435,17 +437,43 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     qrs = buffer_rsrc(q + base, nb);
     drs = buffer_rsrc(dout + base, nb);
   }
-  // Pair rows 8w .. 8w + 7 of tile w0 (this wave's share) into buffer `buf`.
-  auto dma_tile = [&](int w0, int buf) {
-#pragma unroll
-    for (int i = 0; i < NP / 4; ++i) {
-      const int r = (NP / 4) * w + i;
-      const int pw = w0 + r;
-      const uint32_t off = (uint32_t)(((pw / G) * hq + pw % G) * D * 2);
-      dma_row(lds_addr(qts[buf] + r * C::kLd), qrs, off, lane);
-      dma_row(lds_addr(dts[buf] + r * C::kLd), drs, off, lane);
+  // Pair p = (row - lo) * G + head.  Tiles are visited in order, NP pairs
+  // each, so a fixed slot's (row - lo, head) advances by (NP / G, NP % G) per
+  // tile, with a carry: the loop needs no division.
+  const int adv_q = NP / G, adv_m = NP % G;
+  auto advance = [&](int& pq, int& pm) {
+    pq += adv_q;
+    pm += adv_m;
+    if (pm >= G) {
+      pm -= G;
+      ++pq;
     }
   };
+  // Direct loads: this wave's slots are pair rows 8w .. 8w + 7 of a tile.
+  constexpr int kSlots = NP / 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int sq[kSlots], sm[kSlots];
+#pragma unroll
+  for (int i = 0; i < kSlots; ++i) {
+    sq[i] = (kSlots * wu + i) / G;
+    sm[i] = (kSlots * wu + i) % G;
+  }
+  // The next tile's row offsets (slot i), then its loads: row e / 2 of Q
+  // (e even) or dout (e odd) into buffer `buf`.
+  auto dma_offsets = [&](uint32_t* off) {
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+      off[i] = (uint32_t)((sq[i] * hq + sm[i]) * D * 2);
+      advance(sq[i], sm[i]);
+    }
+  };
+  auto dma_load = [&](int e, int buf, const uint32_t* off) {
+    const int r = kSlots * wu + e / 2;
+    if (e % 2 == 0) dma_row(lds_addr(qts[buf] + r * C::kLd), qrs, off[e / 2], lane);
+    else dma_row(lds_addr(dts[buf] + r * C::kLd), drs, off[e / 2], lane);
+  };
+  // Metadata lanes (tid < NP): pair w0 + tid of the next tile.
+  int lq = tid / G, lm = tid % G;
   auto fetch = [&](int w0) {
     auto pair_src = [&](const bf16* base, int r) -> const bf16* {
       const int pw = w0 + r;
@@ -457,13 +485,12 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       dr.fetch([&](int r) { return pair_src(dout, r); }, tid);
     }
     if (tid < NP) {
-      const int pw = w0 + tid;
       mrow = -1;
       mss = mse = 0;
       ml2 = mdl = 0.f;
-      if (pw < n_pairs) {
-        mrow = lo + pw / G;
-        const size_t ro = (size_t)(seq0 + mrow) * hq + kvh * G + pw % G;
+      if (lq < hi - lo) {
+        mrow = lo + lq;
+        const size_t ro = (size_t)(seq0 + mrow) * hq + kvh * G + lm;
         ml2 = lse[ro] * 1.4426950408889634f;
         mdl = delta[ro];
         if (num_spans > 0 && find_span(spans, num_spans, seq0 + mrow, s0, e0)) {
@@ -471,6 +498,7 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           mse = e0 - seq0;
         }
       }
+      advance(lq, lm);
     }
   };
   auto put = [&](int buf) {
@@ -489,17 +517,37 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Pair tile t sits in buffer t & 1; tile t+1's loads fly while tile t is
   // used (in registers with prefetch; straight to LDS with direct loads).
   if (n_pairs > 0) {
-    if constexpr (kDma) dma_tile(0, 0);
+    if constexpr (kDma) {
+      uint32_t off[kSlots];
+      dma_offsets(off);
+#pragma unroll
+      for (int e = 0; e < 2 * kSlots; ++e) dma_load(e, 0, off);
+    }
     fetch(0);
     put(0);
   }
   if constexpr (kDma) wait_vmem();
+  // K and V have arrived: the loop waits only for the tile it has in flight,
+  // at the end of each step.
+#pragma unroll
+  for (int st = 0; st < C::kSt; ++st) {
+    arrived(kop[st]);
+    arrived(vop[st]);
+  }
   __syncthreads();
   for (int w0 = 0, t = 0; w0 < n_pairs; w0 += NP, ++t) {
     const bool more = w0 + NP < n_pairs;
-    if (more) {
-      if constexpr (kDma) dma_tile(w0 + NP, (t & 1) ^ 1);
-      fetch(w0 + NP);
+    // Direct loads of the next tile: offsets here, the loads spread over this
+    // step's score MFMAs (issued at once, each waits for the memory unit to
+    // take the one before, and nothing else would run meanwhile); its
+    // metadata after the first barrier, behind them (ahead of them, a span
+    // lookup's waits would wait for them).  Without direct loads, the next
+    // tile's registers and metadata now.
+    uint32_t doff[kSlots];
+    if constexpr (kDma) {
+      if (more) dma_offsets(doff);
+    } else {
+      if (more) fetch(w0 + NP);
     }
     const int cb = t & 1;
     const bf16* qt = qts[cb];
@@ -515,16 +563,36 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int hf = 0; hf < C::kHalves; ++hf) {
       const bf16* qh = qt + 32 * hf * C::kLd;
       const bf16* dh = dt + 32 * hf * C::kLd;
-      // (Pair blocks outermost: at head dim 512 the other order spills.)
+      // MFMA k = (pair block, k-step), pair blocks outermost (at head dim
+      // 512 the other order spills); the operands of k + kAhead - 1 are read
+      // while k runs.
+      constexpr int kK = 2 * C::kSt;
+      constexpr int kAhead = kK < 4 ? kK : 4;
+      auto q_op = [&](int k) {
+        return ld_lds_x8(qh + (16 * (k / C::kSt) + x) * C::kLd + 32 * (k % C::kSt) + 8 * g);
+      };
+      auto d_op = [&](int k) {
+        return ld_lds_x8(dh + (16 * (k / C::kSt) + x) * C::kLd + 32 * (k % C::kSt) + 8 * g);
+      };
+      bf16x8 qb[kAhead], dbf[kAhead];
+#pragma unroll
+      for (int a = 0; a < kAhead; ++a) {
+        qb[a] = q_op(a);
+        dbf[a] = d_op(a);
+      }
       f32x4 s[2], dp[2];
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
-#pragma unroll
-        for (int st = 0; st < C::kSt; ++st) {
-          const bf16x8 qa = ld_lds_x8(qh + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
-          const bf16x8 da = ld_lds_x8(dh + (16 * pb + x) * C::kLd + 32 * st + 8 * g);
-          s[pb] = mfma16(qa, kop[st], st == 0 ? f32x4{} : s[pb]);
-          dp[pb] = mfma16(da, vop[st], st == 0 ? f32x4{} : dp[pb]);
+      for (int k = 0; k < kK; ++k) {
+        const int pb = k / C::kSt, st = k % C::kSt;
+        s[pb] = mfma16(qb[k % kAhead], kop[st], st == 0 ? f32x4{} : s[pb]);
+        dp[pb] = mfma16(dbf[k % kAhead], vop[st], st == 0 ? f32x4{} : dp[pb]);
+        if (k + kAhead < kK) {
+          qb[k % kAhead] = q_op(k + kAhead);
+          dbf[k % kAhead] = d_op(k + kAhead);
+        }
+        if constexpr (kDma) {
+          static_assert(!kDma || kK == 4 * kSlots, "one direct load per two MFMA k-steps");
+          if (k % 2 == 0 && more) dma_load(k / 2, cb ^ 1, doff);
         }
       }
       f32x4 p[2], ds[2];
@@ -553,6 +621,9 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       xch[1][hf][w][lane] = pack8(ds[0], ds[1]);
     }
     __syncthreads();
+    if constexpr (kDma) {
+      if (more) fetch(w0 + NP);
+    }
     // dV^T[d][key] += dout^T[d][pair] P[pair][key];  dK^T += Q^T dS.  Each
     // transpose read serves the four key blocks; halves in pair order.
 #pragma unroll
@@ -570,6 +641,13 @@ void bwd_dkv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
     }
     if (more) put(cb ^ 1);
+    // The next step's loads reuse these registers: wait for this step's here
+    // (they were stored above whenever they were issued), not mid-step.
+    arrived(mrow);
+    arrived(mss);
+    arrived(mse);
+    arrived(ml2);
+    arrived(mdl);
     if constexpr (kDma) wait_vmem();
     __syncthreads();
   }
@@ -623,15 +701,14 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) float plses[kRing][NP], pdels[kRing][NP];
   __shared__ __attribute__((aligned(16))) int prows[kRing][NP], psss[kRing][NP], pses[kRing][NP];
   __shared__ bf16x8 xch[2][2][4][64];   // [step parity][P, dS][key block][lane]
-  // Logical item = (key tile, KV head, sequence), tile fastest, placed
-  // XCD-aware (neighbouring key tiles share most of their rows); key tiles
-  // run from the start of the sequence (the most rows first).
-  const long long item = bwd_item<D>(tiles);
-  if (item >= (long long)tiles * hkv * nseq) return;
-  const int b = (int)(item / ((long long)tiles * hkv));
-  const int kvh = (int)((item / tiles) % hkv), G = hq / hkv;
+  // Item = (key tile, KV head, sequence), key tiles numbered from the start
+  // of the sequence (the most rows first); neighbouring key tiles share most
+  // of their rows.
+  int tile, b, kvh;
+  if (!bwd_item(tiles, hkv, nseq, tile, b, kvh)) return;
+  const int G = hq / hkv;
   const int seq0 = cu_seqlens[b], L = cu_seqlens[b + 1] - seq0;
-  const int j0 = (int)(item % tiles) * kBwdRows;
+  const int j0 = tile * kBwdRows;
   if (j0 >= L) return;
   const int j1 = min(j0 + kBwdRows, L);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -700,7 +777,34 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       pdels[buf][tid] = mdl;
     }
   };
+  // The next step's loads reuse the fetch registers: wait for this step's at
+  // the end of the step (where put stored them), not at the next one's start.
+  auto settle_fetch = [&]() {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      arrived(qr[u]);
+      arrived(dr[u]);
+    }
+    arrived(mrow);
+    arrived(mss);
+    arrived(mse);
+    arrived(ml2);
+    arrived(mdl);
+  };
 
+  // Score waves: K and V of key j as B operands, loaded while the first
+  // tile is.
+  const int j = j0 + 16 * w + x;
+  const int jc = j < j1 ? j : j0;
+  bf16x8 kop[C::kSt], vop[C::kSt];
+  if (scorer) {
+    const size_t ko = ((size_t)(seq0 + jc) * hkv + kvh) * D;
+#pragma unroll
+    for (int st = 0; st < C::kSt; ++st) {
+      kop[st] = ld_global_x8(k + ko + 32 * st + 8 * g);
+      vop[st] = ld_global_x8(v + ko + 32 * st + 8 * g);
+    }
+  }
   if (n_tiles > 0) {
     fetch(0);
     put(0);
@@ -709,15 +813,11 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Each kind runs its own loop (so that its registers do not overlap the
   // other kind's); both pass n_tiles + 1 barriers.
   if (scorer) {
-    // K and V of key j as B operands.
-    const int j = j0 + 16 * w + x;
-    const int jc = j < j1 ? j : j0;
-    bf16x8 kop[C::kSt], vop[C::kSt];
-    const size_t ko = ((size_t)(seq0 + jc) * hkv + kvh) * D;
+    // K and V have arrived: the loop waits only for the tile in flight.
 #pragma unroll
     for (int st = 0; st < C::kSt; ++st) {
-      kop[st] = ld_global_x8(k + ko + 32 * st + 8 * g);
-      vop[st] = ld_global_x8(v + ko + 32 * st + 8 * g);
+      arrived(kop[st]);
+      arrived(vop[st]);
     }
     for (int t = 0; t <= n_tiles; ++t) {
       const bool more = t + 1 < n_tiles;
@@ -762,6 +862,7 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         xch[t & 1][1][w][lane] = pack8(ds[0], ds[1]);
       }
       if (more) put((t + 1) % kRing);
+      settle_fetch();
       __syncthreads();
     }
     return;
@@ -803,6 +904,7 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
     }
     if (more) put((t + 1) % kRing);
+    settle_fetch();
     __syncthreads();
   }
 #pragma unroll
@@ -832,8 +934,8 @@ namespace {
 template <int D>
 hipError_t launch_bwd_d(const BackwardArgs& a, hipStream_t stream) {
   const int tiles = (a.max_seqlen + kBwdRows - 1) / kBwdRows;
-  const long long dq_blocks = xcd_padded_blocks((long long)tiles * a.hq * a.batch);
-  const long long kv_blocks = xcd_padded_blocks((long long)tiles * a.hkv * a.batch);
+  const long long dq_blocks = run_major_blocks(tiles, (long long)a.hq * a.batch);
+  const long long kv_blocks = run_major_blocks(tiles, (long long)a.hkv * a.batch);
   if (dq_blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)dq_blocks), dim3(kBwdThreads), 0, stream,
                      (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.o,

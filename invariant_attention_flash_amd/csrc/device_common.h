@@ -106,6 +106,17 @@ __device__ __forceinline__ void wait_vmem() {
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Read a loaded register here, so that the compiler's own wait insertion
+// (to which the waits above are opaque) waits for its load at this point.
+// Placed before a loop, it keeps a register loaded before the loop and first
+// read inside it from getting a wait in the loop body: such a wait runs every
+// iteration and, since the hardware counter does not tell loads apart, also
+// waits for the loads the loop has in flight by then.
+template <class T>
+__device__ __forceinline__ void arrived(const T& x) {
+  __asm__ volatile("" ::"v"(x));
+}
+
 // Wait until at most `n` vector-memory loads of this wave are outstanding
 // (the newest ones); N is the pipeline depth minus two (0 = wait for all).
 template <int N>

@@ -99,6 +99,30 @@ __device__ inline long long xcd_logical_block(long long i, int tiles) {
   return (c * kXcds + (x + r) % kXcds) * kXcdChunk + j % kXcdChunk;
 }
 
+// Run-major block order.  The same runs of kXcdChunk consecutive tiles of
+// one group (a sequence and head), one XCD per run, but the runs are ordered
+// by their place in the group first: run k of every group, then run k + 1.
+// Callers number a group's tiles most work first, so every XCD starts on
+// the longest tiles of every group and ends on short ones, whatever the
+// sequence lengths (with groups in order, the tiles of the last and perhaps
+// longest sequence would start last).  Run group c (eight runs) is rotated
+// by c over the XCDs, so that no XCD keeps the same groups.  Block i:
+// x = i % 8, c = (i/8) / kXcdChunk, run 8c + (x + c) % 8, tile (i/8) %
+// kXcdChunk of the run.  Returns false for blocks past the last tile.
+__host__ __device__ inline long long run_major_blocks(int tiles, long long groups) {
+  const long long runs = (long long)((tiles + kXcdChunk - 1) / kXcdChunk) * groups;
+  return xcd_padded_blocks(runs * kXcdChunk);
+}
+
+__device__ inline bool run_major_item(long long i, int tiles, long long groups, int& tile,
+                                      long long& group) {
+  const long long x = i % kXcds, j = i / kXcds, c = j / kXcdChunk;
+  const long long run = c * kXcds + (x + c) % kXcds;
+  group = run % groups;
+  tile = (int)((run / groups) * kXcdChunk + j % kXcdChunk);
+  return tile < tiles;
+}
+
 bool prefill_schedule(int d, int group, PrefillSchedule* s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
