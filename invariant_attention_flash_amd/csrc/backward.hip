@@ -269,19 +269,19 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }, tid);
   };
   // Key rows 8w .. 8w + 7 of the tile at k0 (this wave's share) into `buf`.
-  auto dma_tile = [&](int k0, int buf) {
-#pragma unroll
-    for (int r8 = 0; r8 < kBwdTile / 4; ++r8) {
-      const int r = (kBwdTile / 4) * w + r8;
-      const uint32_t off = (uint32_t)((k0 + r) * hkv * D * 2);
-      dma_row(lds_addr(kts[buf] + r * C::kLd), krs, off, lane);
-      dma_row(lds_addr(vts[buf] + r * C::kLd), vrs, off, lane);
-    }
+  // Load e of this wave's share: K (e even) or V (e odd) of row 8w + e / 2.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto dma_load = [&](int k0, int buf, int e) {
+    const int r = (kBwdTile / 4) * wu + e / 2;
+    const uint32_t off = (uint32_t)((k0 + r) * hkv * D * 2);
+    if (e % 2 == 0) dma_row(lds_addr(kts[buf] + r * C::kLd), krs, off, lane);
+    else dma_row(lds_addr(vts[buf] + r * C::kLd), vrs, off, lane);
   };
   // Tile t sits in buffer t & 1; tile t+1's loads fly while tile t is used,
   // one barrier per tile.
   if constexpr (kDma) {
-    dma_tile(lo, 0);
+#pragma unroll
+    for (int e = 0; e < kBwdTile / 2; ++e) dma_load(lo, 0, e);
     wait_vmem();
   } else {
     fetch(lo);
@@ -291,24 +291,49 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __syncthreads();
   for (int k0 = lo, t = 0; k0 < hi; k0 += kBwdTile, ++t) {
     const bool more = k0 + kBwdTile < hi;
-    if (more) {
-      if constexpr (kDma) dma_tile(k0 + kBwdTile, (t + 1) & 1);
-      else fetch(k0 + kBwdTile);
+    if constexpr (!kDma) {
+      if (more) fetch(k0 + kBwdTile);
     }
     const bf16* kt = kts[t & 1];
     const bf16* vt = vts[t & 1];
     // S^T and dP^T: keys 16kb + 4g + e of row x.
     // Four independent MFMA chains (S and dP of both key blocks), k-steps
-    // outermost.
+    // outermost.  At head dim 512 (one wave per SIMD, nothing else to run
+    // while a read is outstanding) the operands of k-step st + 2 are read
+    // while st runs, and the next tile's direct loads are spread over the
+    // k-steps (issued at once, each waits for the memory unit to take the
+    // one before).
+    constexpr int kAhead = D >= 512 ? 3 : 1;
+    auto k_op = [&](int st, int kb) {
+      return ld_lds_x8(kt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
+    };
+    auto v_op = [&](int st, int kb) {
+      return ld_lds_x8(vt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
+    };
+    bf16x8 ka[kAhead][2], va[kAhead][2];
+#pragma unroll
+    for (int a = 0; a < kAhead; ++a) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        ka[a][kb] = k_op(a, kb);
+        va[a][kb] = v_op(a, kb);
+      }
+    }
     f32x4 s[2], dp[2];
 #pragma unroll
     for (int st = 0; st < C::kSt; ++st) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = ld_lds_x8(kt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
-        const bf16x8 va = ld_lds_x8(vt + (16 * kb + x) * C::kLd + 32 * st + 8 * g);
-        s[kb] = mfma16(ka, qop[st], st == 0 ? f32x4{} : s[kb]);
-        dp[kb] = mfma16(va, dop[st], st == 0 ? f32x4{} : dp[kb]);
+        s[kb] = mfma16(ka[st % kAhead][kb], qop[st], st == 0 ? f32x4{} : s[kb]);
+        dp[kb] = mfma16(va[st % kAhead][kb], dop[st], st == 0 ? f32x4{} : dp[kb]);
+        if (st + kAhead < C::kSt) {
+          ka[st % kAhead][kb] = k_op(st + kAhead, kb);
+          va[st % kAhead][kb] = v_op(st + kAhead, kb);
+        }
+      }
+      if constexpr (kDma) {
+        static_assert(!kDma || C::kSt == kBwdTile / 2, "one direct load per k-step");
+        if (more) dma_load(k0 + kBwdTile, (t + 1) & 1, st);
       }
     }
     f32x4 ds[2];
