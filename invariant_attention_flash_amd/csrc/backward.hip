@@ -91,11 +91,7 @@ __device__ __forceinline__ float masked_exp2(bool ok, float arg) {
 }
 
 // Work item of this workgroup: tile `tile` (numbered most work first) of
-// group `group` = sequence * heads + head, in run-major order (kernels.h):
-// runs of consecutive tiles of one group share an XCD's L2, and the longest
-// tiles of every group start first on every XCD.  At head dim 512 that order
-// took the global workload's backward from 26.6 to 24.6 ms (blocks in group
-// order had left the longest sequence's tiles for last).
+// sequence b, head h, in run-major order (kernels.h).
 __device__ __forceinline__ bool bwd_item(int tiles, int heads, int nseq, int& tile, int& b,
                                          int& h) {
   long long grp;

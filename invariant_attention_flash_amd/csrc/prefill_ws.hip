@@ -232,18 +232,19 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ __attribute__((aligned(16))) float lrow[C::kRows];
   static_assert(C::kRoleWaves == 4, "one flag word per score wave, read as one 16-byte word");
 
-  // Logical item = (tile, KV head, sequence), tile fastest; tiles run from
-  // the end of the sequence (longest causal rows first).  Tile t covers
-  // positions [t*P, (t+1)*P), counted from the first tile holding a query
-  // row of the sequence.
-  const long long item = xcd_logical_block(blockIdx.x, tiles);
-  if (item >= (long long)tiles * hkv * nseq) return;
-  const int g = (int)((item / tiles) % hkv);
-  const int b = (int)(item / ((long long)tiles * hkv));
+  // Item = (tile, KV head, sequence) in run-major order (kernels.h); tiles
+  // are numbered from the end of the sequence (longest causal rows first).
+  // Tile t covers positions [t*P, (t+1)*P), counted from the first tile
+  // holding a query row of the sequence.
+  int tile;
+  long long grp;
+  if (!run_major_item(blockIdx.x, tiles, (long long)hkv * nseq, tile, grp)) return;
+  const int g = (int)(grp % hkv);
+  const int b = (int)(grp / hkv);
   constexpr bool PAGED = C::kPaged;
   const SeqGeo sg = seq_geo<PAGED>(cu_seqlens, pk, b);
   const int L = sg.L;
-  const int t = sg.qlo / C::kPositions + tiles - 1 - (int)(item % tiles);
+  const int t = sg.qlo / C::kPositions + tiles - 1 - tile;
   const int p0 = t * C::kPositions;
   if (p0 >= sg.qhi) return;
   const int p1 = min(p0 + C::kPositions, sg.qhi);
@@ -600,7 +601,7 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 template <class C>
 static hipError_t launch_ws(const PrefillArgs& a, hipStream_t stream) {
   const int tiles = prefill_grid_tiles(a, C::kPositions);
-  const long long blocks = xcd_padded_blocks((long long)tiles * a.hkv * a.batch);
+  const long long blocks = run_major_blocks(tiles, (long long)a.hkv * a.batch);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const PagedKv pk{a.q_start, a.block_table, a.max_blocks, a.num_blocks, a.max_context};
   if (a.q_start != nullptr)
