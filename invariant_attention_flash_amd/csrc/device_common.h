@@ -173,4 +173,29 @@ __device__ __forceinline__ bool find_span(const int32_t* __restrict__ spans, int
   return false;
 }
 
+// The spans of a sorted, disjoint list of [start, end) pairs that meet the
+// packed tokens [a, b): indices [first, last), with first the first span
+// ending after a and last the first starting at or after b.  A token t in
+// [a, b) lies in span i (start_i <= t < end_i) for at most one i, in
+// [first, last): the span find_span returns for t.  a and b are
+// wave-uniform, and the list is read with scalar loads (spans_at), so a
+// search costs scalar-cache round trips rather than vector-memory ones.
+__device__ __forceinline__ int span_word(const int32_t* __restrict__ spans, int i) {
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  return ((ConstI32*)spans)[i];
+}
+__device__ __forceinline__ void spans_meeting(const int32_t* __restrict__ spans, int n, int a,
+                                              int b, int& first, int& last) {
+  a = __builtin_amdgcn_readfirstlane(a);
+  b = __builtin_amdgcn_readfirstlane(b);
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (span_word(spans, 2 * mid + 1) <= a) lo = mid + 1; else hi = mid;
+  }
+  first = lo;
+  while (lo < n && span_word(spans, 2 * lo) < b) ++lo;
+  last = lo;
+}
+
 }  // namespace invattn

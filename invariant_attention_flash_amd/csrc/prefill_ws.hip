@@ -256,14 +256,20 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int widx = wave & (C::kRoleWaves - 1);  // index among the waves of its kind
   const bool windowed = window > 0;
 
-  int ss, se;
   // Key range of the workgroup: the window below its first row, the span
   // holding its first row, its last row, the span holding its last row.
+  // Spans [sp0, sp1) are those meeting the workgroup's positions [p0, p1).
   int lo = windowed ? max(0, p0 - window + 1) : 0;
   int hi = p1;
+  int sp0 = 0, sp1 = 0;
   if (num_spans > 0) {
-    if (find_span(spans, num_spans, seq0 + p0, ss, se)) lo = min(lo, max(ss - seq0, 0));
-    if (find_span(spans, num_spans, seq0 + p1 - 1, ss, se)) hi = max(hi, min(se - seq0, L));
+    spans_meeting(spans, num_spans, seq0 + p0, seq0 + p1, sp0, sp1);
+    if (sp0 < sp1) {
+      const int s_first = span_word(spans, 2 * sp0);
+      const int e_last = span_word(spans, 2 * sp1 - 1);
+      if (s_first <= seq0 + p0) lo = min(lo, max(s_first - seq0, 0));
+      if (e_last > seq0 + p1 - 1) hi = max(hi, min(e_last - seq0, L));
+    }
   }
   const int kt0 = lo / BN, kt1 = (hi + BN - 1) / BN;
 
@@ -305,12 +311,6 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       qhead[rb] = g * G + row % G;
       const bool valid = pos >= sg.qlo && pos < sg.qhi;
       qpos[rb] = valid ? pos : -1;  // an invalid row admits no key
-      my_ss[rb] = 0;
-      my_se[rb] = 0;
-      if (num_spans > 0 && valid && find_span(spans, num_spans, seq0 + pos, ss, se)) {
-        my_ss[rb] = ss - seq0;
-        my_se[rb] = min(se - seq0, L);
-      }
     }
     // Q^T operands: lane holds q[row][32*st + 8*gq .. +7] for every st.
     // Rows outside the sequence's query rows load its first query row
@@ -322,6 +322,24 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                               qhead[rb]) * D + 8 * ln.gq;
 #pragma unroll
       for (int st = 0; st < C::kSt; ++st) qr[rb][st] = ld_global_x8(qrow + 32 * st);
+    }
+    // Each row's span (while Q is in flight): the one of the workgroup's
+    // spans that holds it, if any.
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      my_ss[rb] = 0;
+      my_se[rb] = 0;
+    }
+    for (int i = sp0; i < sp1; ++i) {
+      const int s_i = span_word(spans, 2 * i), e_i = span_word(spans, 2 * i + 1);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int tok = seq0 + qpos[rb];
+        if (qpos[rb] >= 0 && tok >= s_i && tok < e_i) {
+          my_ss[rb] = s_i - seq0;
+          my_se[rb] = min(e_i - seq0, L);
+        }
+      }
     }
     RowStats<RB> rs;
     rs.init();
