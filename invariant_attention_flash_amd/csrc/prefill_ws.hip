@@ -579,13 +579,20 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // same bits as dividing, at a quarter of the instructions.  A row block in
   // which some live row's quotient is below kRecipDivMin, zero or NaN divides
   // instead.
+  // Every row block's sum and reciprocal first (independent of each other),
+  // so that their latencies overlap.
+  float lrs[kRB], ys[kRB];
+#pragma unroll
+  for (int r = 0; r < kRB; ++r) lrs[r] = lrow[16 * r + ln.x];
+#pragma unroll
+  for (int r = 0; r < kRB; ++r) ys[r] = 1.0f / lrs[r];
 #pragma unroll
   for (int r = 0; r < kRB; ++r) {
     const int row = 16 * r + ln.x;
     const int pos = p0 + row / G;
     const bool live = pos >= sg.qlo && pos < sg.qhi;
-    const float lr = lrow[row];
-    const float y = 1.0f / lr;
+    const float lr = lrs[r];
+    const float y = ys[r];
     float qv[C::kDbW][4];
     bool small = false;
 #pragma unroll
