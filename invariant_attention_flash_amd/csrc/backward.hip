@@ -714,9 +714,11 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   using C = BwdCfg<D>;
   constexpr int NP = kBwdTile;
   constexpr int kRing = 3;
-  constexpr int kThreads = 2 * kBwdThreads;
-  constexpr int kPer = NP * D / 8 / kThreads;   // 16-byte chunks per thread per tensor
-  static_assert((NP * D / 8) % kThreads == 0, "whole chunks per thread");
+  // The gradient waves load every pair tile (the score waves, the longer
+  // path, would otherwise stall on their issue): loader lt = tid - 256 holds
+  // 16-byte chunks lt + 256u of Q and dout, and lanes lt < NP the metadata.
+  constexpr int kPer = NP * D / 8 / kBwdThreads;   // chunks per loader per tensor
+  static_assert((NP * D / 8) % kBwdThreads == 0, "whole chunks per loader");
   __shared__ __attribute__((aligned(16))) bf16 qts[kRing][NP * C::kLd];
   __shared__ __attribute__((aligned(16))) bf16 dts[kRing][NP * C::kLd];
   __shared__ __attribute__((aligned(16))) float plses[kRing][NP], pdels[kRing][NP];
@@ -747,14 +749,16 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int n_pairs = (hi - lo) * G;
   const int n_tiles = (n_pairs + NP - 1) / NP;
 
+  const int lt = tid - kBwdThreads;
   bf16x8 qr[kPer], dr[kPer];
   int mrow = -1, mss = 0, mse = 0;
   float ml2 = 0.f, mdl = 0.f;
   auto fetch = [&](int t) {
+    if (scorer) return;
     const int w0 = t * NP;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads;
+      const int e = lt + u * kBwdThreads;
       const int pw = w0 + e / (D / 8), c = 8 * (e % (D / 8));
       if (pw < n_pairs) {
         const size_t ro = ((size_t)(seq0 + lo + pw / G) * hq + kvh * G + pw % G) * D + c;
@@ -765,8 +769,8 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         dr[u] = bf16x8{};
       }
     }
-    if (tid < NP) {
-      const int pw = w0 + tid;
+    if (lt < NP) {
+      const int pw = w0 + lt;
       mrow = -1;
       mss = mse = 0;
       ml2 = mdl = 0.f;
@@ -783,19 +787,20 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   };
   auto put = [&](int buf) {
+    if (scorer) return;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int e = tid + u * kThreads;
+      const int e = lt + u * kBwdThreads;
       const int r = e / (D / 8), c = 8 * (e % (D / 8));
       st_lds_x8(qts[buf] + r * C::kLd + c, qr[u]);
       st_lds_x8(dts[buf] + r * C::kLd + c, dr[u]);
     }
-    if (tid < NP) {
-      prows[buf][tid] = mrow;
-      psss[buf][tid] = mss;
-      pses[buf][tid] = mse;
-      plses[buf][tid] = ml2;
-      pdels[buf][tid] = mdl;
+    if (lt < NP) {
+      prows[buf][lt] = mrow;
+      psss[buf][lt] = mss;
+      pses[buf][lt] = mse;
+      plses[buf][lt] = ml2;
+      pdels[buf][lt] = mdl;
     }
   };
   // The next step's loads reuse the fetch registers: wait for this step's at
@@ -841,8 +846,6 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       arrived(vop[st]);
     }
     for (int t = 0; t <= n_tiles; ++t) {
-      const bool more = t + 1 < n_tiles;
-      if (more) fetch(t + 1);
       if (t < n_tiles) {
         const int cb = t % kRing;
         const bf16* qt = qts[cb];
@@ -882,8 +885,6 @@ void bwd_dkv_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         xch[t & 1][0][w][lane] = pack8(p[0], p[1]);
         xch[t & 1][1][w][lane] = pack8(ds[0], ds[1]);
       }
-      if (more) put((t + 1) % kRing);
-      settle_fetch();
       __syncthreads();
     }
     return;
