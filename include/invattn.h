@@ -199,8 +199,8 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
  *   p_ij    = exp2(fma(s_ij, c, -lse2_i))         (0 off the mask)
  *   ds_ij   = p_ij (dp_ij - delta_i)
  *   dq_i    = scale * sum_j bf16(ds_ij) k_j       MFMAs over 32 keys, key
- *                                                  tiles ascending from a
- *                                                  start fixed by the row tile
+ *                                                  tiles [32m, 32m + 32) of
+ *                                                  the sequence, ascending
  *   dk_j    = scale * sum_(i,h) bf16(ds_ij) q_ih  MFMAs over 32 (row, head)
  *   dv_j    =         sum_(i,h) bf16(p_ij) dout_ih pairs: rows ascending, then
  *                                                  the group's heads

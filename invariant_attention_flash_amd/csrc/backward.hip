@@ -16,8 +16,9 @@
 //           delta by the same MFMA sequence as dp)
 //   p_ij    = exp2(fma(s_ij, c, -lse2_i))   (0 where the mask excludes j)
 //   ds_ij   = p_ij * (dp_ij - delta_i)
-//   dq_i    = scale * sum_j bf16(ds_ij) k_j          32 keys per MFMA, key
-//                                                    tiles ascending
+//   dq_i    = scale * sum_j bf16(ds_ij) k_j          32 keys per MFMA (key
+//                                                    tiles at multiples of
+//                                                    32), ascending
 //   dk_j    = scale * sum_(i,h) bf16(ds_ij) q_(i,h)  32 (row, head) pairs per
 //   dv_j    =         sum_(i,h) bf16(p_ij) dout_(i,h) MFMA: rows ascending, then
 //                                                    the group's heads
@@ -232,6 +233,11 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (find_span(spans, num_spans, seq0 + r0, s0, e0)) lo = min(lo, max(s0 - seq0, 0));
     if (find_span(spans, num_spans, seq0 + r1 - 1, s0, e0)) hi = max(hi, min(e0 - seq0, L));
   }
+  // Key tiles on the grid of multiples of kBwdTile from the sequence start
+  // (the forward's): which keys share an MFMA then depends on the keys
+  // alone, not on where the row tile starts.  Keys below the window edge in
+  // the first tile are masked for every row.
+  lo &= ~(kBwdTile - 1);
 
   // The wave accumulates dQ^T for its quarter of the head dim (columns
   // w*D/4 + 16*db + ...) and all four row blocks of the workgroup.
