@@ -102,6 +102,29 @@ def decode_bytes(seq_lens, hq, hkv, d, window=-1, block=16):
     return b
 
 
+def bf16_rne_bits(x):
+    """fp64 values rounded once to bf16 (round to nearest, ties to even), as
+    bf16 bit patterns.  Exact: the value is rounded at its own binade's bf16
+    spacing (2^(e-7), floored at the subnormal spacing 2^-133) in fp64, where
+    scaling by a power of two is exact and numpy rounds halves to even; the
+    result is a bf16 value, which float32 holds exactly."""
+    x = np.asarray(x, np.float64)
+    finite = np.isfinite(x) & (x != 0)
+    _, e2 = np.frexp(np.where(finite, x, 1.0))   # |x| in [2^(e2-1), 2^e2)
+    e = np.maximum(e2 - 1, -126)
+    ulp = np.ldexp(1.0, e - 7)
+    r = np.where(finite, np.round(x / ulp) * ulp, x)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def correctly_rounded_share(got_bits, ref):
+    """Share of bf16 outputs equal in value to the bf16 rounding of the fp64
+    reference (+0 and -0 count as equal)."""
+    def f32(b):
+        return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return float(np.mean(f32(got_bits) == f32(bf16_rne_bits(ref))))
+
+
 def load_traffic(kernel: str):
     """HBM traffic per launch from the committed counter summary, only if it
     was taken on the current kernel sources."""
@@ -544,23 +567,28 @@ def main():
                                    scale=c["scale"], spans=h["spans"], rows=rows)
                 dt += time.perf_counter() - t
                 fl += float((4.0 * c["d"] * h["per_row"][rows[:, 0]]).sum())
-                got = synth.bf16_to_f32(h["out"][rows[:, 0], rows[:, 1]]).astype(np.float64)
+                bits = h["out"][rows[:, 0], rows[:, 1]]
+                got = synth.bf16_to_f32(bits).astype(np.float64)
                 err = np.abs(got - o)
-                par.append((err.max(), float((err ** 2).sum()), float((o ** 2).sum())))
+                par.append((err.max(), float((err ** 2).sum()), float((o ** 2).sum()),
+                            correctly_rounded_share(bits, o)))
             return dt, fl, par
 
         # rounds of 256 rows per layer until the oracle has run cpu_seconds
         dt = fl = 0.0
         n = 0
-        acc = [[0.0, 0.0, 0.0] for _ in layers]
+        acc = [[0.0, 0.0, 0.0, 0.0] for _ in layers]
+        rounds = 0
         while dt < args.cpu_seconds and n < HY_N * HY_LEN * 32:
             d_, f_, par = sample(256)
             dt, fl, n = dt + d_, fl + f_, n + 256
-            for a, (mx, e2, o2) in zip(acc, par):
+            rounds += 1
+            for a, (mx, e2, o2, cr) in zip(acc, par):
                 a[0] = max(a[0], mx)
                 a[1] += e2
                 a[2] += o2
-        par = [(a[0], float(np.sqrt(a[1] / a[2])), n) for a in acc]
+                a[3] += cr
+        par = [(a[0], float(np.sqrt(a[1] / a[2])), a[3] / max(rounds, 1)) for a in acc]
         cpu = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
                "cpu_model": cpu_model(),
                "sample": f"{n} seeded (token, head) rows of each of the {nl} hybrid layers "
@@ -568,8 +596,12 @@ def main():
                          f"{dt:.1f} s"}
         log(f"prefill oracle: {n * nl} rows in {dt:.1f} s")
         parity = {"rows_per_layer": n,
-                  "layers": [{"max_abs": a, "rel_l2": r} for a, r, _ in par],
-                  "max_abs": max(a for a, _, _ in par), "rel_l2": max(r for _, r, _ in par)}
+                  "layers": [{"max_abs": a, "rel_l2": r, "correctly_rounded": cr}
+                             for a, r, cr in par],
+                  "max_abs": max(a for a, _, _ in par), "rel_l2": max(r for _, r, _ in par),
+                  "correctly_rounded_min": min(cr for _, _, cr in par),
+                  "correctly_rounded_note": "share of sampled outputs equal to the bf16 "
+                                            "round-to-nearest-even of the fp64 oracle"}
         parity["pass"] = parity["max_abs"] <= 2e-2 and parity["rel_l2"] <= 1e-2
 
         # decode oracle: the batch-1 decode (sequence 0, whole context) on the host
@@ -583,13 +615,15 @@ def main():
         t = time.perf_counter()
         od = oracle.decode(q0, kc0, vc0, bt0, np.array([L0], np.int32), scale=dc["scale"])
         ddt = time.perf_counter() - t
-        got = synth.bf16_to_f32(host_bits(outs[1])).astype(np.float64)
+        dbits = host_bits(outs[1])
+        got = synth.bf16_to_f32(dbits).astype(np.float64)
         cpu["decode"] = {"value": decode_bytes(dlen[:1], 32, 4, 512) / ddt / 1e9, "unit": "GB/s",
                          "cores": threads, "kind": "oracle",
                          "sample": f"the batch-1 decode (context {L0}), fp64, {ddt:.2f} s"}
         parity["decode_batch1"] = {"max_abs": float(np.abs(got - od[0]).max()),
                                    "rel_l2": float(np.linalg.norm(got - od[0])
-                                                   / np.linalg.norm(od[0]))}
+                                                   / np.linalg.norm(od[0])),
+                                   "correctly_rounded": correctly_rounded_share(dbits, od[0])}
         parity["pass"] = parity["pass"] and parity["decode_batch1"]["max_abs"] <= 2e-2 and \
             parity["decode_batch1"]["rel_l2"] <= 1e-2
 
