@@ -160,13 +160,14 @@ __device__ __forceinline__ void score_phase(const bf16* __restrict__ kt, uint32_
 //   P^T operand (row block r): lane l's element pt[64*r + l]; 16x16x32 MFMAs
 //     over the 32 keys of a tile, or 16x16x16 MFMAs over the 16 of a
 //     16-key tile.
-template <class C, bool DMA>
+template <class C, bool DMA, class PRE>
 __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
                                          const typename C::PT* __restrict__ pt, uint32_t kpre,
                                          const u32x4& krs, int kk0, uint32_t vpre,
                                          const u32x4& vrs, int vk0, uint32_t rs_bytes, int widx,
                                          int lane,
-                                         uint32_t vrow, uint32_t vc16w, f32x4 (*o)[C::kDbW]) {
+                                         uint32_t vrow, uint32_t vc16w, f32x4 (*o)[C::kDbW],
+                                         PRE&& pre) {
   constexpr int kN = C::kRowBlocks;           // one row block per group
   // Loads of the step: K (when this wave loads K) then V.
   constexpr int kKL = C::kPvLoadsK ? C::kLoads : 0;
@@ -184,11 +185,14 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
     if constexpr (C::BN == 32) vop[db] = cat8(ld_lds_tr(p), ld_lds_tr(p + 16 * C::D));
     else vop[db] = ld_lds_tr(p);
   }
-  PT pop[2];
-  pop[0] = pt[lane];
+  // Every row block's P^T operand of the step, read together with V^T: the
+  // step waits for one LDS round trip, not one per row block.
+  PT pop[kN];
+#pragma unroll
+  for (int r = 0; r < kN; ++r) pop[r] = pt[64 * r + lane];
+  pre();  // the accumulator scaling of the step, while the reads are in flight
 #pragma unroll
   for (int r = 0; r < kN; ++r) {
-    if (r + 1 < kN) pop[(r + 1) & 1] = pt[64 * (r + 1) + lane];
     if constexpr (DMA) {
       constexpr bool kFirst = C::kLoadsFirst;
       if (kFirst ? r == 0 : r % kEvery == 0) {
@@ -205,8 +209,8 @@ __device__ __forceinline__ void pv_phase(const bf16* __restrict__ vt,
     }
 #pragma unroll
     for (int db = 0; db < C::kDbW; ++db) {
-      if constexpr (C::BN == 32) o[r][db] = mfma16(vop[db], pop[r & 1], o[r][db]);
-      else o[r][db] = mfma16k16(vop[db], pop[r & 1], o[r][db]);
+      if constexpr (C::BN == 32) o[r][db] = mfma16(vop[db], pop[r], o[r][db]);
+      else o[r][db] = mfma16k16(vop[db], pop[r], o[r][db]);
     }
   }
 }
@@ -484,8 +488,10 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // Scale the accumulator blocks whose rows moved their reference max in
   // tile kt (flags and factors written by the score waves in step kt).
-  auto rescale_from = [&](int kt) {
-    const u32x4 f = *reinterpret_cast<const u32x4*>(fl[kt & 1]);
+  // The flags are read before the step's operands (flags_of), and used once
+  // those reads are in flight (rescale_with).
+  auto flags_of = [&](int kt) { return *reinterpret_cast<const u32x4*>(fl[kt & 1]); };
+  auto rescale_with = [&](int kt, const u32x4& f) {
     const uint32_t mask = __builtin_amdgcn_readfirstlane(
         f[0] | (f[1] << RB) | (f[2] << (2 * RB)) | (f[3] << (3 * RB)));
     if (mask != 0) {
@@ -552,9 +558,11 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int i = 0; i < C::kLoads; ++i)
         dma_rows<C::kChunks, C::kLoads, 1, C::kSwV>(vpre, vrs, vk0, i, rs_bytes, widx, lane);
     } else {
-      if constexpr (MODE == 2) rescale_from(kt - 1);
+      const u32x4 f = MODE == 2 ? flags_of(kt - 1) : u32x4{};
       pv_phase<C, true>(vcur, pcur, kpre, krs, kk0, vpre, vrs, vk0, rs_bytes, widx, lane,
-                        ln.vrow, opaque(vc16w), oacc);
+                        ln.vrow, opaque(vc16w), oacc, [&] {
+                          if constexpr (MODE == 2) rescale_with(kt - 1, f);
+                        });
     }
   };
   step(kt0, Mode0{});
@@ -566,11 +574,13 @@ void prefill_ws_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int kl = kt1 - 1;
   wait_vmcnt<0>();
   lds_barrier();
-  if (kl > kt0) rescale_from(kl);
   {
     const u32x4 none = buffer_rsrc(v, 0);
+    const u32x4 f = flags_of(kl);
     pv_phase<C, false>(vs[(kl - kt0) % NR], pl[kl & 1], 0, none, 0, 0, none, 0, rs_bytes, widx,
-                       lane, ln.vrow, vc16w, oacc);
+                       lane, ln.vrow, vc16w, oacc, [&] {
+                         if (kl > kt0) rescale_with(kl, f);
+                       });
   }
 
   // Epilogue: o = acc / l (the IEEE fp32 quotient), bf16 RNE, store this
