@@ -531,9 +531,26 @@ def main():
         t = time_calls(lambda: torch.matmul(ga, gb, out=gc), args.reps)
         gemm_tf = 2.0 * n ** 3 / (float(np.median(t)) * 1e-3) / 1e12
         del ga, gb, gc
+        # HBM: a plain device-to-device copy of 1 GiB (read + write) and a sum
+        # over the same GiB (read only), both through torch's own kernels
+        src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        sink = torch.zeros((), dtype=torch.float32, device=dev)
+        dst.copy_(src)
+        t = time_calls(lambda: dst.copy_(src), args.reps)
+        copy_gbs = 2.0 * CALIBRATION_BYTES / (float(np.median(t)) * 1e-3) / 1e9
+        torch.sum(src, dim=0, out=sink)
+        t = time_calls(lambda: torch.sum(src, dim=0, out=sink), args.reps)
+        read_gbs = CALIBRATION_BYTES / (float(np.median(t)) * 1e-3) / 1e9
+        del src, dst, sink
         ceilings = {"gemm_bf16_tflops": gemm_tf, "gemm": f"torch.matmul bf16 {n}x{n}x{n}, median",
-                    "prefill_frac_of_gemm": hy_tflops / gemm_tf}
-        log(f"ceiling: bf16 GEMM {gemm_tf:.0f} TFLOP/s")
+                    "prefill_frac_of_gemm": hy_tflops / gemm_tf,
+                    "hbm_copy_gbs": copy_gbs, "hbm_read_gbs": read_gbs,
+                    "hbm": "torch copy_ of 1 GiB (read + write bytes) and torch.sum over 1 GiB "
+                           "(read bytes), median",
+                    "decode_frac_of_read": dc_gbs / read_gbs}
+        log(f"ceiling: bf16 GEMM {gemm_tf:.0f} TFLOP/s, HBM copy {copy_gbs:.0f} GB/s, "
+            f"read {read_gbs:.0f} GB/s")
 
     # ---------------- CPU oracle baselines + parity spot-checks on sampled rows
     cpu = None
