@@ -64,6 +64,9 @@ def open_library(path: str):
     lib.oracle_prefill_backward_units.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp,
                                                   ctypes.c_int, vp, vp, vp, vp, i32, i32, i32,
                                                   i32, i32, dbl, vp, i32, vp, i64, vp, i64, i32]
+    lib.oracle_qk_prologue.restype = ctypes.c_int
+    lib.oracle_qk_prologue.argtypes = [vp, ctypes.c_int, i64, i32, i32, vp, vp, ctypes.c_int,
+                                       dbl, dbl, i32, i32, dbl, vp, i32]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = [i32]
     return lib
@@ -211,3 +214,29 @@ def prefill_backward(q, k, v, dout, cu_seqlens, window=NO_WINDOW, scale=None, sp
     if rc != 0:
         raise ValueError("oracle_prefill_backward_units rejected its arguments")
     return dq, dk, dv
+
+
+def qk_prologue(x, positions, weight=None, eps=1e-6, offset=0.0, rotary_dims=0, freq_dims=None,
+                theta=10000.0, threads=0, lib=None):
+    """The layer's attention prologue on Q or K: RMSNorm over the head dim
+    (skipped when ``weight`` is None), then RoPE on the first ``rotary_dims``
+    dims (pairs i, i + R/2; angle pos * theta^(-2i/F), F = ``freq_dims``,
+    default R).  x [T, H, D]; positions [T]; weight [D].  Returns fp64
+    [T, H, D].  The readings behind this definition are listed in oracle.c.
+    """
+    x = np.ascontiguousarray(x)
+    T, h, d = x.shape
+    pos = np.ascontiguousarray(positions, dtype=np.int32).reshape(-1)
+    if pos.shape[0] != T:
+        raise ValueError("positions must have one entry per row")
+    w = None if weight is None else np.ascontiguousarray(weight)
+    R = int(rotary_dims)
+    F = R if freq_dims is None else int(freq_dims)
+    out = np.zeros((T, h, d), np.float64)
+    rc = (lib or _load()).oracle_qk_prologue(_ptr(x), _code(x), T, h, d, _ptr(pos), _ptr(w),
+                                             F64 if w is None else _code(w), float(eps),
+                                             float(offset), R, F, float(theta), _ptr(out),
+                                             int(threads))
+    if rc != 0:
+        raise ValueError("oracle_qk_prologue rejected its arguments")
+    return out

@@ -410,6 +410,72 @@ int oracle_prefill_backward(const void* q, int qdtype, const void* k, const void
                                          num_spans, NULL, 0, NULL, 0, threads);
 }
 
+/*
+ * The attention prologue of a layer: RMSNorm over the head dim of every
+ * (row, head) vector of Q or K, then rotary position embedding (RoPE).
+ * Sources: the layer's prologue names a Q/K RMSNorm for head dims 256 and
+ * 512, a RoPE on the sliding layers and a proportional ("p") RoPE on the
+ * global layers ("RFC: Gemma-4-31B-it train/rollout consistency", section 6,
+ * items 4 and 6); the RMSNorm formula with an additive weight offset and
+ * fp32 math is the one of "Gated RMSNorm CUDA kernel for the GDN block"
+ * (Summary), without its gate.  The pages give no epsilon, offset, rotary
+ * width, frequency base or pairing; they are arguments here.  Readings
+ * (every one a reading, not a page fact):
+ *
+ *   norm:  r = 1 / sqrt(mean_d x_d^2 + eps),  y_d = x_d * r * (offset + w_d)
+ *          (skipped when weight is NULL: y = x);
+ *   rope:  for i < R/2 the pair (y_i, y_{i+R/2}) turns by the angle
+ *          pos * theta^(-2i/F):  (a, b) -> (a cos - b sin, a sin + b cos);
+ *          dims R .. D-1 pass through.  R = D is the full RoPE; R < D with
+ *          F = D is the proportional reading (the turned dims keep the
+ *          frequencies of a full RoPE over D), F = R the plain partial one.
+ *
+ * x [rows, heads, d] (bf16 bits, fp32 or fp64), positions [rows], weight
+ * [d] or NULL, out [rows, heads, d] fp64.
+ */
+int oracle_qk_prologue(const void* x, int xdtype, int64_t rows, int32_t heads, int32_t d,
+                       const int32_t* positions, const void* weight, int wdtype, double eps,
+                       double offset, int32_t rotary_dims, int32_t freq_dims, double theta,
+                       double* out, int32_t threads) {
+    if (rows < 0 || heads <= 0 || d <= 0 || rotary_dims < 0 || rotary_dims > d ||
+        rotary_dims % 2 != 0 || (rotary_dims > 0 && (freq_dims <= 0 || !(theta > 0))) ||
+        !(eps >= 0) || (rows > 0 && positions == NULL))
+        return -1;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for schedule(dynamic, 16)
+#else
+    (void)threads;
+#endif
+    for (int64_t rh = 0; rh < rows * heads; ++rh) {
+        const int64_t base = rh * d;
+        const int64_t row = rh / heads;
+        double* y = out + base;
+        if (weight != NULL) {
+            double ss = 0.0;
+            for (int32_t j = 0; j < d; ++j) {
+                const double v = load_elem(x, xdtype, base + j);
+                ss += v * v;
+            }
+            const double r = 1.0 / sqrt(ss / d + eps);
+            for (int32_t j = 0; j < d; ++j)
+                y[j] = load_elem(x, xdtype, base + j) * r * (offset + load_elem(weight, wdtype, j));
+        } else {
+            for (int32_t j = 0; j < d; ++j) y[j] = load_elem(x, xdtype, base + j);
+        }
+        const int32_t half = rotary_dims / 2;
+        const double pos = (double)positions[row];
+        for (int32_t i = 0; i < half; ++i) {
+            const double ang = pos * pow(theta, -2.0 * i / freq_dims);
+            const double c = cos(ang), s = sin(ang);
+            const double a = y[i], b = y[i + half];
+            y[i] = a * c - b * s;
+            y[i + half] = a * s + b * c;
+        }
+    }
+    return 0;
+}
+
 /* Number of threads an OpenMP region of this library runs with. */
 int oracle_num_threads(int32_t threads) {
 #ifdef _OPENMP

@@ -431,10 +431,131 @@ def pin_bruteforce_stored_formats(lib=None):
             assert np.abs(o - bruteforce.decode(q, kc, vc, bt, sl, window=w)).max() <= 1e-12
 
 
+
+
+
+# ---------------------------------------------------------------------------
+# The attention prologue (RMSNorm over the head dim, then RoPE), pinned by
+# closed forms, invariants and a brute force written with complex numbers.
+
+def _prologue_brute(x, pos, weight, eps, offset, R, F, theta):
+    """numpy: the norm by mean/sqrt, the rotation as a complex product."""
+    x = np.asarray(x, np.float64)
+    if weight is not None:
+        rms = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+        y = x / rms * (offset + np.asarray(weight, np.float64))
+    else:
+        y = x.copy()
+    h = R // 2
+    if h:
+        freq = theta ** (-2.0 * np.arange(h) / F)
+        rot = np.exp(1j * np.asarray(pos, np.float64)[:, None] * freq[None, :])  # [T, h]
+        z = (y[..., :h] + 1j * y[..., h:R]) * rot[:, None, :]
+        y[..., :h] = z.real
+        y[..., h:R] = z.imag
+    return y
+
+
+def pin_prologue_hand_values(lib=None):
+    """Angles written out by hand from the definition pos * theta^(-2i/F):
+    theta = 10000, R = 4: pair 0 turns by pos, pair 1 by pos * 10000^(-2/F),
+    i.e. pos / 100 for F = 4 and pos / 10 for F = 8 (proportional)."""
+    e = np.eye(4)[:, None, :]                              # rows e0 .. e3, one head
+    for F, step1 in ((4, 0.01), (8, 0.1)):
+        for pos in (1, 3):
+            y = oracle.qk_prologue(e, [pos] * 4, rotary_dims=4, freq_dims=F, theta=10000.0,
+                                   lib=lib)[:, 0, :]
+            a0, a1 = pos * 1.0, pos * step1
+            want = np.array([[math.cos(a0), 0, math.sin(a0), 0],
+                             [0, math.cos(a1), 0, math.sin(a1)],
+                             [-math.sin(a0), 0, math.cos(a0), 0],
+                             [0, -math.sin(a1), 0, math.cos(a1)]])
+            assert np.abs(y - want).max() <= 1e-13, (F, pos)
+    # dims past the rotary width pass through untouched
+    x = np.arange(1.0, 9.0)[None, None, :]
+    y = oracle.qk_prologue(x, [5], rotary_dims=4, freq_dims=8, lib=lib)
+    assert np.array_equal(y[0, 0, 4:], x[0, 0, 4:])
+
+
+def pin_prologue_norm_closed_form(lib=None):
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((5, 3, 16)) * rng.uniform(0.1, 10.0, (5, 3, 1))
+    ones = np.ones(16)
+    y = oracle.qk_prologue(x, np.zeros(5), weight=ones, eps=0.0, lib=lib)
+    assert np.abs(np.mean(y * y, axis=-1) - 1.0).max() <= 1e-12   # unit RMS
+    y2 = oracle.qk_prologue(7.5 * x, np.zeros(5), weight=ones, eps=0.0, lib=lib)
+    assert np.abs(y2 - y).max() <= 1e-12                           # scale-free
+    eps = 0.3
+    ye = oracle.qk_prologue(x, np.zeros(5), weight=ones, eps=eps, lib=lib)
+    ms = np.mean(x * x, axis=-1)
+    assert np.abs(np.mean(ye * ye, axis=-1) - ms / (ms + eps)).max() <= 1e-12
+    w = rng.standard_normal(16)
+    a = oracle.qk_prologue(x, np.zeros(5), weight=w, eps=eps, offset=1.0, lib=lib)
+    b = oracle.qk_prologue(x, np.zeros(5), weight=w + 1.0, eps=eps, offset=0.0, lib=lib)
+    assert np.abs(a - b).max() <= 1e-12                            # offset adds to the weight
+    c = oracle.qk_prologue(x, np.zeros(5), weight=2.0 * w, eps=eps, lib=lib)
+    d = oracle.qk_prologue(x, np.zeros(5), weight=w, eps=eps, lib=lib)
+    assert np.abs(c - 2.0 * d).max() <= 1e-12                      # linear in the weight
+
+
+def pin_prologue_rope_invariants(lib=None):
+    rng = np.random.default_rng(43)
+    T, H, D, R = 6, 2, 16, 12
+    q = rng.standard_normal((T, H, D))
+    k = rng.standard_normal((T, H, D))
+    pos = rng.integers(0, 40000, T)
+    for F in (R, D):
+        # position 0 is the identity
+        assert np.abs(oracle.qk_prologue(q, np.zeros(T), rotary_dims=R, freq_dims=F, lib=lib)
+                      - q).max() == 0
+        y = oracle.qk_prologue(q, pos, rotary_dims=R, freq_dims=F, lib=lib)
+        # each turned pair keeps its length; other dims are unchanged
+        h = R // 2
+        n0 = q[..., :h] ** 2 + q[..., h:R] ** 2
+        n1 = y[..., :h] ** 2 + y[..., h:R] ** 2
+        assert np.abs(n1 - n0).max() <= 1e-9
+        assert np.array_equal(y[..., R:], q[..., R:])
+        # turning by a then by b is turning by a + b
+        a, b = rng.integers(0, 3000, T), rng.integers(0, 3000, T)
+        yab = oracle.qk_prologue(oracle.qk_prologue(q, a, rotary_dims=R, freq_dims=F, lib=lib),
+                                 b, rotary_dims=R, freq_dims=F, lib=lib)
+        assert np.abs(yab - oracle.qk_prologue(q, a + b, rotary_dims=R, freq_dims=F,
+                                               lib=lib)).max() <= 1e-9
+        # scores depend on the relative position only
+        m, n, s = 1234, 77, 5000
+        qm = oracle.qk_prologue(q[:1], [m], rotary_dims=R, freq_dims=F, lib=lib)
+        kn = oracle.qk_prologue(k[:1], [n], rotary_dims=R, freq_dims=F, lib=lib)
+        qs = oracle.qk_prologue(q[:1], [m + s], rotary_dims=R, freq_dims=F, lib=lib)
+        ks = oracle.qk_prologue(k[:1], [n + s], rotary_dims=R, freq_dims=F, lib=lib)
+        assert abs(np.sum(qm * kn) - np.sum(qs * ks)) <= 1e-9
+
+
+def pin_prologue_bruteforce(lib=None):
+    rng = np.random.default_rng(47)
+    T, H = 7, 3
+    pos = rng.integers(0, 32768, T)
+    for D, R, F in ((64, 64, 64), (32, 8, 32), (32, 16, 16), (16, 0, 16)):
+        for make in (lambda s: rng.standard_normal(s),
+                     lambda s: rng.standard_normal(s).astype(np.float32),
+                     lambda s: _random_bf16(rng, s)):
+            x = make((T, H, D))
+            w = make((D,))
+            xf = bruteforce._f64(x)
+            wf = bruteforce._f64(w)
+            for weight, eps, off in ((w, 1e-6, 0.0), (w, 0.25, 1.0), (None, 0.0, 0.0)):
+                y = oracle.qk_prologue(x, pos, weight=weight, eps=eps, offset=off, rotary_dims=R,
+                                       freq_dims=F, theta=10000.0 if R else 1.0, lib=lib)
+                want = _prologue_brute(xf, pos, None if weight is None else wf, eps, off, R, F,
+                                       10000.0)
+                assert np.abs(y - want).max() <= 1e-9 * max(1.0, np.abs(want).max()), (D, R, F)
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_rows_sum_to_one,
             pin_window_covering_sequence_is_global, pin_one_token_returns_v,
             pin_zero_query_is_mean, pin_dominant_key, pin_gqa_reduces_to_mha,
             pin_packing_invariance, pin_row_subset, pin_decode,
             pin_backward_finite_differences, pin_backward_single_key,
             pin_backward_gqa_is_mha_summed, pin_backward_units, pin_bf16_widening,
-            pin_bruteforce_stored_formats]
+            pin_bruteforce_stored_formats, pin_prologue_hand_values,
+            pin_prologue_norm_closed_form, pin_prologue_rope_invariants,
+            pin_prologue_bruteforce]

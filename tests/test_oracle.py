@@ -48,6 +48,17 @@ MUTANTS = [
      "del += load_elem(dout, dodtype, w * (int64_t)d + c) * load_elem(v, kvdtype, c);"),
     ("backward: dq uses q", "dqi[c] += scale * ds * load_elem(k, kvdtype, key_off[a] + c);",
      "dqi[c] += scale * ds * load_elem(q, qdtype, w * (int64_t)d + c);"),
+    ("prologue: rope partner", "const double a = y[i], b = y[i + half];",
+     "const double a = y[i], b = y[half - 1 - i + half];"),
+    ("prologue: rope sign", "y[i] = a * c - b * s;", "y[i] = a * c + b * s;"),
+    ("prologue: frequency exponent", "pow(theta, -2.0 * i / freq_dims)",
+     "pow(theta, -1.0 * i / freq_dims)"),
+    ("prologue: mean over d - 1", "sqrt(ss / d + eps)", "sqrt(ss / (d - 1) + eps)"),
+    ("prologue: eps outside the root", "1.0 / sqrt(ss / d + eps)", "1.0 / (sqrt(ss / d) + eps)"),
+    ("prologue: offset ignored", "(offset + load_elem(weight, wdtype, j))",
+     "(load_elem(weight, wdtype, j))"),
+    ("prologue: position of another row", "const int64_t row = rh / heads;",
+     "const int64_t row = rh % heads;"),
 ]
 
 
@@ -59,10 +70,14 @@ def test_planted_mistake_is_caught(tmp_path, name, old, new):
     mutated.write_text(src.replace(old, new))
     so = oracle.build(src=str(mutated), out=str(tmp_path / "liboracle_mutant.so"), werror=False)
     lib = oracle.open_library(so)
+    # the pins of the mutated function's own family first; stop at the first catch
+    family = name.split(":")[0] if ":" in name else ""
+    pins = sorted(oracle_pins.ALL_PINS, key=lambda f: 0 if family and family in f.__name__ else 1)
     caught = []
-    for pin in oracle_pins.ALL_PINS:
+    for pin in pins:
         try:
             pin(lib)
         except (AssertionError, ValueError, FloatingPointError):
             caught.append(pin.__name__)
+            break
     assert caught, f"no pin caught the planted mistake {name!r}"
