@@ -519,6 +519,43 @@ def main():
         log(f"backward (global, head dim 512): {ms:.3f} ms ({tf:.1f} TFLOP/s)")
         del dq, dk, dv, bws, dout, lse
 
+    # ---------------- the attention prologue (RMSNorm + RoPE on Q and K, in
+    # place) at the hybrid layers' shapes; HBM-bound: each vector is read and
+    # written once
+    prologue = None
+    if not args.step_only:
+        prologue = {}
+        for kind, (hq_, hkv_, d_) in (("sliding", (32, 16, 256)), ("global", (32, 4, 512))):
+            R, F = synth.prologue_rotary(kind, d_)
+            pc = synth.prologue_case(7, [HY_LEN] * HY_N, hq_, hkv_, d_, std=0.5)
+            pq = torch.from_numpy(pc.q.view(np.int16)).view(torch.bfloat16).to(dev)
+            pk = torch.from_numpy(pc.k.view(np.int16)).view(torch.bfloat16).to(dev)
+            pp = torch.from_numpy(pc.positions).to(dev)
+            pqw = torch.from_numpy(pc.q_weight).to(dev)
+            pkw = torch.from_numpy(pc.k_weight).to(dev)
+
+            def run_prologue():
+                ia.attn_qk_prologue(pq, pk, pp, q_weight=pqw, k_weight=pkw,
+                                    eps=synth.PROLOGUE_EPS, rotary_dims=R, freq_dims=F,
+                                    rope_theta=synth.PROLOGUE_THETA[kind])
+
+            run_prologue()
+            t = time_calls(run_prologue, args.reps, before=flush_llc)
+            ms = float(np.mean(t))
+            T_ = HY_N * HY_LEN
+            pbytes = 2 * T_ * (hq_ + hkv_) * d_ * 2 + 4 * T_ + 2 * 4 * d_
+            gbs = pbytes / (ms * 1e-3) / 1e9
+            prologue[kind] = {"value": gbs, "unit": "GB/s",
+                              "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                                   f"qk_prologue_kernel<{d_}>",
+                                                   f"{pbytes} B: q and k read and written once "
+                                                   f"({T_} tokens x {hq_}+{hkv_} heads x {d_} x "
+                                                   "2 B x 2), positions, weights", ms),
+                              "ms_mean": ms, "rotary_dims": R, "freq_dims": F,
+                              "theta": synth.PROLOGUE_THETA[kind]}
+            log(f"prologue ({kind}, d {d_}): {ms * 1e3:.1f} us ({gbs:.0f} GB/s)")
+            del pq, pk, pp, pqw, pkw
+
     # ---------------- a measured ceiling beside the published peak: a large
     # bf16 GEMM through the vendor library (torch.matmul)
     ceilings = None
@@ -678,6 +715,7 @@ def main():
                    "k_eq_v_llc_flushed": alias},
         **reported,
         "backward": bw,
+        "prologue": prologue,
         "measured_ceilings": ceilings,
         "cpu_baseline": cpu,
         "parity_sample": parity,

@@ -233,6 +233,54 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v,
                                  hipStream_t stream);
 
 /*
+ * attn_qk_prologue -- the attention prologue of a layer, in place on Q and
+ * K: RMSNorm of every (token, head) vector over the head dim, then rotary
+ * position embedding on its first rotary_dims dims.
+ *
+ * Passage: the layer prologue names a Q/K RMSNorm for head dims 256 and 512,
+ * a RoPE on the sliding layers and a proportional RoPE on the global layers
+ * ("RFC: Gemma-4-31B-it train/rollout consistency", section 6, items 4 and
+ * 6); the norm's fp32 math, its (offset + weight) scale and its single
+ * store cast follow "Gated RMSNorm CUDA kernel for the GDN block" (Summary),
+ * without the gate.  The pages fix no epsilon, offset, rotary width,
+ * frequency base or pairing: all are arguments, and dims i and i + R/2 form
+ * a pair (R = rotary_dims).
+ *
+ * Arithmetic (fp32 unless stated), per vector x of head_dim bf16 values at
+ * position pos:
+ *   ss   = sum of x_d^2: each of 64 lanes adds its head_dim/64 consecutive
+ *          elements in ascending order, then the lanes combine by the
+ *          exchange tree xor 32, 16, 8, 4, 2, 1
+ *   y_d  = (x_d * (1 / sqrt(ss / head_dim + eps))) * (weight_offset + w_d)
+ *          (IEEE division and square root; skipped when w is NULL)
+ *   a_i  = pos * rope_theta^(-2i / freq_dims) in fp64, c_i, s_i = fp32 of
+ *          its cosine and sine, i < R/2
+ *   out_i = y_i c_i - y_{i+R/2} s_i,  out_{i+R/2} = y_i s_i + y_{i+R/2} c_i,
+ *          dims R .. head_dim-1 unchanged; bf16 round to nearest even.
+ * freq_dims = rotary_dims is the plain partial RoPE; freq_dims = head_dim
+ * with rotary_dims < head_dim keeps the turned dims at the frequencies of a
+ * full RoPE (the proportional reading).  A vector's bytes depend only on its
+ * values, its position and the arguments.
+ *
+ * Arguments (device pointers caller-owned; q and k are read and overwritten):
+ *   q           bf16 [num_tokens, num_q_heads, head_dim], 16-byte aligned
+ *   k           bf16 [num_tokens, num_kv_heads, head_dim] or NULL (Q only)
+ *   positions   int32 [num_tokens]: the position of each row in its sequence
+ *   q_weight, k_weight  fp32 [head_dim] or NULL (no norm on that tensor)
+ *   eps >= 0, weight_offset finite
+ *   rotary_dims  0 (no RoPE) .. head_dim, a multiple of head_dim / 32
+ *   freq_dims    > 0 when rotary_dims > 0; rope_theta > 0
+ *   head_dim     64, 256 or 512
+ * Errors: ATTN_E_NULL, ATTN_E_SHAPE, ATTN_E_UNSUPPORTED, ATTN_E_ALIGN,
+ * ATTN_E_HIP; nothing is enqueued on error.  num_tokens = 0 does nothing.
+ */
+int attn_qk_prologue(void* q, void* k, const int32_t* positions, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     const float* q_weight, const float* k_weight, float eps,
+                     float weight_offset, int32_t rotary_dims, int32_t freq_dims,
+                     double rope_theta, hipStream_t stream);
+
+/*
  * attn_decode_workspace_size -- bytes of fp32 workspace attn_decode_paged
  * needs for this batch: [batch, num_q_heads, ceil(max_seq_len /
  * ATTN_DECODE_CHUNK), head_dim + 4] fp32 (per chunk record: the unnormalised

@@ -18,6 +18,8 @@ Entry points (same names as the C ABI):
                        the same without a workspace (the library's static
                        scratch), for callers that cannot allocate
   attn_decode_workspace_size
+  attn_qk_prologue     the layer's prologue on Q and K in place: RMSNorm over
+                       the head dim, then RoPE on the first rotary_dims dims
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ import os
 
 __all__ = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_paged",
            "attn_decode_paged", "attn_decode_paged_noalloc", "attn_decode_workspace_size",
+           "attn_qk_prologue",
            "ATTN_NOALLOC_SCRATCH_BYTES",
            "last_provenance", "last_error", "AttnError", "library", "LIB_PATH",
            "ATTN_WINDOW_NONE", "ATTN_DECODE_CHUNK", "ERROR_CODES", "EXPORTS"]
@@ -39,7 +42,7 @@ ERROR_CODES = {0: "ATTN_OK", 1: "ATTN_E_NULL", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNS
                4: "ATTN_E_ALIGN", 5: "ATTN_E_WORKSPACE", 6: "ATTN_E_HIP", 7: "ATTN_E_VALIDATE"}
 EXPORTS = ["attn_prefill_varlen", "attn_prefill_varlen_backward", "attn_prefill_paged",
            "attn_decode_workspace_size", "attn_decode_paged", "attn_decode_paged_noalloc",
-           "attn_last_error", "attn_last_provenance", "attn_version"]
+           "attn_qk_prologue", "attn_last_error", "attn_last_provenance", "attn_version"]
 
 
 class AttnError(RuntimeError):
@@ -79,6 +82,9 @@ def library():
         lib.attn_decode_paged_noalloc.restype = ctypes.c_int
         lib.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32,
                                                   i32, i32, i32, f32, vp, vp]
+        lib.attn_qk_prologue.restype = ctypes.c_int
+        lib.attn_qk_prologue.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, f32, f32, i32,
+                                         i32, ctypes.c_double, vp]
         lib.attn_last_error.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
         lib.attn_last_provenance.restype = ctypes.c_int
@@ -388,3 +394,39 @@ def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_se
         float(softmax_scale), _ptr(out), _stream(stream))
     _check(rc)
     return out
+
+
+def attn_qk_prologue(q, k, positions, q_weight=None, k_weight=None, eps=1e-6, weight_offset=0.0,
+                     rotary_dims=0, freq_dims=None, rope_theta=10000.0, stream=None):
+    """The layer's attention prologue, in place: RMSNorm of every head vector
+    of q (and k) over the head dim, then RoPE on its first ``rotary_dims``
+    dims (pairs i, i + R/2; angle pos * rope_theta^(-2i/F), F = ``freq_dims``,
+    default R).
+
+    q bf16 [T, Hq, D]; k bf16 [T, Hkv, D] or None; positions int32 [T];
+    q_weight / k_weight fp32 [D] or None (no norm on that tensor).  Returns
+    (q, k).
+    """
+    import torch
+    _require(q, "q", torch.bfloat16, 3)
+    T, hq, d = q.shape
+    hkv = 0
+    if k is not None:
+        _require(k, "k", torch.bfloat16, 3)
+        if k.shape[0] != T or k.shape[2] != d:
+            raise ValueError(f"k must be [T={T}, Hkv, D={d}], got {tuple(k.shape)}")
+        hkv = k.shape[1]
+    _require(positions, "positions", torch.int32, 1)
+    _shape(positions, "positions", (T,))
+    for name, w in (("q_weight", q_weight), ("k_weight", k_weight)):
+        if w is not None:
+            _require(w, name, torch.float32, 1)
+            _shape(w, name, (d,))
+    _on_one_gpu(q=q, k=k, positions=positions, q_weight=q_weight, k_weight=k_weight)
+    R = int(rotary_dims)
+    F = R if freq_dims is None else int(freq_dims)
+    _check(library().attn_qk_prologue(_ptr(q), _ptr(k), _ptr(positions), T, hq, hkv, d,
+                                      _ptr(q_weight), _ptr(k_weight), float(eps),
+                                      float(weight_offset), R, F, float(rope_theta),
+                                      _stream(stream)))
+    return q, k

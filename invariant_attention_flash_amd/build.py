@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libinvattn.so")
-SOURCES = ["api.hip", "prefill.hip", "prefill_ws.hip", "decode.hip", "backward.hip"]
+SOURCES = ["api.hip", "prefill.hip", "prefill_ws.hip", "decode.hip", "backward.hip", "prologue.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

@@ -540,6 +540,70 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v, co
   return ATTN_OK;
 }
 
+int attn_qk_prologue(void* q, void* k, const int32_t* positions, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     const float* q_weight, const float* k_weight, float eps,
+                     float weight_offset, int32_t rotary_dims, int32_t freq_dims,
+                     double rope_theta, hipStream_t stream) {
+  g_err.clear();
+  if (num_tokens < 0) return fail(ATTN_E_SHAPE, "num_tokens=%d must be >= 0", num_tokens);
+  if (num_q_heads <= 0) return fail(ATTN_E_SHAPE, "num_q_heads=%d must be positive", num_q_heads);
+  if (k != nullptr && num_kv_heads <= 0)
+    return fail(ATTN_E_SHAPE, "num_kv_heads=%d must be positive when k is given", num_kv_heads);
+  if (head_dim != 64 && head_dim != 256 && head_dim != 512)
+    return fail(ATTN_E_UNSUPPORTED, "head_dim=%d not in {64,256,512}", head_dim);
+  const int per_lane = head_dim / 64;
+  if (rotary_dims < 0 || rotary_dims > head_dim || rotary_dims % (2 * per_lane) != 0)
+    return fail(ATTN_E_UNSUPPORTED, "rotary_dims=%d must lie in [0, %d] and be a multiple of %d",
+                rotary_dims, head_dim, 2 * per_lane);
+  if (rotary_dims > 0 && freq_dims <= 0)
+    return fail(ATTN_E_UNSUPPORTED, "freq_dims=%d must be positive", freq_dims);
+  if (rotary_dims > 0 && (!std::isfinite(rope_theta) || !(rope_theta > 0.0)))
+    return fail(ATTN_E_UNSUPPORTED, "rope_theta=%g must be finite and > 0", rope_theta);
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(ATTN_E_UNSUPPORTED, "eps=%g must be finite and >= 0", (double)eps);
+  if (!std::isfinite(weight_offset))
+    return fail(ATTN_E_UNSUPPORTED, "weight_offset=%g must be finite", (double)weight_offset);
+  const int hkv = k != nullptr ? num_kv_heads : 0;
+  if ((long long)num_q_heads + hkv > 65536)
+    return fail(ATTN_E_UNSUPPORTED, "num_q_heads + num_kv_heads = %d exceeds 65536",
+                num_q_heads + hkv);
+  char sid[128];
+  snprintf(sid, sizeof sid, "prologue_d%d_rmsnorm%s%s_rope%d_f%d_t256", head_dim,
+           q_weight ? "_q" : "", (k && k_weight) ? "_k" : "", rotary_dims, freq_dims);
+  const char* kernel = "none (empty input)";
+  if (num_tokens > 0) {
+    if (!q) return fail(ATTN_E_NULL, "q is NULL");
+    if (!positions) return fail(ATTN_E_NULL, "positions is NULL");
+    if (!aligned16(q)) return fail(ATTN_E_ALIGN, "q is not 16-byte aligned");
+    if (k && !aligned16(k)) return fail(ATTN_E_ALIGN, "k is not 16-byte aligned");
+    if (!aligned4(positions)) return fail(ATTN_E_ALIGN, "positions is not 4-byte aligned");
+    if (q_weight && !aligned4(q_weight)) return fail(ATTN_E_ALIGN, "q_weight is not 4-byte aligned");
+    if (k_weight && !aligned4(k_weight)) return fail(ATTN_E_ALIGN, "k_weight is not 4-byte aligned");
+    PrologueArgs a{q, k, positions, num_tokens, num_q_heads, hkv, head_dim, q_weight,
+                   k ? k_weight : nullptr, eps, weight_offset, rotary_dims, freq_dims, rope_theta};
+    hipError_t e = launch_qk_prologue(a, stream, &kernel);
+    if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  }
+  int dev = -1;
+  (void)hipGetDevice(&dev);
+  char buf[768];
+  snprintf(buf, sizeof buf,
+           "{\"op\":\"attn_qk_prologue\",\"requested_backend\":\"invattn-hip\",\"actual_backend\":"
+           "\"invattn-hip\",\"kernel_id\":\"%s\",\"schedule_id\":\"%s\",\"split_policy\":\"none\","
+           "\"accumulator_dtype\":\"fp32\",\"layer_type\":\"%s\",\"device\":%d,\"arch\":\"%s\","
+           "\"dtype\":\"bf16\",\"shape\":{\"tokens\":%d,\"num_q_heads\":%d,\"num_kv_heads\":%d,"
+           "\"head_dim\":%d,\"rotary_dims\":%d,\"freq_dims\":%d},\"casts\":[\"out->bf16 rne\"],"
+           "\"angles\":\"fp64\",\"fallback\":\"none\",\"version\":\"%s\"}",
+           kernel, sid, rotary_dims < head_dim ? "partial rope" : "full rope", dev,
+           device_name(dev < 0 ? 0 : dev).c_str(), num_tokens, num_q_heads, hkv, head_dim,
+           rotary_dims, freq_dims, attn_version());
+  g_prov = buf;
+  g_have_prov = true;
+  if (trace_enabled()) fprintf(stderr, "invattn: %s\n", buf);
+  return ATTN_OK;
+}
+
 size_t attn_decode_workspace_size(int32_t batch, int32_t max_seq_len, int32_t num_q_heads,
                                   int32_t head_dim) {
   if (batch <= 0 || max_seq_len <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;

@@ -146,6 +146,22 @@ hipError_t launch_prefill_ws(const PrefillArgs& a, hipStream_t stream);
 
 // Attention backward (backward.hip): dq and delta (one kernel), then dk and
 // dv (a second kernel reading delta), on the caller's stream.
+// The attention prologue (prologue.hip): RMSNorm then RoPE of every Q and K
+// head vector, in place.  k == nullptr means hkv == 0 here.
+struct PrologueArgs {
+  void* q;
+  void* k;
+  const int32_t* positions;
+  int tokens, hq, hkv, d;
+  const float* q_weight;
+  const float* k_weight;
+  float eps, offset;
+  int rotary_dims, freq_dims;
+  double theta;
+};
+
+hipError_t launch_qk_prologue(const PrologueArgs& a, hipStream_t stream, const char** kernel);
+
 struct BackwardArgs {
   const void* q;
   const void* k;

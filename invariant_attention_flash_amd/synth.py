@@ -433,3 +433,49 @@ def prefill_case_device(seed, lengths, hq, hkv, d, window, std=0.5, spans=None, 
             "spans_host": spans_np, "max_seqlen": max(lengths) if lengths else 0,
             "hq": hq, "hkv": hkv, "d": d, "window": window, "scale": 1.0 / float(np.sqrt(d)),
             "lengths": [lengths[i] for i in order]}
+
+
+# --------------------------------------------------------------------------
+# prologue cases (RMSNorm + RoPE on Q and K before attention)
+# --------------------------------------------------------------------------
+# Prologue readings used by the tests and the benchmark (the pages fix none of
+# them): eps, RoPE base, and the rotary width of each layer type (sliding:
+# every dim; global: a quarter of the dims at the frequencies of a full RoPE).
+PROLOGUE_EPS = 1e-6
+PROLOGUE_THETA = {"sliding": 10000.0, "global": 1000000.0}
+
+
+def prologue_rotary(kind: str, d: int):
+    """(rotary_dims, freq_dims) of a layer type: full RoPE on sliding layers,
+    proportional p-RoPE (p = 1/4, frequencies over the whole head dim) on
+    global ones."""
+    return (d, d) if kind == "sliding" else (d // 4, d)
+
+
+@dataclass
+class PrologueCase:
+    q: np.ndarray          # [T, Hq, D] uint16 bf16 bits
+    k: np.ndarray          # [T, Hkv, D] uint16 bf16 bits
+    positions: np.ndarray  # [T] int32
+    q_weight: np.ndarray   # [D] float32
+    k_weight: np.ndarray   # [D] float32
+
+
+def prologue_case(seed, lengths, hq, hkv, d, std=1.0, weight_std=0.1, start=None):
+    """Packed sequences: token t of sequence i sits at position (start_i + t);
+    Q, K ~ N(0,1)*std per sequence stream (as in prefill cases), weights ~
+    N(0, weight_std^2) from the case stream.  ``start`` defaults to 0 for
+    every sequence (a prefill)."""
+    rng = np.random.default_rng([seed, 0])
+    qs, ks, ps = [], [], []
+    for i, L in enumerate(lengths):
+        r = np.random.default_rng([seed, 1000 + i])
+        qs.append(_normal_bf16(r, (L, hq, d), std))
+        ks.append(_normal_bf16(r, (L, hkv, d), std))
+        s0 = 0 if start is None else int(start[i])
+        ps.append(np.arange(s0, s0 + L, dtype=np.int32))
+    qw = (rng.standard_normal(d) * weight_std).astype(np.float32)
+    kw = (rng.standard_normal(d) * weight_std).astype(np.float32)
+    cat = lambda a, shp: np.concatenate(a) if a else np.zeros(shp, np.uint16)
+    return PrologueCase(cat(qs, (0, hq, d)), cat(ks, (0, hkv, d)),
+                        np.concatenate(ps) if ps else np.zeros(0, np.int32), qw, kw)

@@ -266,3 +266,54 @@ def test_noalloc_decode_rejects_beyond_scratch_before_any_gpu_call():
                                                 512, -1, ctypes.c_float(0.044), x, None)
     assert rc == E["ATTN_E_WORKSPACE"]
     assert "scratch" in ia.last_error()
+
+
+def call_prologue(**kw):
+    a = dict(q=1 << 20, k=1 << 20, pos=1 << 20, T=8, hq=4, hkv=2, d=256, qw=1 << 20, kw=1 << 20,
+             eps=1e-6, off=0.0, R=256, F=256, theta=10000.0)
+    a.update(kw)
+    ptr = lambda x: None if x is None else ctypes.c_void_p(x)
+    rc = ia.library().attn_qk_prologue(ptr(a["q"]), ptr(a["k"]), ptr(a["pos"]), a["T"], a["hq"],
+                                       a["hkv"], a["d"], ptr(a["qw"]), ptr(a["kw"]), a["eps"],
+                                       a["off"], a["R"], a["F"], a["theta"], None)
+    return rc, ia.last_error()
+
+
+PROLOGUE_ERRORS = [
+    (dict(q=None), "ATTN_E_NULL", "q is NULL"),
+    (dict(pos=None), "ATTN_E_NULL", "positions is NULL"),
+    (dict(T=-1), "ATTN_E_SHAPE", "num_tokens"),
+    (dict(hq=0), "ATTN_E_SHAPE", "num_q_heads"),
+    (dict(hkv=0), "ATTN_E_SHAPE", "num_kv_heads"),
+    (dict(d=128), "ATTN_E_UNSUPPORTED", "head_dim"),
+    (dict(R=258), "ATTN_E_UNSUPPORTED", "rotary_dims"),
+    (dict(R=-2), "ATTN_E_UNSUPPORTED", "rotary_dims"),
+    (dict(R=4), "ATTN_E_UNSUPPORTED", "multiple of 8"),
+    (dict(d=512, R=8), "ATTN_E_UNSUPPORTED", "multiple of 16"),
+    (dict(F=0), "ATTN_E_UNSUPPORTED", "freq_dims"),
+    (dict(theta=0.0), "ATTN_E_UNSUPPORTED", "rope_theta"),
+    (dict(theta=float("inf")), "ATTN_E_UNSUPPORTED", "rope_theta"),
+    (dict(eps=-1.0), "ATTN_E_UNSUPPORTED", "eps"),
+    (dict(eps=float("nan")), "ATTN_E_UNSUPPORTED", "eps"),
+    (dict(off=float("inf")), "ATTN_E_UNSUPPORTED", "weight_offset"),
+    (dict(q=(1 << 20) + 4), "ATTN_E_ALIGN", "q is not 16-byte"),
+    (dict(k=(1 << 20) + 8), "ATTN_E_ALIGN", "k is not 16-byte"),
+    (dict(pos=(1 << 20) + 2), "ATTN_E_ALIGN", "positions is not 4-byte"),
+    (dict(qw=(1 << 20) + 2), "ATTN_E_ALIGN", "q_weight is not 4-byte"),
+]
+
+
+@pytest.mark.parametrize("kw,code,text", PROLOGUE_ERRORS,
+                         ids=[c[2] + str(i) for i, c in enumerate(PROLOGUE_ERRORS)])
+def test_prologue_rejects(kw, code, text):
+    rc, msg = call_prologue(**kw)
+    assert ia.ERROR_CODES[rc] == code, (rc, msg)
+    assert text in msg
+
+
+def test_prologue_empty_input_needs_no_pointers():
+    rc, msg = call_prologue(T=0, q=None, k=None, pos=None, qw=None, kw=None)
+    assert rc == 0, msg
+    # no RoPE: the rotary checks do not apply
+    rc, msg = call_prologue(T=0, R=0, F=0, theta=0.0)
+    assert rc == 0, msg
