@@ -253,8 +253,9 @@ int attn_prefill_varlen_backward(const void* q, const void* k, const void* v,
  *          exchange tree xor 32, 16, 8, 4, 2, 1
  *   y_d  = (x_d * (1 / sqrt(ss / head_dim + eps))) * (weight_offset + w_d)
  *          (IEEE division and square root; skipped when w is NULL)
- *   a_i  = pos * rope_theta^(-2i / freq_dims) in fp64, c_i, s_i = fp32 of
- *          its cosine and sine, i < R/2
+ *   a_i  = pos * 2^(-2i / freq_dims * log2 rope_theta) in fp64 (i < R/2),
+ *          reduced in fp64 by the nearest multiple k of pi/2; c_i, s_i = fp32
+ *          cosine and sine of the reduced angle, placed by quadrant k mod 4
  *   out_i = y_i c_i - y_{i+R/2} s_i,  out_{i+R/2} = y_i s_i + y_{i+R/2} c_i,
  *          dims R .. head_dim-1 unchanged; bf16 round to nearest even.
  * freq_dims = rotary_dims is the plain partial RoPE; freq_dims = head_dim

@@ -594,7 +594,7 @@ int attn_qk_prologue(void* q, void* k, const int32_t* positions, int32_t num_tok
            "\"accumulator_dtype\":\"fp32\",\"layer_type\":\"%s\",\"device\":%d,\"arch\":\"%s\","
            "\"dtype\":\"bf16\",\"shape\":{\"tokens\":%d,\"num_q_heads\":%d,\"num_kv_heads\":%d,"
            "\"head_dim\":%d,\"rotary_dims\":%d,\"freq_dims\":%d},\"casts\":[\"out->bf16 rne\"],"
-           "\"angles\":\"fp64\",\"fallback\":\"none\",\"version\":\"%s\"}",
+           "\"angles\":\"fp64, reduced by pi/2\",\"fallback\":\"none\",\"version\":\"%s\"}",
            kernel, sid, rotary_dims < head_dim ? "partial rope" : "full rope", dev,
            device_name(dev < 0 ? 0 : dev).c_str(), num_tokens, num_q_heads, hkv, head_dim,
            rotary_dims, freq_dims, attn_version());

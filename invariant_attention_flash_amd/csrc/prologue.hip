@@ -17,8 +17,10 @@
 //        1 (each step adds two lanes' sums; every lane ends with the same bits)
 //   r  = 1 / sqrt(ss / D + eps)          (IEEE fp32 division and square root)
 //   y_d = (x_d * r) * (offset + w_d)     (no norm when the weight is NULL)
-//   for i < R/2, the angle a_i = pos * theta^(-2i/F) is formed in fp64 and
-//   c_i = fp32(cos a_i), s_i = fp32(sin a_i); then
+//   for i < R/2, the angle a_i = pos * 2^(-2i/F * log2 theta) is formed in
+//   fp64 and reduced in fp64 by the nearest multiple k of pi/2 (pi/2 held as
+//   two doubles); c_i and s_i are the fp32 cosine and sine of the reduced
+//   angle (|r| <= pi/4, rounded to fp32), placed by the quadrant k mod 4; then
 //   out_i = y_i c_i - y_{i+R/2} s_i,  out_{i+R/2} = y_i s_i + y_{i+R/2} c_i
 //   (fp32, each product rounded), dims R .. D-1 pass through; bf16 RNE store.
 // A vector's bytes depend only on itself, its position and the arguments:
@@ -83,9 +85,19 @@ __global__ __launch_bounds__(kPrologueThreads) void qk_prologue_kernel(
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const double pos = (double)positions[t];
+  const double l2t = log2(theta);
   for (int i = tid; i < half; i += kPrologueThreads) {
-    const double ang = pos * pow(theta, -2.0 * i / freq_dims);
-    cs[i] = make_float2((float)cos(ang), (float)sin(ang));
+    const double ang = pos * exp2(-2.0 * i / freq_dims * l2t);
+    // reduce by pi/2 in fp64 (2/pi, and pi/2 as a leading double plus the
+    // rest), then the fp32 functions on |r| <= pi/4
+    const double kq = rint(ang * 0.63661977236758134308);
+    const float r =
+        (float)(__builtin_fma(-kq, 1.5707963267948966192, ang) - kq * 6.123233995736766e-17);
+    const float sr = sinf(r), cr = cosf(r);
+    const int qd = (int)((long long)kq & 3);
+    const float cv = qd == 0 ? cr : qd == 1 ? -sr : qd == 2 ? -cr : sr;
+    const float sv = qd == 0 ? sr : qd == 1 ? cr : qd == 2 ? -sr : -cr;
+    cs[i] = make_float2(cv, sv);
   }
   __syncthreads();
 
