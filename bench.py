@@ -582,12 +582,14 @@ def main():
         del src, dst, sink
         ceilings = {"gemm_bf16_tflops": gemm_tf, "gemm": f"torch.matmul bf16 {n}x{n}x{n}, median",
                     "prefill_frac_of_gemm": hy_tflops / gemm_tf,
-                    "hbm_copy_gbs": copy_gbs, "hbm_read_gbs": read_gbs,
-                    "hbm": "torch copy_ of 1 GiB (read + write bytes) and torch.sum over 1 GiB "
-                           "(read bytes), median",
-                    "decode_frac_of_read": dc_gbs / read_gbs}
-        log(f"ceiling: bf16 GEMM {gemm_tf:.0f} TFLOP/s, HBM copy {copy_gbs:.0f} GB/s, "
-            f"read {read_gbs:.0f} GB/s")
+                    "torch_streaming": {
+                        "copy_gbs": copy_gbs, "sum_gbs": read_gbs,
+                        "note": "torch's own copy_ (read + write bytes) and sum (read bytes) over "
+                                "1 GiB, median: context, not ceilings (the decode kernel streams "
+                                "faster than both)",
+                        "decode_over_sum": dc_gbs / read_gbs}}
+        log(f"ceiling: bf16 GEMM {gemm_tf:.0f} TFLOP/s; torch copy {copy_gbs:.0f} GB/s, "
+            f"torch sum {read_gbs:.0f} GB/s")
 
     # ---------------- CPU oracle baselines + parity spot-checks on sampled rows
     cpu = None

@@ -28,7 +28,7 @@
 //
 // Work map: one workgroup of four waves per token; the table of (c_i, s_i)
 // is formed once per token in LDS, and each wave takes every fourth head
-// vector of the token (Q heads, then K heads), four at a time, lane l
+// vector of the token (Q heads, then K heads), one or two at a time, lane l
 // holding elements [l*D/64, (l+1)*D/64).  HBM-bound: every vector is read
 // and written once.
 #include "device_common.h"
@@ -39,7 +39,11 @@ namespace invattn {
 namespace {
 
 constexpr int kPrologueThreads = 256;
-constexpr int kPrologueBatch = 4;  // head vectors a wave loads before it computes
+// Head vectors a wave loads before it computes: 2 at head dims up to 256, 1
+// at 512 (more registers per vector cost more occupancy than the extra loads
+// in flight gain; batches of 4 and 8 were slower at both).
+template <int D>
+constexpr int prologue_batch() { return D >= 512 ? 1 : 2; }
 
 template <int E>
 struct Chunk;
@@ -80,6 +84,7 @@ __global__ __launch_bounds__(kPrologueThreads) void qk_prologue_kernel(
     int hkv, const float* __restrict__ qw, const float* __restrict__ kw, float eps, float offset,
     int half, int freq_dims, double theta) {
   constexpr int E = D / 64;  // elements per lane
+  constexpr int kPrologueBatch = prologue_batch<D>();
   using CT = typename Chunk<E>::T;
   __shared__ float2 cs[D / 2];
   const int t = blockIdx.x;
