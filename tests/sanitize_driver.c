@@ -169,6 +169,18 @@ int main(void) {
   CHECK(attn_decode_paged(p, p, p, ip, 4, ip, 2, 100, 16, 16, 32, 4, 512, -1, 0.044f, p, 1 << 20, p, NULL) == ATTN_E_SHAPE);
   CHECK(attn_decode_paged_noalloc(p, p, p, ip, 2048, ip, 64, 32768, 100, 16, 32, 4, 512, -1, 0.044f, p, NULL) == ATTN_E_WORKSPACE);
   CHECK(strstr(attn_last_error(), "scratch") != NULL);
+  /* the prologue's argument checks (no launch), then its empty-input record */
+  const float* fp = (const float*)p;
+  CHECK(attn_qk_prologue(p, p, ip, 8, 4, 2, 128, fp, fp, 1e-6f, 0.f, 128, 128, 1e4, NULL) == ATTN_E_UNSUPPORTED);
+  CHECK(attn_qk_prologue(p, p, ip, 8, 4, 2, 256, fp, fp, 1e-6f, 0.f, 4, 256, 1e4, NULL) == ATTN_E_UNSUPPORTED);
+  CHECK(attn_qk_prologue(p, p, ip, 8, 4, 2, 256, fp, fp, -1.f, 0.f, 256, 256, 1e4, NULL) == ATTN_E_UNSUPPORTED);
+  CHECK(attn_qk_prologue(p, p, ip, 8, 4, 2, 256, fp, fp, 1e-6f, 0.f, 256, 256, 0.0, NULL) == ATTN_E_UNSUPPORTED);
+  CHECK(attn_qk_prologue(NULL, p, ip, 8, 4, 2, 256, fp, fp, 1e-6f, 0.f, 256, 256, 1e4, NULL) == ATTN_E_NULL);
+  CHECK(attn_qk_prologue(odd, p, ip, 8, 4, 2, 256, fp, fp, 1e-6f, 0.f, 256, 256, 1e4, NULL) == ATTN_E_ALIGN);
+  CHECK(attn_qk_prologue(p, p, ip, -1, 4, 2, 256, fp, fp, 1e-6f, 0.f, 256, 256, 1e4, NULL) == ATTN_E_SHAPE);
+  CHECK(attn_qk_prologue(NULL, NULL, NULL, 0, 4, 2, 256, NULL, NULL, 1e-6f, 0.f, 256, 256, 1e4, NULL) == ATTN_OK);
+  CHECK(attn_last_provenance(buf, sizeof buf) > 0);
+  CHECK(strstr(buf, "attn_qk_prologue") != NULL);
   printf("abi driver ok\n");
   return 0;
 }
